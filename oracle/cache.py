@@ -1,0 +1,79 @@
+"""The oracle's own quantized cache of one sequence.
+
+Built directly from the raw bf16 keys and values: every position gets INT4 codes
+(keys rotated, values not), and the positions of the INT8 region get INT8
+codes of the same rotated keys / raw values (KV4-RL, "Methodology in Plain
+English"; SAW-INT4, section 2).  Nothing here depends on how a GPU lays the
+cache out in memory.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .hadamard import fwht_f32
+from .numerics import bf16_to_f32
+from .quant import quantize, dequantize, INT4_QMAX, INT8_QMAX
+from .regions import int8_region, ring_entry
+
+
+@dataclass
+class SeqCache:
+    L: int
+    s: int
+    w: int
+    h: int
+    # INT4, every position: codes [L, H, d] uint8, scale/zero fp16 bits [L, H]
+    k4: np.ndarray
+    k4_scale: np.ndarray
+    k4_zero: np.ndarray
+    v4: np.ndarray
+    v4_scale: np.ndarray
+    v4_zero: np.ndarray
+    # INT8, region positions only: positions [n8], codes [n8, H, d], bits [n8, H]
+    pos8: np.ndarray
+    k8: np.ndarray
+    k8_scale: np.ndarray
+    k8_zero: np.ndarray
+    v8: np.ndarray
+    v8_scale: np.ndarray
+    v8_zero: np.ndarray
+
+    def ring(self) -> np.ndarray:
+        """Side-cache entry of each INT8 position."""
+        return np.array([ring_entry(int(p), self.s, self.w) for p in self.pos8], dtype=np.int64)
+
+
+def rotated_keys_f32(k_bits, h: int) -> np.ndarray:
+    """fp32 rotated keys (the quantizer's input) from bf16 key patterns [..., d]."""
+    return fwht_f32(bf16_to_f32(k_bits), h)
+
+
+def quantize_sequence(k_bits, v_bits, h: int, s: int, w: int) -> SeqCache:
+    """Quantize a whole sequence's keys/values [L, H, d] (bf16 patterns)."""
+    k_bits = np.asarray(k_bits, dtype=np.uint16)
+    v_bits = np.asarray(v_bits, dtype=np.uint16)
+    L = k_bits.shape[0]
+    yk = rotated_keys_f32(k_bits, h)
+    yv = bf16_to_f32(v_bits)
+    k4, k4s, k4z = quantize(yk, INT4_QMAX)
+    v4, v4s, v4z = quantize(yv, INT4_QMAX)
+    pos8 = np.array(int8_region(L, s, w), dtype=np.int64)
+    k8, k8s, k8z = quantize(yk[pos8], INT8_QMAX)
+    v8, v8s, v8z = quantize(yv[pos8], INT8_QMAX)
+    return SeqCache(L, s, w, h, k4, k4s, k4z, v4, v4s, v4z, pos8, k8, k8s, k8z, v8, v8s, v8z)
+
+
+def dequantized_kv(c: SeqCache):
+    """fp64 keys (rotated basis) and values the attention sees, [L, H, d] each.
+
+    Positions of the INT8 region take the INT8 values, all others the INT4 ones.
+    """
+    K = dequantize(c.k4, c.k4_scale, c.k4_zero)
+    V = dequantize(c.v4, c.v4_scale, c.v4_zero)
+    if len(c.pos8):
+        K[c.pos8] = dequantize(c.k8, c.k8_scale, c.k8_zero)
+        V[c.pos8] = dequantize(c.v8, c.v8_scale, c.v8_zero)
+    return K, V

@@ -1,0 +1,120 @@
+"""Per-token asymmetric quantization of one 128-dim token-head vector.
+
+KV4-RL ("Methodology in Plain English"): every new K/V vector is quantized on
+the fly into one affine group per 128-dimensional token-head vector with an
+FP16 scale and an FP16 offset; the INT8 side cache uses the same scheme with
+256 levels (reading: the pages do not describe the INT8 format beyond its
+width).  SAW-INT4 (section 2) calls this token-wise INT4 quantization.
+
+Steps, all in fp32 because they decide integer codes (the pages fix only the
+FP16 storage of scale and offset):
+
+1. mn = min_i y_i, mx = max_i y_i (exact);
+2. scale_f = fp32(fp32(mx - mn) / qmax)   (IEEE division; qmax = 15 or 255);
+3. scale_h = fp16(scale_f), zero_h = fp16(mn)   (round to nearest even);
+4. if scale_h == 0 every code is 0 (constant or nearly constant vector);
+   otherwise t_i = fp32(fp32(y_i - zero_h) / scale_h) and
+   c_i = clamp(rint(t_i), 0, qmax) with ties to even;
+5. dequantized value = scale_h * c_i + zero_h, evaluated in fp64.
+
+The codes are taken against the stored fp16 scale and offset, so that the
+dequantized value is the one attention actually sees.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import f32_to_f16_bits, f16_bits_to_f32, f16_bits_to_f64
+
+INT4_QMAX = 15
+INT8_QMAX = 255
+
+
+def quantize(y, qmax: int):
+    """Quantize fp32 vectors y[..., n] along the last axis.
+
+    Returns (codes uint8 [..., n], scale_bits uint16 [...], zero_bits uint16 [...]).
+    """
+    y = np.asarray(y, dtype=np.float32)
+    mn = y.min(axis=-1)
+    mx = y.max(axis=-1)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        scale_f = (mx - mn) / np.float32(qmax)
+    scale_bits = f32_to_f16_bits(scale_f)
+    zero_bits = f32_to_f16_bits(mn)
+    sf = f16_bits_to_f32(scale_bits)
+    zf = f16_bits_to_f32(zero_bits)
+    guard = sf == 0
+    safe_sf = np.where(guard, np.float32(1.0), sf).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        t = (y - zf[..., None]) / safe_sf[..., None]
+    c = np.clip(np.rint(t), 0, qmax)
+    c = np.where(guard[..., None], 0, c)
+    return c.astype(np.uint8), scale_bits, zero_bits
+
+
+def dequantize(codes, scale_bits, zero_bits) -> np.ndarray:
+    """scale_h * c + zero_h in fp64."""
+    s = f16_bits_to_f64(scale_bits)[..., None]
+    z = f16_bits_to_f64(zero_bits)[..., None]
+    return s * np.asarray(codes, dtype=np.float64) + z
+
+
+def tie_near(y, qmax: int, rel: float = 1e-6):
+    """Flags of elements whose integer code sits within `rel` (relative) of a rounding tie.
+
+    An element is flagged when its t_i lies within rel of a half-integer, or
+    when its vector's scale_f or mn lies within rel of an fp16 rounding
+    midpoint.  Such elements may legitimately round differently under any
+    other evaluation order; they are counted and reported by the parity tests.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    mn = y.min(axis=-1)
+    mx = y.max(axis=-1)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        scale_f = (mx - mn) / np.float32(qmax)
+    vec_flag = _near_f16_midpoint(scale_f, rel) | _near_f16_midpoint(mn, rel)
+    sb = f32_to_f16_bits(scale_f)
+    zb = f32_to_f16_bits(mn)
+    sf = f16_bits_to_f32(sb)
+    zf = f16_bits_to_f32(zb)
+    safe = np.where(sf == 0, np.float32(1.0), sf).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        t = ((y - zf[..., None]) / safe[..., None]).astype(np.float64)
+    frac = t - np.floor(t)
+    el_flag = np.abs(frac - 0.5) <= rel * np.maximum(np.abs(t), 1.0)
+    el_flag &= (sf != 0)[..., None]
+    return el_flag | vec_flag[..., None]
+
+
+def _near_f16_midpoint(x, rel):
+    """True where fp32 x lies within rel of the midpoint between two fp16 neighbours."""
+    x = np.asarray(x, dtype=np.float64)
+    h = np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
+    # the two fp16 neighbours around x
+    up = np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(h.astype(np.float16), np.float16(-np.inf)).astype(np.float64)
+    other = np.where(x >= h, up, dn)
+    mid = 0.5 * (h + other)
+    with np.errstate(invalid="ignore"):
+        return np.abs(x - mid) <= rel * np.maximum(np.abs(x), 1e-30)
+
+
+def pack_int4(codes) -> np.ndarray:
+    """Two codes per byte, low nibble = even index (canonical byte form of a vector)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def bytes_per_token_head(head_dim: int, bits: int) -> int:
+    """K+V bytes of one (token, KV head): codes plus an fp16 scale and offset each."""
+    return 2 * (head_dim * bits // 8 + 4)

@@ -1,0 +1,143 @@
+"""Pins for the oracle's fp64 decode attention and the regional log-sum-exp merge."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import (attend, attend_regions, merge, region_stats,
+                              rotated_query, softmax_attention, unquantized_attention)
+from oracle.cache import dequantized_kv, quantize_sequence
+from oracle.hadamard import rotate_f64
+from workloads import build_workload, get_config, seq_kv, seq_query, bf16_bits
+
+
+def _brute(q, K, V):
+    """Pure-Python loops: out[j] = sum_p softmax_p(q_j.k_p / sqrt(d)) v_p."""
+    Hq, d = len(q), len(q[0])
+    L, Hkv = len(K), len(K[0])
+    g = Hq // Hkv
+    out = []
+    for j in range(Hq):
+        kv = j // g
+        z = [sum(q[j][i] * K[p][kv][i] for i in range(d)) / math.sqrt(d) for p in range(L)]
+        m = max(z)
+        e = [math.exp(x - m) for x in z]
+        tot = sum(e)
+        out.append([sum(e[p] * V[p][kv][i] for p in range(L)) / tot for i in range(d)])
+    return np.array(out)
+
+
+def test_softmax_attention_matches_brute_force():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((4, 8))
+    K = rng.standard_normal((5, 2, 8)) * 3
+    V = rng.standard_normal((5, 2, 8))
+    out, lse = softmax_attention(q, K, V)
+    assert np.allclose(out, _brute(q.tolist(), K.tolist(), V.tolist()), rtol=0, atol=1e-13)
+    z = np.einsum("pd,d->p", K[:, 0], q[0]) / np.sqrt(8)
+    assert abs(lse[0] - math.log(sum(math.exp(x) for x in z))) < 1e-12
+
+
+def test_softmax_attention_matches_torch_sdpa_fp64():
+    rng = np.random.default_rng(1)
+    Hq, Hkv, L, d = 8, 2, 300, 128
+    q = rng.standard_normal((Hq, d))
+    K = rng.standard_normal((L, Hkv, d)) * 2
+    V = rng.standard_normal((L, Hkv, d))
+    out, _ = softmax_attention(q, K, V)
+    g = Hq // Hkv
+    tq = torch.from_numpy(q)[:, None, :]                             # [Hq, 1, d]
+    tk = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(g, 0)  # [Hq, L, d]
+    tv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(g, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[:, 0, :].numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_single_token_and_identical_keys():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 16))
+    V = rng.standard_normal((1, 1, 16))
+    K = rng.standard_normal((1, 1, 16))
+    out, _ = softmax_attention(q, K, V)
+    assert np.allclose(out, np.repeat(V[0], 4, axis=0), atol=1e-15)
+    K = np.repeat(rng.standard_normal((1, 1, 16)), 9, axis=0)
+    V = rng.standard_normal((9, 1, 16))
+    out, _ = softmax_attention(q, K, V)
+    assert np.allclose(out, np.repeat(V.mean(axis=0), 4, axis=0), atol=1e-14)
+
+
+def test_empty_context():
+    out, lse = softmax_attention(np.ones((2, 4)), np.zeros((0, 1, 4)), np.zeros((0, 1, 4)))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_merge_of_random_partition_equals_single_pass(seed):
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, L, d = 4, 1, 97, 32
+    q = rng.standard_normal((Hq, d))
+    K = rng.standard_normal((L, Hkv, d)) * 4
+    V = rng.standard_normal((L, Hkv, d))
+    want, want_lse = softmax_attention(q, K, V)
+    labels = rng.integers(0, 4, L)
+    parts = [np.nonzero(labels == r)[0] for r in range(4)] + [np.array([], dtype=np.int64)]
+    got, got_lse = merge([region_stats(q, K, V, p) for p in parts])
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    assert np.allclose(got_lse, want_lse, rtol=0, atol=1e-12)
+
+
+def test_rotation_leaves_unquantized_attention_unchanged():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((8, 128))
+    K = rng.standard_normal((50, 2, 128)) * 5
+    V = rng.standard_normal((50, 2, 128))
+    a, _ = softmax_attention(q, K, V)
+    b, _ = softmax_attention(rotate_f64(q, 64), rotate_f64(K, 64), V)
+    assert np.allclose(a, b, atol=1e-12)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = build_workload(get_config("tiny_1x1024"))
+    k, v = seq_kv(wl, 0)
+    q = seq_query(wl)
+    return wl, bf16_bits(q[0]), bf16_bits(k), bf16_bits(v)
+
+
+def test_regional_merge_equals_single_pass_on_tiny_workload(tiny):
+    wl, q, k, v = tiny
+    c = wl.cfg
+    cache = quantize_sequence(k, v, c.had_block, c.sink, c.recent)
+    a, la = attend(q, cache)
+    b, lb = attend_regions(q, cache)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    assert np.allclose(la, lb, rtol=0, atol=1e-12)
+
+
+def test_int8_region_is_more_accurate_than_int4(tiny):
+    wl, q, k, v = tiny
+    c = wl.cfg
+    cache = quantize_sequence(k, v, c.had_block, c.sink, c.recent)
+    K, V = dequantized_kv(cache)
+    from oracle.cache import rotated_keys_f32
+    from oracle.quant import dequantize
+    yk = rotated_keys_f32(k, c.had_block).astype(np.float64)
+    K4 = dequantize(cache.k4, cache.k4_scale, cache.k4_zero)
+    e8 = np.abs(K[cache.pos8] - yk[cache.pos8]).mean()
+    e4 = np.abs(K4[cache.pos8] - yk[cache.pos8]).mean()
+    assert e8 < e4 / 8
+
+
+def test_quantized_attention_error_vs_unquantized_is_reported(tiny):
+    wl, q, k, v = tiny
+    c = wl.cfg
+    a, _ = attend(q, quantize_sequence(k, v, c.had_block, c.sink, c.recent))
+    u, _ = unquantized_attention(q, k, v)
+    err = np.abs(a - u).max()
+    print(f"tiny workload: max-abs error of INT4/INT8 attention vs unquantized bf16 = {err:.4f}")
+    assert err < 2.0
+    # the rotated-basis scores equal the unrotated ones: rotation alone changes nothing
+    qr = rotated_query(q, c.had_block)
+    assert qr.shape == (8, 128)

@@ -1,0 +1,143 @@
+"""Pins for the oracle's per-token asymmetric quantizer."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.hadamard import fwht_f32
+from oracle.numerics import f16_bits_to_f64
+from oracle.quant import (INT4_QMAX, INT8_QMAX, bytes_per_token_head, dequantize,
+                          pack_int4, quantize, tie_near, unpack_int4)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _vectors(n, seed, outliers=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 128))
+    if outliers:
+        x[:, rng.choice(128, 4, replace=False)] *= 20
+    return x.astype(np.float32)
+
+
+def _brute_nearest(y, scale_h, zero_h, qmax):
+    """Exhaustive nearest grid level zero + c*scale over all qmax+1 codes (fp64,
+    exact for these magnitudes), ties to the even code."""
+    s = f16_bits_to_f64(scale_h)[:, None, None]
+    z = f16_bits_to_f64(zero_h)[:, None, None]
+    levels = z + s * np.arange(qmax + 1)[None, None, :]
+    dist = np.abs(y.astype(np.float64)[:, :, None] - levels)
+    cand = dist == dist.min(axis=-1, keepdims=True)
+    even = cand & (np.arange(qmax + 1) % 2 == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return code
+
+
+@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+def test_codes_are_nearest_levels(qmax):
+    y = fwht_f32(_vectors(3000, 1), 128)
+    c, sb, zb = quantize(y, qmax)
+    nonzero = f16_bits_to_f64(sb) > 0
+    brute = _brute_nearest(y[nonzero], sb[nonzero], zb[nonzero], qmax)
+    # levels outside [0, qmax] are clamped in both; compare inside the grid
+    mism = brute != c[nonzero]
+    ties = tie_near(y, qmax)[nonzero]
+    assert not np.any(mism & ~ties), int((mism & ~ties).sum())
+
+
+@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+def test_scale_and_zero_are_fp16_of_range_and_min(qmax):
+    y = _vectors(2000, 2)
+    c, sb, zb = quantize(y, qmax)
+    mn = y.min(axis=1).astype(np.float64)
+    mx = y.max(axis=1).astype(np.float64)
+    s = f16_bits_to_f64(sb)
+    z = f16_bits_to_f64(zb)
+    exact = (mx - mn) / qmax
+    assert np.all(np.abs(s - exact) <= 2.0 ** -11 * exact * 1.0001 + 1e-12)
+    assert np.all(np.abs(z - mn) <= 2.0 ** -11 * np.abs(mn) * 1.0001 + 2.0 ** -25)
+
+
+@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+def test_round_trip_bound(qmax):
+    y = fwht_f32(_vectors(3000, 3), 64)
+    c, sb, zb = quantize(y, qmax)
+    xh = dequantize(c, sb, zb)
+    s = f16_bits_to_f64(sb)
+    z = f16_bits_to_f64(zb)
+    mn = y.min(axis=1).astype(np.float64)
+    mx = y.max(axis=1).astype(np.float64)
+    slack = np.maximum.reduce([np.zeros_like(s), z - mn, mx - z - qmax * s])
+    bound = s / 2 + slack
+    err = np.abs(y.astype(np.float64) - xh).max(axis=1)
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-7)
+    # and in exact arithmetic (fp64 scale/zero, no fp16 rounding) the bound is scale/2
+    assert np.all(err <= s * 0.5 + slack + 1e-6 * np.abs(y).max(axis=1))
+
+
+@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+def test_grid_vectors_round_trip_exactly(qmax):
+    rng = np.random.default_rng(4)
+    n = 200
+    s = (rng.integers(1, 64, n) * 2.0 ** -8).astype(np.float16).astype(np.float32)
+    z = (rng.integers(-64, 64, n) * 2.0 ** -4).astype(np.float16).astype(np.float32)
+    codes = rng.integers(0, qmax + 1, (n, 128))
+    codes[:, 0] = 0
+    codes[:, 1] = qmax
+    y = (z[:, None] + codes * s[:, None]).astype(np.float32)
+    assert np.array_equal(y.astype(np.float64), z[:, None].astype(np.float64) + codes * s[:, None].astype(np.float64))
+    c, sb, zb = quantize(y, qmax)
+    assert np.array_equal(c, codes)
+    assert np.array_equal(f16_bits_to_f64(sb), s.astype(np.float64))
+    assert np.array_equal(f16_bits_to_f64(zb), z.astype(np.float64))
+    assert np.array_equal(dequantize(c, sb, zb), y.astype(np.float64))
+
+
+@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+def test_zero_range_guard(qmax):
+    y = np.stack([np.full(128, 0.3, np.float32), np.zeros(128, np.float32),
+                  np.full(128, -7.25, np.float32)])
+    c, sb, zb = quantize(y, qmax)
+    assert np.all(c == 0)
+    assert np.all(f16_bits_to_f64(sb) == 0)
+    assert np.array_equal(f16_bits_to_f64(zb), np.array([0.3, 0.0, -7.25], np.float32).astype(np.float16).astype(np.float64))
+    assert np.all(np.isfinite(dequantize(c, sb, zb)))
+
+
+def test_tiny_range_underflowing_fp16_scale_is_guarded():
+    y = np.full((1, 128), 1.0, np.float32)
+    y[0, 5] = np.nextafter(np.float32(1.0), np.float32(2.0))   # range 1.2e-7: fp16 scale underflows to 0
+    c, sb, zb = quantize(y, INT4_QMAX)
+    assert f16_bits_to_f64(sb)[0] == 0 and np.all(c == 0)
+
+
+def test_rotation_reduces_error_on_outlier_keys():
+    """SAW-INT4 section 2: rotating blocks before 4-bit quantization spreads outlier
+    channels and lowers the quantization error (checked on outlier-heavy vectors)."""
+    x = _vectors(2000, 5)
+    errs = {}
+    for h in (1, 128):
+        y = fwht_f32(x, h)
+        c, sb, zb = quantize(y, INT4_QMAX)
+        errs[h] = np.mean((dequantize(c, sb, zb) - y) ** 2)
+    assert errs[128] < 0.25 * errs[1]
+
+
+def test_pack_unpack_round_trip():
+    rng = np.random.default_rng(6)
+    c = rng.integers(0, 16, (50, 128)).astype(np.uint8)
+    p = pack_int4(c)
+    assert p.shape == (50, 64)
+    assert np.array_equal(p[:, 0], c[:, 0] | (c[:, 1] << 4))
+    assert np.array_equal(unpack_int4(p), c)
+
+
+def test_storage_accounting_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "storage_accounting.json")))
+    d = g["group_dims"]
+    per_elem_bits = bytes_per_token_head(d, 4) * 8 / (2 * d)
+    assert per_elem_bits == g["bits_per_element"] == g["code_bits"] + g["param_bits_per_group"] / d
+    assert bytes_per_token_head(128, 4) == 136
+    assert bytes_per_token_head(128, 8) == 264
