@@ -1,0 +1,215 @@
+// C ABI of the INT4 KV-cache library: argument checks, buffer sizes, launches.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/kvq.h"
+#include <stdarg.h>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+kvq_status fail(kvq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kvq_status ok() {
+    g_err[0] = '\0';
+    return KVQ_OK;
+}
+
+constexpr int kMinUnitsPerWorker = 8;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_max_workers[kMaxDevices];
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+kvq_status check_cache(const kvq_cache *c) {
+    if (!c) return fail(KVQ_ERR_NULL, "cache descriptor is NULL");
+    if (c->head_dim != kvq::kHeadDim)
+        return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
+    if (c->num_kv_heads < 1) return fail(KVQ_ERR_SHAPE, "num_kv_heads %d < 1", c->num_kv_heads);
+    if (c->page_size < 16 || c->page_size % 16 != 0)
+        return fail(KVQ_ERR_SHAPE, "page_size %d is not a positive multiple of 16", c->page_size);
+    if (c->num_pages < 0 || c->num_slots < 0) return fail(KVQ_ERR_SHAPE, "negative num_pages/num_slots");
+    if (!is_pow2(c->had_block) || c->had_block > 128)
+        return fail(KVQ_ERR_SHAPE, "had_block %d is not a power of two in [1, 128]", c->had_block);
+    if (c->sink < 0 || c->recent < 0) return fail(KVQ_ERR_SHAPE, "negative sink/recent");
+    if ((int64_t)c->sink + c->recent > (1 << 20)) return fail(KVQ_ERR_SHAPE, "sink + recent too large");
+    return KVQ_OK;
+}
+
+int nr8_of(const kvq_cache *c) { return kvq::ceil_div(c->sink + c->recent, kvq::kSub); }
+
+float inv_sqrt(int h) { return (float)(1.0 / sqrt((double)h)); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+kvq_status max_workers(int *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
+    int v = g_max_workers[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        hipError_t e = kvq::decode_max_workers(&v);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        g_max_workers[dev].store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return KVQ_OK;
+}
+
+struct WsLayout {
+    size_t prefix_off, piece_off, total;
+};
+
+WsLayout ws_layout(const kvq_cache *c, int B, int g, int workers) {
+    WsLayout l;
+    l.prefix_off = kvq::kWsHeaderBytes;
+    l.piece_off = align256(l.prefix_off + (size_t)B * sizeof(int64_t));
+    const size_t pieces = (size_t)workers + (size_t)B * c->num_kv_heads;
+    l.total = align256(l.piece_off + pieces * g * kvq::kPieceStride * sizeof(float));
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_int4_pool_bytes(const kvq_cache *c) {
+    if (check_cache(c) != KVQ_OK) return 0;
+    return (size_t)c->num_pages * c->num_kv_heads * (c->page_size / kvq::kSub) * kvq::kSub4Bytes;
+}
+
+size_t kvq_int8_pool_bytes(const kvq_cache *c) {
+    if (check_cache(c) != KVQ_OK) return 0;
+    return (size_t)c->num_slots * c->num_kv_heads * nr8_of(c) * kvq::kSub8Bytes;
+}
+
+kvq_status kv_quant_append(const kvq_cache *c, const uint16_t *k, const uint16_t *v,
+                           const int32_t *slot, const int32_t *pos, int32_t T,
+                           const int32_t *block_table, int32_t bt_stride,
+                           const int32_t *len_after, void *stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (T < 0) return fail(KVQ_ERR_SHAPE, "T = %d < 0", T);
+    if (T == 0) return ok();
+    if ((int64_t)T * c->num_kv_heads > ((int64_t)1 << 31) - 4)
+        return fail(KVQ_ERR_SHAPE, "T * num_kv_heads too large for one call");
+    if (!k || !v || !slot || !pos || !block_table || !len_after)
+        return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
+    if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
+    if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
+    if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+    kvq::AppendArgs a;
+    a.k = k;
+    a.v = v;
+    a.slot = slot;
+    a.pos = pos;
+    a.T = T;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.len_after = len_after;
+    a.int4_pool = static_cast<uint8_t *>(c->int4_pool);
+    a.int8_pool = static_cast<uint8_t *>(c->int8_pool);
+    a.H = c->num_kv_heads;
+    a.P = c->page_size;
+    a.h = c->had_block;
+    a.s = c->sink;
+    a.w = c->recent;
+    a.nr8 = nr8_of(c);
+    a.inv_sqrt_h = inv_sqrt(c->had_block);
+    hipError_t e = kvq::launch_quant_append(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "quant-append launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num_q_heads) {
+    if (check_cache(c) != KVQ_OK || B < 0 || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
+    int workers = 0;
+    if (max_workers(&workers) != KVQ_OK) return 0;
+    return ws_layout(c, B, num_q_heads / c->num_kv_heads, workers).total;
+}
+
+kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads,
+                          const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
+                          const int32_t *ctx_len, int32_t B, float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (B < 0) return fail(KVQ_ERR_SHAPE, "B = %d < 0", B);
+    if (num_q_heads < 1 || num_q_heads % c->num_kv_heads)
+        return fail(KVQ_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, c->num_kv_heads);
+    const int g = num_q_heads / c->num_kv_heads;
+    if (g > 16) return fail(KVQ_ERR_UNSUPPORTED, "query group %d > 16", g);
+    if (B == 0) return ok();
+    if ((int64_t)B * num_q_heads > ((int64_t)1 << 31) - 1) return fail(KVQ_ERR_SHAPE, "B * num_q_heads too large");
+    if (!q || !slot || !block_table || !ctx_len || !out)
+        return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
+    if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
+    if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
+    if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
+    int workers = 0;
+    st = max_workers(&workers);
+    if (st != KVQ_OK) return st;
+    const WsLayout l = ws_layout(c, B, g, workers);
+    if (workspace_bytes < l.total)
+        return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    kvq::DecodeArgs a;
+    a.q = q;
+    a.Hq = num_q_heads;
+    a.g = g;
+    a.slot = slot;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.ctx_len = ctx_len;
+    a.B = B;
+    a.int4_pool = static_cast<const uint8_t *>(c->int4_pool);
+    a.int8_pool = static_cast<const uint8_t *>(c->int8_pool);
+    a.H = c->num_kv_heads;
+    a.P = c->page_size;
+    a.h = c->had_block;
+    a.s = c->sink;
+    a.w = c->recent;
+    a.nr8 = nr8_of(c);
+    a.inv_sqrt_h = inv_sqrt(c->had_block);
+    a.max_workers = workers;
+    a.min_units = kMinUnitsPerWorker;
+    a.ws_header = reinterpret_cast<int64_t *>(ws);
+    a.ws_prefix = reinterpret_cast<int64_t *>(ws + l.prefix_off);
+    a.ws_piece = reinterpret_cast<float *>(ws + l.piece_off);
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = kvq::launch_decode(a, workers, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char *kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_NULL: return "null pointer";
+        case KVQ_ERR_SHAPE: return "bad shape or size";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported";
+        case KVQ_ERR_WORKSPACE: return "workspace too small";
+        case KVQ_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *kvq_last_error(void) { return g_err; }
+
+}  // extern "C"

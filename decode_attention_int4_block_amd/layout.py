@@ -1,0 +1,65 @@
+"""Host-side readers of the INT4 / INT8 cache layouts documented in include/kvq.h.
+
+Used to inspect what the GPU wrote (tests, debugging); nothing here runs on the
+decode path.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+SUB = 16
+SUB4_BYTES = 2176
+SUB8_BYTES = 4224
+
+
+def sub4_index(page, kv_head, row, num_kv_heads: int, page_size: int):
+    """Index of the INT4 subblock holding (page, kv_head, row) in units of SUB4_BYTES."""
+    page = np.asarray(page, dtype=np.int64)
+    return (page * num_kv_heads + np.asarray(kv_head, np.int64)) * (page_size // SUB) + np.asarray(row, np.int64) // SUB
+
+
+def sub8_index(slot, kv_head, entry, num_kv_heads: int, nr8: int):
+    slot = np.asarray(slot, dtype=np.int64)
+    return (slot * num_kv_heads + np.asarray(kv_head, np.int64)) * nr8 + np.asarray(entry, np.int64) // SUB
+
+
+def decode_sub4(blocks: np.ndarray, tok) -> dict:
+    """Codes and fp16 params of token `tok` (0..15) of each INT4 subblock [N, 2176]."""
+    blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, SUB4_BYTES)
+    t = np.asarray(tok, dtype=np.int64).reshape(-1)
+    N = blocks.shape[0]
+    rows = np.arange(N)[:, None]
+    kb = blocks[rows, 64 * t[:, None] + np.arange(64)[None, :]]
+    kc = np.empty((N, 128), np.uint8)
+    kc[:, 0::2] = kb & 0x0F
+    kc[:, 1::2] = kb >> 4
+    G, r = t // 4, t % 4
+    n = np.arange(16)
+    vc = np.empty((N, 128), np.uint8)
+    for c in range(4):
+        off = 1024 + 4 * ((G[:, None] * 16 + n[None, :]) * 4 + c) + r[:, None]
+        byte = blocks[rows, off]
+        vc[:, 32 * c + n] = byte & 0x0F
+        vc[:, 32 * c + 16 + n] = byte >> 4
+    kp = blocks[rows, 2048 + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    vp = blocks[rows, 2112 + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])
+
+
+def decode_sub8(blocks: np.ndarray, ent) -> dict:
+    """Codes and fp16 params of entry `ent` (0..15) of each INT8 subblock [N, 4224]."""
+    blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, SUB8_BYTES)
+    e = np.asarray(ent, dtype=np.int64).reshape(-1)
+    N = blocks.shape[0]
+    rows = np.arange(N)[:, None]
+    kc = blocks[rows, 128 * e[:, None] + np.arange(128)[None, :]]
+    G, r = e // 4, e % 4
+    n = np.arange(16)
+    vc = np.empty((N, 128), np.uint8)
+    for c in range(8):
+        off = 2048 + 4 * ((G[:, None] * 16 + n[None, :]) * 8 + c) + r[:, None]
+        vc[:, 16 * c + n] = blocks[rows, off]
+    kp = blocks[rows, 4096 + 4 * e[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    vp = blocks[rows, 4160 + 4 * e[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])

@@ -1,0 +1,193 @@
+/*
+ * kvq.h -- C ABI of the INT4 KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations make up one decode step of calibration-free 4-bit KV-cache
+ * quantization with a bounded INT8 side cache:
+ *
+ *   kv_quant_append -- quantize new key/value vectors on the fly and write them
+ *                      into a paged INT4 cache (plus the INT8 side cache for
+ *                      sink and recent positions);
+ *   kv_decode_attn  -- decode attention that reads the packed codes directly,
+ *                      attends the INT4 region and the INT8 region as disjoint
+ *                      sets and merges them by log-sum-exp.
+ *
+ * The method: KV4-RL ("Unlocking Faster Asynchronous Rollouts for RLVR with
+ * INT4 KV Cache Quantization"), sections "Key Contributions" item 4 and
+ * "Methodology in Plain English"; the block-diagonal Hadamard rotation of keys
+ * is SAW-INT4 ("System-Aware 4-Bit KV-Cache Quantization for Real-World LLM
+ * Serving"), section 2.
+ *
+ * General rules
+ *   - Every pointer argument except `cache` is DEVICE memory owned by the caller
+ *     (`cache` itself is a host struct that holds device pointers).  The library
+ *     never allocates, frees or synchronizes, keeps no mutable global state
+ *     except a per-device cache of device properties, and may be called from
+ *     several host threads.  Buffers must stay valid until the stream has
+ *     passed the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Host-side argument checks run before anything is enqueued; on failure a
+ *     status is returned and nothing is enqueued.  A failed kernel launch is
+ *     reported as KVQ_ERR_HIP.  Device-side data (positions in range, valid
+ *     block-table entries, slots in range) is a precondition and is NOT
+ *     checked; violating it is undefined behaviour.
+ *   - bf16 and fp16 values are passed as uint16_t bit patterns.
+ *   - No C++ exception crosses this interface.
+ *
+ * Parameters of the method (kvq_cache):
+ *   head_dim   = 128 (one quantization group per 128-dim token-head vector);
+ *   had_block  = h, the Hadamard block size: a power of two in [1, 128];
+ *   sink       = s, recent = w: positions [0, s) and the last w positions of a
+ *                sequence are attended from the INT8 side cache, the rest from
+ *                INT4.  s + w may be 0 (INT4 only).
+ *
+ * ---------------------------------------------------------------------------
+ * Quantization (both caches).  For a 128-dim vector y (keys: the fp32
+ * block-Hadamard rotation of the bf16 key, butterfly strides 1, 2, ..., h/2 in
+ * that order, then one multiply by the fp32 value nearest 1/sqrt(h); values:
+ * the bf16 value itself):
+ *   mn = min y, mx = max y, scale_f = fp32((mx - mn) / qmax), qmax = 15 or 255;
+ *   scale = fp16(scale_f), zero = fp16(mn)         (round to nearest even);
+ *   code_i = 0 if scale == 0, else clamp(rint(fp32(y_i - zero) / scale), 0, qmax)
+ *   dequantized y_i = scale * code_i + zero.
+ *
+ * Regions.  For a sequence of length L: INT8 region = [0, min(s, L)) U
+ * [max(s, L - w), L); INT4 region = [s, L - w) when non-empty.  Every position
+ * is stored in INT4; INT8 copies live in a ring of s + w entries: position
+ * p < s -> entry p, other positions -> entry s + (p - s) mod w.  An append of
+ * position p writes its INT8 copy iff p < s or p >= len_after - w.
+ *
+ * ---------------------------------------------------------------------------
+ * INT4 pool layout (int4_pool, kvq_int4_pool_bytes bytes, 256-byte aligned).
+ *   A page of P tokens (P % 16 == 0) and one KV head is P/16 "subblocks" of 16
+ *   tokens; subblock j of (page, kv_head) starts at byte
+ *       ((page * num_kv_heads + kv_head) * (P / 16) + j) * 2176
+ *   and holds token rows t = 0..15 (position = page_row_base + 16 j + t):
+ *     [   0, 1024) key codes, token-major: byte 64 t + i holds the codes of
+ *                  rotated dims 2i (low nibble) and 2i + 1 (high nibble);
+ *     [1024, 2048) value codes, token-fastest: with G = t / 4 and r = t % 4,
+ *                  byte 4 * ((G * 16 + n) * 4 + c) + r holds value dim
+ *                  32 c + n (low nibble) and 32 c + 16 + n (high nibble),
+ *                  for n = 0..15, c = 0..3;
+ *     [2048, 2112) key   (scale, zero) fp16 pairs, 4 bytes per token;
+ *     [2112, 2176) value (scale, zero) fp16 pairs, 4 bytes per token.
+ *   2176 bytes / (16 tokens * 256 elements) = 4.25 bits per element.
+ *
+ * INT8 side-cache layout (int8_pool, kvq_int8_pool_bytes bytes).
+ *   Each (slot, kv_head) owns NR = ceil((s + w) / 16) subblocks of 16 ring
+ *   entries; subblock j starts at byte
+ *       ((slot * num_kv_heads + kv_head) * NR + j) * 4224
+ *   and holds entries e = 0..15 (ring entry 16 j + e):
+ *     [   0, 2048) key codes, entry-major: byte 128 e + d = code of rotated dim d;
+ *     [2048, 4096) value codes, entry-fastest: with G = e / 4, r = e % 4,
+ *                  byte 4 * ((G * 16 + n) * 8 + c) + r = code of value dim
+ *                  16 c + n, for n = 0..15, c = 0..7;
+ *     [4096, 4160) key   (scale, zero) fp16 pairs, 4 bytes per entry;
+ *     [4160, 4224) value (scale, zero) fp16 pairs, 4 bytes per entry.
+ *
+ * Block table: int32 [num_slots][bt_stride], row = slot; entry i is the page
+ * holding positions [i P, (i + 1) P) of that slot's sequence.  Only entries
+ * i < ceil(L / P) are read.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    KVQ_ERR_SHAPE = 2,       /* sizes are inconsistent or out of range            */
+    KVQ_ERR_UNSUPPORTED = 3, /* valid request outside what is implemented         */
+    KVQ_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required           */
+    KVQ_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed        */
+} kvq_status;
+
+typedef struct {
+    int32_t num_kv_heads;    /* >= 1                                              */
+    int32_t head_dim;        /* must be 128                                       */
+    int32_t page_size;       /* tokens per page, multiple of 16, >= 16            */
+    int32_t num_pages;       /* pages in int4_pool                                */
+    int32_t num_slots;       /* sequence slots (rows of the block table / INT8)   */
+    int32_t had_block;       /* Hadamard block size h: power of two in [1, 128]   */
+    int32_t sink;            /* s >= 0                                            */
+    int32_t recent;          /* w >= 0                                            */
+    void *int4_pool;         /* device, kvq_int4_pool_bytes(cache) bytes          */
+    void *int8_pool;         /* device, kvq_int8_pool_bytes(cache) bytes; may be
+                                NULL only when sink + recent == 0                 */
+} kvq_cache;
+
+/* Bytes of the INT4 pool / INT8 side cache for this descriptor (0 on bad input). */
+size_t kvq_int4_pool_bytes(const kvq_cache *cache);
+size_t kvq_int8_pool_bytes(const kvq_cache *cache);
+
+/*
+ * kv_quant_append -- quantize T new (token, all KV heads) key/value vectors and
+ * append them (KV4-RL, "Methodology in Plain English": every new K/V vector is
+ * quantized on the fly; SAW-INT4 section 2: rotation and quantization fused).
+ *
+ *   k, v        bf16 [T][num_kv_heads][128], row-major (device).
+ *   slot        int32 [T]: slot of each token's sequence (device).
+ *   pos         int32 [T]: position of each token in its sequence (device).
+ *   T           number of tokens; T == 0 is a no-op returning KVQ_OK.
+ *   block_table int32 [num_slots][bt_stride] (device).
+ *   len_after   int32 [num_slots]: sequence length of each slot after this call
+ *               (device); only entries of slots named in `slot` are read.
+ *
+ * Positions within one call must be distinct per slot.  Each (token, head)
+ * has exactly one writer; tokens of different calls on one stream are
+ * ordered by the stream.
+ */
+kvq_status kv_quant_append(const kvq_cache *cache,
+                           const uint16_t *k, const uint16_t *v,
+                           const int32_t *slot, const int32_t *pos, int32_t T,
+                           const int32_t *block_table, int32_t bt_stride,
+                           const int32_t *len_after, void *stream);
+
+/* Workspace bytes kv_decode_attn needs for B rows and num_q_heads query heads
+ * on the current HIP device (0 on bad input). */
+size_t kv_decode_attn_workspace_bytes(const kvq_cache *cache, int32_t B, int32_t num_q_heads);
+
+/*
+ * kv_decode_attn -- one decode step of attention for B rows (KV4-RL, "Key
+ * Contributions" item 4: disjoint INT4 and INT8 regions combined through
+ * regional softmax statistics; "Methodology in Plain English": queries are
+ * rotated to match the rotated keys, packed codes are consumed directly and
+ * scale/offset are applied after the dot-product reduction).
+ *
+ *   q            bf16 [B][num_q_heads][128] (device), unrotated.
+ *   num_q_heads  multiple of num_kv_heads, group g = num_q_heads / num_kv_heads
+ *                with 1 <= g <= 16; query head j uses KV head j / g.
+ *   slot         int32 [B] (device): slot of each row.
+ *   block_table  int32 [num_slots][bt_stride] (device).
+ *   ctx_len      int32 [B] (device): context length L of each row, counting any
+ *                token appended this step; 0 <= L <= bt_stride * page_size.
+ *   out          fp32 [B][num_q_heads][128] (device): softmax(q.k / sqrt(128)) v.
+ *                Rows with L == 0 get 0.
+ *   lse          fp32 [B][num_q_heads] (device) or NULL: natural-log
+ *                log-sum-exp of the scaled scores; -inf when L == 0.
+ *   workspace    device scratch of at least kv_decode_attn_workspace_bytes();
+ *                contents need no initialization and are overwritten.
+ */
+kvq_status kv_decode_attn(const kvq_cache *cache,
+                          const uint16_t *q, int32_t num_q_heads,
+                          const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
+                          const int32_t *ctx_len, int32_t B,
+                          float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *kvq_status_string(kvq_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

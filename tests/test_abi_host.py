@@ -1,0 +1,104 @@
+"""The C ABI library loads without a GPU, exports every symbol include/kvq.h
+declares, and rejects bad arguments on the host before enqueuing anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof", "defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from decode_attention_int4_block_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return _lib.load()
+
+
+def test_header_declares_the_two_entry_points():
+    names = _declared_functions()
+    assert "kv_quant_append" in names and "kv_decode_attn" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from decode_attention_int4_block_amd import _lib
+    names = _declared_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def _desc(**kw):
+    from decode_attention_int4_block_amd._lib import KvqCache
+    d = dict(num_kv_heads=8, head_dim=128, page_size=16, num_pages=100, num_slots=4,
+             had_block=128, sink=4, recent=128, int4_pool=None, int8_pool=None)
+    d.update(kw)
+    return KvqCache(**d)
+
+
+def test_pool_sizes_follow_the_documented_layout(lib):
+    d = _desc()
+    assert lib.kvq_int4_pool_bytes(ctypes.byref(d)) == 100 * 8 * 1 * 2176
+    assert lib.kvq_int8_pool_bytes(ctypes.byref(d)) == 4 * 8 * 9 * 4224
+    d64 = _desc(page_size=64)
+    assert lib.kvq_int4_pool_bytes(ctypes.byref(d64)) == 100 * 8 * 4 * 2176
+    # 4.25 bits per element: 2176 bytes hold 16 tokens x 256 K+V elements
+    assert 2176 * 8 / (16 * 256) == 4.25
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 64), ("page_size", 24), ("page_size", 0),
+                                         ("had_block", 3), ("had_block", 256), ("sink", -1),
+                                         ("num_kv_heads", 0)])
+def test_bad_descriptors_are_rejected(lib, field, value):
+    d = _desc(**{field: value})
+    assert lib.kvq_int4_pool_bytes(ctypes.byref(d)) == 0
+    st = lib.kv_quant_append(ctypes.byref(d), None, None, None, None, 1, None, 1, None, None)
+    assert st in (2, 3)
+    assert lib.kvq_last_error()
+
+
+def test_append_argument_checks(lib):
+    d = _desc(int4_pool=0x1000, int8_pool=0x2000)
+    assert lib.kv_quant_append(ctypes.byref(d), None, None, None, None, 0, None, 1, None, None) == 0
+    assert lib.kv_quant_append(ctypes.byref(d), None, None, None, None, -1, None, 1, None, None) == 2
+    assert lib.kv_quant_append(ctypes.byref(d), None, None, None, None, 5, None, 1, None, None) == 1
+    p = ctypes.c_void_p(0x3000)
+    assert lib.kv_quant_append(ctypes.byref(d), p, p, p, p, 5, p, 0, p, None) == 2
+    d0 = _desc(int4_pool=0x1000, int8_pool=None)
+    assert lib.kv_quant_append(ctypes.byref(d0), p, p, p, p, 5, p, 4, p, None) == 1
+    assert lib.kv_quant_append(None, p, p, p, p, 5, p, 4, p, None) == 1
+
+
+def test_decode_argument_checks(lib):
+    d = _desc(int4_pool=0x1000, int8_pool=0x2000)
+    p = ctypes.c_void_p(0x3000)
+    # group 32 > 16 is unsupported; query heads not a multiple of KV heads
+    assert lib.kv_decode_attn(ctypes.byref(d), p, 256, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
+    assert lib.kv_decode_attn(ctypes.byref(d), p, 12, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 2
+    assert lib.kv_decode_attn(ctypes.byref(d), p, 32, p, p, 4, p, -1, p, None, p, 1 << 30, None) == 2
+    assert lib.kv_decode_attn(ctypes.byref(d), p, 32, p, p, 4, p, 0, p, None, p, 1 << 30, None) == 0
+    assert lib.kv_decode_attn(ctypes.byref(d), None, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 1
+    assert lib.kv_decode_attn(ctypes.byref(d), p, 32, p, p, 4, p, 2, p, None, None, 1 << 30, None) == 4
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.kvq_status_string(s)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from decode_attention_int4_block_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -34,6 +34,9 @@ def draw_lengths(cfg: WorkloadConfig, rng: np.random.Generator) -> np.ndarray:
     a = cfg.length_args
     if cfg.lengths == "fixed":
         L = np.full(B, a[0], dtype=np.int64)
+    elif cfg.lengths == "explicit":
+        L = np.asarray(a, dtype=np.int64)
+        assert len(L) == B
     elif cfg.lengths == "lognormal":
         median, sigma, lo, hi = a
         z = rng.standard_normal(B)
