@@ -1,0 +1,238 @@
+"""Benchmark: one decode step of INT4/INT8 KV-cache quantize-append + decode attention.
+
+A step is the whole hot path over one batch: quantize-append of one new token
+per row (kv_quant_append) followed by decode attention over the quantized
+cache (kv_decode_attn).  The workload is the Qwen3-8B-shaped async-rollout
+batch (256 slots, 32 query / 8 KV heads, Pareto(1.5) lengths from 512 clipped
+at 32K, 16-token pages, h = 128, s = 4, w = 128), with inputs resident in HBM.
+
+The steps cycle through `--layers` independent copies of the cache, as the
+layers of a model would, so the working set (~0.43 GB per copy) exceeds the
+256 MB Infinity Cache and each step streams its cache from HBM.
+
+Prints one JSON line (see the fields at the end of main()).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective KV GB/s + tokens·heads/s; % of MI355X HBM peak"
+HBM_PEAK_GBPS = 8000.0
+BYTES_INT4 = 136     # K+V codes + fp16 scale/zero of one (token, KV head), INT4
+BYTES_INT8 = 264     # same, INT8
+
+
+def region_sizes(L, s, w):
+    L = np.asarray(L, np.int64)
+    n8 = np.minimum(L, s + w)
+    n4 = np.maximum(L - w - s, 0)
+    return n4, n8
+
+
+def decode_bytes(wl):
+    """Algorithmic bytes one decode-attention launch must move."""
+    c = wl.cfg
+    n4, n8 = region_sizes(wl.lengths, c.sink, c.recent)
+    kv = int((c.num_kv_heads * (BYTES_INT4 * n4 + BYTES_INT8 * n8)).sum())
+    P = wl.page_size
+    lo4, hi4 = c.sink, wl.lengths - c.recent
+    pages = np.where(hi4 > lo4, (hi4 + P - 1) // P - lo4 // P, 0)
+    bt = int(4 * pages.sum())
+    q = c.batch * c.num_q_heads * c.head_dim * 2
+    out = c.batch * c.num_q_heads * (c.head_dim + 1) * 4
+    meta = c.batch * 8
+    return dict(kv=kv, total=kv + bt + q + out + meta, bf16_equiv=int((wl.lengths * c.num_kv_heads * 512).sum()))
+
+
+def append_bytes(wl):
+    c = wl.cfg
+    n = int((wl.lengths >= 1).sum())
+    ins = n * c.num_kv_heads * c.head_dim * 2 * 2
+    # every appended token is written to INT4; the step token is always in the recent window
+    outs = n * c.num_kv_heads * (BYTES_INT4 + (BYTES_INT8 if c.sink + c.recent > 0 else 0))
+    return ins + outs
+
+
+def cpu_baseline(wl, dw, budget_s=12.0):
+    """The oracle as it stands, on a seeded sample of rows, single-threaded BLAS.
+
+    The oracle has no incremental cache: its decode step for a row quantizes
+    the row's keys/values (the append) and attends with fp64 softmax.
+    """
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import attend
+    from oracle.cache import quantize_sequence
+    from workloads import bf16_bits, seq_kv
+
+    c = wl.cfg
+    order = np.random.default_rng(12345).permutation(c.batch)
+    qb = bf16_bits(dw.q)
+    t_total = 0.0
+    done_rows, tok_heads, kvbytes = 0, 0, 0
+    with threadpool_limits(limits=1):
+        for b in order:
+            b = int(b)
+            k, v = seq_kv(wl, b, device="cpu")
+            kb, vb = bf16_bits(k), bf16_bits(v)
+            L = int(wl.lengths[b])
+            t0 = time.perf_counter()
+            attend(qb[b], quantize_sequence(kb, vb, c.had_block, c.sink, c.recent))
+            t_total += time.perf_counter() - t0
+            done_rows += 1
+            tok_heads += L * c.num_q_heads
+            n4, n8 = region_sizes([L], c.sink, c.recent)
+            kvbytes += int(c.num_kv_heads * (BYTES_INT4 * n4[0] + BYTES_INT8 * n8[0]))
+            if t_total >= budget_s:
+                break
+    return dict(value=round(kvbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                tokens_heads_per_s=round(tok_heads / t_total, 1),
+                sample=f"{done_rows} of {c.batch} rows in seeded order, one decode step each "
+                       f"(oracle quantization of the row + fp64 attention), {t_total:.1f} s, 1 thread")
+
+
+def traffic_from_profile(kernel_src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    p = os.path.join(ROOT, "profiles", "decode_split_qwen3_8b_async_256_pmc.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256") != kernel_src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_8b_async_256")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path is data-parallel over decode rows and is not run across GPUs here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_int4_block_amd.harness import DeviceWorkload
+    from workloads import build_workload, get_config
+
+    cfg = get_config(args.workload)
+    wl = build_workload(cfg)
+    print(f"[bench] workload {cfg.name}: B={cfg.batch} tokens={int(wl.lengths.sum())} "
+          f"max_len={wl.max_len}", file=sys.stderr, flush=True)
+    t0 = time.time()
+    dw = DeviceWorkload(wl, device="cuda", gen_device="cuda")
+    dw.prefill()
+    # independent copies of the cache for the rotating "layers"
+    layers = [dw.cache]
+    from decode_attention_int4_block_amd import QuantKVCache
+    for _ in range(args.layers - 1):
+        c2 = QuantKVCache(cfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
+                          cfg.had_block, cfg.sink, cfg.recent)
+        c2.int4_pool.copy_(dw.cache.int4_pool)
+        c2.int8_pool.copy_(dw.cache.int8_pool)
+        layers.append(c2)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill + {args.layers} cache copies in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    def step(i, ev=None):
+        dw.cache = layers[i % len(layers)]
+        if ev is not None:
+            ev[0].record()
+        dw.append_step()
+        if ev is not None:
+            ev[1].record()
+        dw.decode_step()
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    db = decode_bytes(wl)
+    ab = append_bytes(wl)
+    tok_heads = float((wl.lengths * cfg.num_q_heads).sum())
+    step_s = ms_per_step / 1e3
+    value = db["kv"] / step_s / 1e9
+    dec_avg_s = float(dec_ms.mean()) / 1e3
+    achieved = db["total"] / dec_avg_s / 1e9
+
+    src = open(os.path.join(ROOT, "decode_attention_int4_block_amd", "csrc", "decode.hip"), "rb").read()
+    traffic = traffic_from_profile(hashlib.sha256(src).hexdigest())
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-split-f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "batch": cfg.batch, "num_q_heads": cfg.num_q_heads,
+            "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "page_size": wl.page_size,
+            "had_block": cfg.had_block, "sink": cfg.sink, "recent": cfg.recent,
+            "lengths": "pareto(xm=512, alpha=1.5) clipped at 32768", "total_tokens": int(wl.lengths.sum()),
+            "rotating_cache_copies": args.layers,
+        },
+        "tokens_heads_per_s": round(tok_heads / step_s, 1),
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "decode_us": round(float(dec_ms.mean()) * 1e3, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                              round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
+        "append_us": round(float(app_ms.mean()) * 1e3, 2),
+        "decode_kv_bytes": db["kv"],
+        "decode_algorithmic_bytes": db["total"],
+        "append_algorithmic_bytes": ab,
+        "bf16_equiv_GBps_decode": round(db["bf16_equiv"] / dec_avg_s / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kv_decode_attn (decode_split_kernel + decode_combine_kernel)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, dw)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

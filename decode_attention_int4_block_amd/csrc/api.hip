@@ -39,8 +39,8 @@ kvq_status check_cache(const kvq_cache *c) {
     if (c->head_dim != kvq::kHeadDim)
         return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
     if (c->num_kv_heads < 1) return fail(KVQ_ERR_SHAPE, "num_kv_heads %d < 1", c->num_kv_heads);
-    if (c->page_size < 16 || c->page_size % 16 != 0)
-        return fail(KVQ_ERR_SHAPE, "page_size %d is not a positive multiple of 16", c->page_size);
+    if (c->page_size < 16 || !is_pow2(c->page_size))
+        return fail(KVQ_ERR_SHAPE, "page_size %d is not a power of two >= 16", c->page_size);
     if (c->num_pages < 0 || c->num_slots < 0) return fail(KVQ_ERR_SHAPE, "negative num_pages/num_slots");
     if (!is_pow2(c->had_block) || c->had_block > 128)
         return fail(KVQ_ERR_SHAPE, "had_block %d is not a power of two in [1, 128]", c->had_block);
@@ -181,6 +181,7 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     a.int8_pool = static_cast<const uint8_t *>(c->int8_pool);
     a.H = c->num_kv_heads;
     a.P = c->page_size;
+    a.logP = __builtin_ctz((unsigned)c->page_size);
     a.h = c->had_block;
     a.s = c->sink;
     a.w = c->recent;

@@ -29,13 +29,14 @@ constexpr size_t kWsHeaderBytes = 256;
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Work of one row: INT4 steps of 32 positions aligned to multiples of 32, and
-// INT8 steps of 32 ring entries that weigh two units each (their bytes are ~2x).
+// Work of one row, in units of roughly equal bytes: INT4 steps of 32 positions
+// aligned to multiples of 32 (2 x 2176 B) and INT8 steps of one 16-entry
+// subblock (4224 B).
 struct RowPlan {
     int lo4, hi4;   // INT4 region [lo4, hi4)
     int k0, n4;     // first 32-position step index and number of INT4 steps
     int n8e, n8;    // valid ring entries and INT8 steps
-    int cost;       // n4 + 2 * n8 units
+    int cost;       // n4 + n8 units
 };
 
 __host__ __device__ inline RowPlan row_plan(int L, int s, int w) {
@@ -52,8 +53,8 @@ __host__ __device__ inline RowPlan row_plan(int L, int s, int w) {
     int cap = s + w;
     r.n8e = L < cap ? L : cap;
     if (r.n8e < 0) r.n8e = 0;
-    r.n8 = (r.n8e + 31) >> 5;
-    r.cost = r.n4 + 2 * r.n8;
+    r.n8 = (r.n8e + 15) >> 4;
+    r.cost = r.n4 + r.n8;
     return r;
 }
 
@@ -98,7 +99,7 @@ struct DecodeArgs {
     int32_t B;
     const uint8_t *int4_pool;
     const uint8_t *int8_pool;
-    int32_t H, P, h, s, w, nr8;
+    int32_t H, P, logP, h, s, w, nr8;
     float inv_sqrt_h;
     int32_t max_workers, min_units;
     int64_t *ws_header;     // [0] total units, [1] effective workers

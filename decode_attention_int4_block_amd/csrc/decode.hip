@@ -8,13 +8,17 @@
 // statistics, so the INT4/INT8 merge and the split-K merge are one log-sum-exp
 // combine.
 //
-// Work: a row's (KV head) segment is a list of units -- INT4 steps of 32
-// positions and INT8 steps of 32 ring entries (2 units) -- and the units of all
-// segments are split evenly over the resident waves (one wave per workgroup),
-// so a long-tailed length mix costs the same per wave.
+// Work: a (row, KV head) segment is a list of units of roughly equal bytes --
+// INT4 steps of 32 positions and INT8 steps of 16 ring entries -- and the units
+// of all segments are split evenly over the resident waves (one wave per
+// workgroup), so a long-tailed length mix costs every wave the same.
 //
-// Per 32-position step a wave runs, with 16x16x32 f16 MFMA:
-//   scores[tok][head] = codes[tok][:] . q[head][:]   (A = codes, B = query)
+// Memory: each wave streams its steps through a ring of kStages LDS buffers
+// with direct global->LDS loads (5 x 16 B per lane per step), kStages - 1 steps
+// ahead of the step it computes, so the bytes in flight do not cost VGPRs.
+//
+// Compute per step, with 16x16x32 f16 MFMA:
+//   scores[tok][head] = codes[tok][:] . q[head][:]    (A = codes, B = query)
 //   acc[head][dim]   += p[head][tok] * vcodes[tok][dim] (A = p, B = codes)
 // The query and p are split into f16 hi + lo parts so the products keep fp32
 // accuracy; 4-bit and 8-bit codes become f16 values exactly by masking them
@@ -31,9 +35,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
+
+constexpr int kStages = 4;
+constexpr int kStageBytes = 4352;       // 4 x 1 KB codes + 256 B params
+constexpr int kDmaPerStep = 5;
 
 __device__ inline floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -42,11 +49,6 @@ __device__ inline floatx4 mfma16(half8 a, half8 b, floatx4 c) {
 __device__ inline half8 pack8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
     u32x4 u = {a0, a1, a2, a3};
     return __builtin_bit_cast(half8, u);
-}
-
-__device__ inline uint32_t pack_h2(float lo, float hi) {
-    half2v v = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(uint32_t, v);
 }
 
 // f16 hi/lo split of a pair: hi = f16(x), lo = f16(x - hi).
@@ -66,32 +68,94 @@ __device__ inline float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
 template <typename T>
 __device__ inline T ldg(const void *p) { return *reinterpret_cast<const T *>(p); }
 
-// ---------------------------------------------------------------------------
-// Loaded data of one 32-position step: two subblocks A and B.
-struct Step4 {
-    u32x4 kA, kB;       // key codes: token l%16, dims 32(l/16)..+32
-    u32x4 vA, vB;       // value codes: dims n + 32c, n + 16 + 32c of tokens 4G..4G+3
-    u32x4 kpA, kpB;     // key params of tokens 4G..4G+3
-    u32x4 vpA, vpB;     // value params
-};
+typedef __attribute__((address_space(3))) void *lds_ptr;
 
-struct Step8 {
-    u32x4 kA0, kA1, kB0, kB1;   // key codes (bytes): entry l%16, dims 32(l/16)..+32
-    u32x4 vA0, vA1, vB0, vB1;   // value codes: tiles 0..7 of dims n, entries 4G..4G+3
-    u32x4 kpA, kpB, vpA, vpB;
+// Values every lane holds the same copy of, made visibly wave-uniform so that
+// the loads they index become scalar loads.
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Read-only launch inputs (lengths, slots, block table) read through the
+// constant address space so that wave-uniform reads are scalar loads.
+__device__ inline int ldc(const int32_t *p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+__device__ inline int64_t uni64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane.
+__device__ inline void dma16(const void *src, uint8_t *dst_lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst_lds, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define KVQ_VMCNT(n) (((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+#define KVQ_LGKM0 ((0xF) | (0x3 << 14) | (0x7 << 4))
+
+// The waitcnt intrinsic does not order memory accesses at the IR level; the
+// empty asm with a memory clobber keeps LDS reads of a stage below its wait.
+#define KVQ_FENCE() __asm__ volatile("" ::: "memory")
+
+__device__ inline void wait_vm_steps(int steps_after) {
+    // outstanding DMA instructions allowed = kDmaPerStep * steps_after
+    switch (steps_after) {
+        case 0: __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(5)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(10)); break;
+        default: __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(15)); break;
+    }
+    KVQ_FENCE();
+    static_assert(kStages == 4 && kDmaPerStep == 5, "wait table assumes 4 stages x 5 loads");
+}
+
+__device__ inline void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(KVQ_LGKM0);
+    KVQ_FENCE();
+}
+
+// ---------------------------------------------------------------------------
+// Data of one step as read from its LDS stage.
+struct StepRegs {
+    u32x4 kA, kB;       // INT4: key codes of token l%16 (A/B), dims 32G..+32
+                        // INT8: key bytes of entry l%16, dims 32G..+16 (kA) and +16..+32 (kB)
+    u32x4 vA, vB;       // INT4: value codes, dims n + 32c / n + 16 + 32c, tokens 4G..4G+3
+                        // INT8: value bytes, tiles 0..3 (vA) and 4..7 (vB), entries 4G..4G+3
+    u32x4 kpA, kpB;     // key params of tokens 4G..4G+3 (INT8: kpA only)
+    u32x4 vpA, vpB;     // value params
 };
 
 struct SegCtx {
     int lane, G, n;
     int g;
-    // query operands (B of the score MFMA), hi/lo, INT4 order and INT8 order
-    half8 q4h[4], q4l[4], q8h[4], q8l[4];
+    half8 q4h[4], q4l[4], q8h[4], q8l[4];   // query operands, INT4 and INT8 element orders
     float K1;           // 2^(24 - e) * log2(e) / sqrt(128)
     float K2;           // sum(q~) * log2(e) / sqrt(128) for head l%16
-    // running softmax state: per lane for head l%16 (m), partial over group G (l, z)
     float m, lsum, zsum;
     floatx4 O[8];       // acc[head 4G+i][16 t + n], odd tiles scaled by 16
 };
+
+// Wave-uniform position in the unit stream of one worker.
+struct Cursor {
+    int b, hk;          // segment (row, KV head)
+    RowPlan rp;
+    int r;              // unit index inside the segment
+    int64_t u;          // global unit
+};
+
+__device__ inline void cursor_next(const DecodeArgs &a, Cursor &c) {
+    ++c.u;
+    if (++c.r < c.rp.cost) return;
+    c.r = 0;
+    if (++c.hk < a.H) return;
+    c.hk = 0;
+    for (++c.b; c.b < a.B; ++c.b) {
+        c.rp = row_plan(ldc(a.ctx_len, c.b), a.s, a.w);
+        if (c.rp.cost > 0) return;
+    }
+}
 
 __device__ inline void build_query(const DecodeArgs &a, int b, int hk, SegCtx &c) {
     const int j = c.lane & 15;
@@ -128,8 +192,7 @@ __device__ inline void build_query(const DecodeArgs &a, int b, int hk, SegCtx &c
     // strides 32 and 64 cross lanes (lane groups G differ in bit 0 / bit 1)
 #pragma unroll
     for (int ls = 16; ls <= 32; ls <<= 1) {
-        const int len = ls * 2;     // element distance: 32 for ls = 16, 64 for ls = 32
-        if (len < a.h) {
+        if (2 * ls < a.h) {
             const bool upper = (c.lane & ls) != 0;
 #pragma unroll
             for (int i = 0; i < 32; ++i) {
@@ -177,9 +240,9 @@ __device__ inline void build_query(const DecodeArgs &a, int b, int hk, SegCtx &c
     }
 }
 
-// Online-softmax update for 8 scores of this lane (tokens 4G+i of subblocks A, B)
-// and the f16 hi/lo p*scale_v operands of the value MFMA.  Returns the A
-// operands (rows = heads, k = [A0 A2 A1 A3 B0 B2 B1 B3]).
+// Online-softmax update for 8 scores of this lane (tokens 4G+i of subblocks A,
+// B) and the f16 hi/lo p*scale_v operands of the value MFMA (rows = heads,
+// k = [A0 A2 A1 A3 B0 B2 B1 B3]).
 __device__ inline void softmax_step(SegCtx &c, float sc[8], const u32x4 &vpA, const u32x4 &vpB,
                                     const bool valid[8], half8 &ph, half8 &pl) {
     float mstep = kNegInf;
@@ -222,51 +285,88 @@ __device__ inline void softmax_step(SegCtx &c, float sc[8], const u32x4 &vpA, co
     pl = pack8(l0, l1, l2, l3);
 }
 
-__device__ inline Step4 load_step4(const DecodeArgs &a, const int32_t *bt, int hk, int pos0,
-                                   bool vA, bool vB, int lane) {
-    Step4 r;
+// ---------------------------------------------------------------------------
+// Producer: issue the 5 direct-to-LDS loads of the step at cursor c into stage st.
+__device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, uint8_t *st, int lane) {
     const int G = lane >> 4, n = lane & 15;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    r.kA = r.kB = r.vA = r.vB = r.kpA = r.kpB = r.vpA = r.vpB = z;
-    const int subs = a.P >> 4;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const bool valid = x == 0 ? vA : vB;
-        if (!valid) continue;
-        const int p = pos0 + 16 * x;
-        const int page = bt[p / a.P];
-        const int sub = (p % a.P) >> 4;
-        const uint8_t *base = a.int4_pool + ((size_t)((int64_t)page * a.H + hk) * subs + sub) * kSub4Bytes;
-        const u32x4 k = ldg<u32x4>(base + kSub4K + n * 64 + G * 16);
-        const u32x4 v = ldg<u32x4>(base + kSub4V + lane * 16);
-        const u32x4 kp = ldg<u32x4>(base + kSub4KP + G * 16);
-        const u32x4 vp = ldg<u32x4>(base + kSub4VP + G * 16);
-        if (x == 0) { r.kA = k; r.vA = v; r.kpA = kp; r.vpA = vp; }
-        else        { r.kB = k; r.vB = v; r.kpB = kp; r.vpB = vp; }
+    const int slot = ldc(a.slot, c.b);
+    if (c.r < c.rp.n4) {
+        const int pos0 = (c.rp.k0 + c.r) * 32;
+        const int32_t *bt = a.block_table + (int64_t)slot * a.bt_stride;
+        const int subs = a.P >> 4;
+        const int pA = pos0, pB = pos0 + 16;
+        const int pageA = ldc(bt, pA >> a.logP);
+        const uint8_t *baseA = a.int4_pool +
+            ((size_t)((int64_t)pageA * a.H + c.hk) * subs + ((pA & (a.P - 1)) >> 4)) * kSub4Bytes;
+        const uint8_t *baseB = baseA;
+        if (pB < c.rp.hi4) {
+            const int pageB = ldc(bt, pB >> a.logP);
+            baseB = a.int4_pool +
+                ((size_t)((int64_t)pageB * a.H + c.hk) * subs + ((pB & (a.P - 1)) >> 4)) * kSub4Bytes;
+        }
+        dma16(baseA + kSub4K + n * 64 + G * 16, st + 0);
+        dma16(baseB + kSub4K + n * 64 + G * 16, st + 1024);
+        dma16(baseA + kSub4V + lane * 16, st + 2048);
+        dma16(baseB + kSub4V + lane * 16, st + 3072);
+        if (lane < 16) {
+            const uint8_t *b = (lane & 4) ? baseB : baseA;
+            dma16(b + ((lane & 8) ? kSub4VP : kSub4KP) + (lane & 3) * 16, st + 4096);
+        }
+    } else {
+        const int sub = c.r - c.rp.n4;
+        const uint8_t *base = a.int8_pool + ((size_t)((int64_t)slot * a.H + c.hk) * a.nr8 + sub) * kSub8Bytes;
+        dma16(base + kSub8K + n * 128 + G * 32, st + 0);
+        dma16(base + kSub8K + n * 128 + G * 32 + 16, st + 1024);
+        dma16(base + kSub8V + lane * 32, st + 2048);
+        dma16(base + kSub8V + lane * 32 + 16, st + 3072);
+        if (lane < 8) {
+            dma16(base + ((lane & 4) ? kSub8VP : kSub8KP) + (lane & 3) * 16, st + 4096);
+        }
+    }
+}
+
+__device__ inline StepRegs read_stage(const uint8_t *st, bool int4, int lane) {
+    StepRegs r;
+    const int G = lane >> 4;
+    r.kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
+    r.kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
+    r.vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
+    r.vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
+    if (int4) {
+        r.kpA = *reinterpret_cast<const u32x4 *>(st + 4096 + G * 16);
+        r.kpB = *reinterpret_cast<const u32x4 *>(st + 4160 + G * 16);
+        r.vpA = *reinterpret_cast<const u32x4 *>(st + 4224 + G * 16);
+        r.vpB = *reinterpret_cast<const u32x4 *>(st + 4288 + G * 16);
+    } else {
+        r.kpA = *reinterpret_cast<const u32x4 *>(st + 4096 + G * 16);
+        r.vpA = *reinterpret_cast<const u32x4 *>(st + 4160 + G * 16);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        r.kpB = z;
+        r.vpB = z;
     }
     return r;
 }
 
-__device__ inline void compute_step4(SegCtx &c, const Step4 &r, int pos0, int lo4, int hi4) {
+__device__ inline void compute_step4(SegCtx &c, const StepRegs &r, int pos0, int lo4, int hi4) {
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 dA = zero4, dB = zero4;
+    floatx4 dAh = zero4, dAl = zero4, dBh = zero4, dBl = zero4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t x = r.kA[i], x8 = x >> 8;
         const half8 ak = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
-        dA = mfma16(ak, c.q4h[i], dA);
-        dA = mfma16(ak, c.q4l[i], dA);
         const uint32_t y = r.kB[i], y8 = y >> 8;
         const half8 bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
-        dB = mfma16(bk, c.q4h[i], dB);
-        dB = mfma16(bk, c.q4l[i], dB);
+        dAh = mfma16(ak, c.q4h[i], dAh);
+        dBh = mfma16(bk, c.q4h[i], dBh);
+        dAl = mfma16(ak, c.q4l[i], dAl);
+        dBl = mfma16(bk, c.q4l[i], dBl);
     }
     float sc[8];
     bool valid[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t kp = i < 4 ? r.kpA[i] : r.kpB[i - 4];
-        const float d = i < 4 ? dA[i] : dB[i - 4];
+        const float d = i < 4 ? dAh[i] + dAl[i] : dBh[i - 4] + dBl[i - 4];
         const int p = pos0 + (i < 4 ? 0 : 16) + 4 * c.G + (i & 3);
         valid[i] = p >= lo4 && p < hi4;
         const float s = d * (h_lo(kp) * c.K1) + h_hi(kp) * c.K2;
@@ -280,63 +380,41 @@ __device__ inline void compute_step4(SegCtx &c, const Step4 &r, int pos0, int lo
         const half8 ve = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
         const half8 vo = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
         c.O[2 * cc] = mfma16(ph, ve, c.O[2 * cc]);
-        c.O[2 * cc] = mfma16(pl, ve, c.O[2 * cc]);
         c.O[2 * cc + 1] = mfma16(ph, vo, c.O[2 * cc + 1]);
+        c.O[2 * cc] = mfma16(pl, ve, c.O[2 * cc]);
         c.O[2 * cc + 1] = mfma16(pl, vo, c.O[2 * cc + 1]);
     }
 }
 
-__device__ inline Step8 load_step8(const DecodeArgs &a, int slot, int hk, int e0, bool vA, bool vB, int lane) {
-    Step8 r;
-    const int G = lane >> 4, n = lane & 15;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    r.kA0 = r.kA1 = r.kB0 = r.kB1 = r.vA0 = r.vA1 = r.vB0 = r.vB1 = z;
-    r.kpA = r.kpB = r.vpA = r.vpB = z;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const bool valid = x == 0 ? vA : vB;
-        if (!valid) continue;
-        const int sub = (e0 >> 4) + x;
-        const uint8_t *base = a.int8_pool + ((size_t)((int64_t)slot * a.H + hk) * a.nr8 + sub) * kSub8Bytes;
-        const u32x4 k0 = ldg<u32x4>(base + kSub8K + n * 128 + G * 32);
-        const u32x4 k1 = ldg<u32x4>(base + kSub8K + n * 128 + G * 32 + 16);
-        const u32x4 v0 = ldg<u32x4>(base + kSub8V + lane * 32);
-        const u32x4 v1 = ldg<u32x4>(base + kSub8V + lane * 32 + 16);
-        const u32x4 kp = ldg<u32x4>(base + kSub8KP + G * 16);
-        const u32x4 vp = ldg<u32x4>(base + kSub8VP + G * 16);
-        if (x == 0) { r.kA0 = k0; r.kA1 = k1; r.vA0 = v0; r.vA1 = v1; r.kpA = kp; r.vpA = vp; }
-        else        { r.kB0 = k0; r.kB1 = k1; r.vB0 = v0; r.vB1 = v1; r.kpB = kp; r.vpB = vp; }
-    }
-    return r;
-}
-
-__device__ inline uint32_t dw8(const u32x4 &lo, const u32x4 &hi, int i) { return i < 4 ? lo[i] : hi[i - 4]; }
-
-__device__ inline void compute_step8(SegCtx &c, const Step8 &r, int e0, int n8e) {
+// One INT8 subblock of 16 ring entries starting at e0 (the B half of the value
+// MFMA is zero).
+__device__ inline void compute_step8(SegCtx &c, const StepRegs &r, int e0, int n8e) {
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 dA = zero4, dB = zero4;
+    floatx4 dh = zero4, dl = zero4;
     const uint32_t M8 = 0x00FF00FFu;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t x = dw8(r.kA0, r.kA1, 2 * i), y = dw8(r.kA0, r.kA1, 2 * i + 1);
+        // dims 32G + 8i .. +8: dwords 2i, 2i+1 of the lane's 32 bytes
+        const uint32_t x = i < 2 ? r.kA[2 * i] : r.kB[2 * i - 4];
+        const uint32_t y = i < 2 ? r.kA[2 * i + 1] : r.kB[2 * i - 3];
         const half8 ak = pack8(x & M8, (x >> 8) & M8, y & M8, (y >> 8) & M8);
-        dA = mfma16(ak, c.q8h[i], dA);
-        dA = mfma16(ak, c.q8l[i], dA);
-        const uint32_t u = dw8(r.kB0, r.kB1, 2 * i), v = dw8(r.kB0, r.kB1, 2 * i + 1);
-        const half8 bk = pack8(u & M8, (u >> 8) & M8, v & M8, (v >> 8) & M8);
-        dB = mfma16(bk, c.q8h[i], dB);
-        dB = mfma16(bk, c.q8l[i], dB);
+        dh = mfma16(ak, c.q8h[i], dh);
+        dl = mfma16(ak, c.q8l[i], dl);
     }
     float sc[8];
     bool valid[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t kp = i < 4 ? r.kpA[i] : r.kpB[i - 4];
-        const float d = i < 4 ? dA[i] : dB[i - 4];
-        const int e = e0 + (i < 4 ? 0 : 16) + 4 * c.G + (i & 3);
-        valid[i] = e < n8e;
-        const float s = d * (h_lo(kp) * c.K1) + h_hi(kp) * c.K2;
-        sc[i] = valid[i] ? s : kNegInf;
+        if (i < 4) {
+            const uint32_t kp = r.kpA[i];
+            const int e = e0 + 4 * c.G + i;
+            valid[i] = e < n8e;
+            const float s = (dh[i] + dl[i]) * (h_lo(kp) * c.K1) + h_hi(kp) * c.K2;
+            sc[i] = valid[i] ? s : kNegInf;
+        } else {
+            valid[i] = false;
+            sc[i] = kNegInf;
+        }
     }
     half8 ph, pl;
     softmax_step(c, sc, r.vpA, r.vpB, valid, ph, pl);
@@ -345,8 +423,8 @@ __device__ inline void compute_step8(SegCtx &c, const Step8 &r, int e0, int n8e)
     const half8 ph16 = ph * sixteen, pl16 = pl * sixteen;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const uint32_t x = dw8(r.vA0, r.vA1, t), y = dw8(r.vB0, r.vB1, t);
-        const half8 vv = pack8(x & M8, (x >> 8) & M8, y & M8, (y >> 8) & M8);
+        const uint32_t x = t < 4 ? r.vA[t] : r.vB[t - 4];
+        const half8 vv = pack8(x & M8, (x >> 8) & M8, 0u, 0u);
         if (t & 1) {
             c.O[t] = mfma16(ph16, vv, c.O[t]);
             c.O[t] = mfma16(pl16, vv, c.O[t]);
@@ -394,10 +472,11 @@ __device__ inline int64_t total_units(const DecodeArgs &a, int lane) {
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
-    return tot;
+    return uni64(tot);
 }
 
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x;
     const int64_t wid = blockIdx.x;
     const int64_t total = total_units(a, lane);
@@ -430,15 +509,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         if (active && b0 < 0) {
             const uint64_t m = __ballot(b < a.B && cost > 0 && excl <= u_begin && u_begin < excl + cost);
             if (m) {
-                const int src = __ffsll((unsigned long long)m) - 1;
-                b0 = c0 + src;
-                pre0 = __shfl(excl, src, 64);
+                const int src = uni(__ffsll((unsigned long long)m) - 1);
+                b0 = uni(c0 + src);
+                pre0 = uni64(__shfl(excl, src, 64));
                 if (wid != 0) break;
             }
         }
-        base += __shfl(incl, 63, 64);
+        base = uni64(base + __shfl(incl, 63, 64));
     }
     if (!active) return;
+    b0 = uni(b0);
+    pre0 = uni64(pre0);
+
+    Cursor start;
+    start.b = b0;
+    start.rp = row_plan(ldc(a.ctx_len, b0), a.s, a.w);
+    start.hk = (int)((u_begin - pre0) / start.rp.cost);
+    start.r = (int)(u_begin - pre0 - (int64_t)start.hk * start.rp.cost);
+    start.u = u_begin;
 
     SegCtx c;
     c.lane = lane;
@@ -446,57 +534,46 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     c.n = lane & 15;
     c.g = a.g;
 
-    int b = b0;
-    RowPlan rp = row_plan(a.ctx_len[b], a.s, a.w);
-    int hk = (int)((u_begin - pre0) / rp.cost);
-    int64_t segc0 = pre0 + (int64_t)hk * rp.cost;
-    while (segc0 < u_end) {
-        if (rp.cost > 0) {
-            const int ra = (int)((u_begin > segc0 ? u_begin : segc0) - segc0);
-            const int rb = (int)((u_end < segc0 + rp.cost ? u_end : segc0 + rp.cost) - segc0);
-            const int slot = a.slot[b];
-            const int32_t *bt = a.block_table + (int64_t)slot * a.bt_stride;
-            build_query(a, b, hk, c);
+    Cursor P = start, C = start;
+    int issued = 0;
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+        if (P.u < u_end) {
+            issue_step(a, P, smem + s * kStageBytes, lane);
+            cursor_next(a, P);
+            ++issued;
+        }
+    }
+    bool open = false;
+    for (int i = 0; C.u < u_end; ++i) {
+        wait_vm_steps(issued - i - 1);
+        uint8_t *st = smem + (i % kStages) * kStageBytes;
+        const bool int4 = C.r < C.rp.n4;
+        const StepRegs r = read_stage(st, int4, lane);
+        wait_lgkm0();
+        if (P.u < u_end) {
+            issue_step(a, P, st, lane);
+            cursor_next(a, P);
+            ++issued;
+        }
+        if (!open) {
+            build_query(a, C.b, C.hk, c);
             c.m = kNegInf;
             c.lsum = 0.0f;
             c.zsum = 0.0f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) c.O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-            // INT4 steps [ra, min(rb, n4))
-            const int k_end = rb < rp.n4 ? rb : rp.n4;
-            if (ra < k_end) {
-                int pos0 = (rp.k0 + ra) * 32;
-                Step4 cur = load_step4(a, bt, hk, pos0, pos0 < rp.hi4 && pos0 + 16 > rp.lo4,
-                                       pos0 + 16 < rp.hi4, lane);
-                for (int k = ra; k < k_end; ++k) {
-                    const int npos = pos0 + 32;
-                    Step4 nxt;
-                    if (k + 1 < k_end)
-                        nxt = load_step4(a, bt, hk, npos, npos < rp.hi4, npos + 16 < rp.hi4, lane);
-                    compute_step4(c, cur, pos0, rp.lo4, rp.hi4);
-                    cur = nxt;
-                    pos0 = npos;
-                }
-            }
-            // INT8 steps j with n4 + 2j in [ra, rb)
-            int j_begin = ra > rp.n4 ? (ra - rp.n4 + 1) / 2 : 0;
-            int j_end = rb > rp.n4 ? (rb - rp.n4 + 1) / 2 : 0;
-            if (j_end > rp.n8) j_end = rp.n8;
-            for (int j = j_begin; j < j_end; ++j) {
-                const int e0 = 32 * j;
-                Step8 r = load_step8(a, slot, hk, e0, e0 < rp.n8e, e0 + 16 < rp.n8e, lane);
-                compute_step8(c, r, e0, rp.n8e);
-            }
-            const int64_t seg = (int64_t)b * a.H + hk;
-            write_piece(a, c, wid + seg);
+            open = true;
         }
-        segc0 += rp.cost;
-        if (++hk == a.H) {
-            hk = 0;
-            if (++b >= a.B) break;
-            rp = row_plan(a.ctx_len[b], a.s, a.w);
+        if (int4)
+            compute_step4(c, r, (C.rp.k0 + C.r) * 32, C.rp.lo4, C.rp.hi4);
+        else
+            compute_step8(c, r, 16 * (C.r - C.rp.n4), C.rp.n8e);
+        if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) {
+            write_piece(a, c, wid + (int64_t)C.b * a.H + C.hk);
+            open = false;
         }
+        cursor_next(a, C);
     }
 }
 

@@ -58,7 +58,7 @@
  *
  * ---------------------------------------------------------------------------
  * INT4 pool layout (int4_pool, kvq_int4_pool_bytes bytes, 256-byte aligned).
- *   A page of P tokens (P % 16 == 0) and one KV head is P/16 "subblocks" of 16
+ *   A page of P tokens (P a power of two >= 16) and one KV head is P/16 "subblocks" of 16
  *   tokens; subblock j of (page, kv_head) starts at byte
  *       ((page * num_kv_heads + kv_head) * (P / 16) + j) * 2176
  *   and holds token rows t = 0..15 (position = page_row_base + 16 j + t):
@@ -110,7 +110,7 @@ typedef enum {
 typedef struct {
     int32_t num_kv_heads;    /* >= 1                                              */
     int32_t head_dim;        /* must be 128                                       */
-    int32_t page_size;       /* tokens per page, multiple of 16, >= 16            */
+    int32_t page_size;       /* tokens per page: a power of two >= 16             */
     int32_t num_pages;       /* pages in int4_pool                                */
     int32_t num_slots;       /* sequence slots (rows of the block table / INT8)   */
     int32_t had_block;       /* Hadamard block size h: power of two in [1, 128]   */

@@ -56,7 +56,7 @@ def test_pool_sizes_follow_the_documented_layout(lib):
     assert 2176 * 8 / (16 * 256) == 4.25
 
 
-@pytest.mark.parametrize("field,value", [("head_dim", 64), ("page_size", 24), ("page_size", 0),
+@pytest.mark.parametrize("field,value", [("head_dim", 64), ("page_size", 24), ("page_size", 0), ("page_size", 48),
                                          ("had_block", 3), ("had_block", 256), ("sink", -1),
                                          ("num_kv_heads", 0)])
 def test_bad_descriptors_are_rejected(lib, field, value):

@@ -89,8 +89,8 @@ def build_workload(cfg: WorkloadConfig) -> Workload:
         P = cfg.page_size
     else:
         # One page per sequence holding the whole context.
-        P = int(max(cfg.page_size, int(L.max())))
-        P = ((P + 15) // 16) * 16
+        P = int(max(cfg.page_size, int(L.max()), 16))
+        P = 1 << (P - 1).bit_length()          # page sizes are powers of two
     npages = (L + P - 1) // P
     num_pages = int(npages.sum())
     bt_stride = max(1, int(npages.max()))
