@@ -30,7 +30,7 @@ kvq_status ok() {
 
 constexpr int kMinUnitsPerWorker = 8;
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_max_workers[kMaxDevices];
+std::atomic<int> g_max_workers[kMaxDevices][3];   // per group class g <= 4, <= 8, <= 16
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -55,15 +55,16 @@ float inv_sqrt(int h) { return (float)(1.0 / sqrt((double)h)); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-kvq_status max_workers(int *out) {
+kvq_status max_workers(int g, int *out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
-    int v = g_max_workers[dev].load(std::memory_order_relaxed);
+    const int cls = g <= 4 ? 0 : (g <= 8 ? 1 : 2);
+    int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
-        hipError_t e = kvq::decode_max_workers(&v);
+        hipError_t e = kvq::decode_max_workers(g, &v);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
-        g_max_workers[dev].store(v, std::memory_order_relaxed);
+        g_max_workers[dev][cls].store(v, std::memory_order_relaxed);
     }
     *out = v;
     return KVQ_OK;
@@ -136,9 +137,11 @@ kvq_status kv_quant_append(const kvq_cache *c, const uint16_t *k, const uint16_t
 
 size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num_q_heads) {
     if (check_cache(c) != KVQ_OK || B < 0 || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
+    const int g = num_q_heads / c->num_kv_heads;
+    if (g > 16) return 0;
     int workers = 0;
-    if (max_workers(&workers) != KVQ_OK) return 0;
-    return ws_layout(c, B, num_q_heads / c->num_kv_heads, workers).total;
+    if (max_workers(g, &workers) != KVQ_OK) return 0;
+    return ws_layout(c, B, g, workers).total;
 }
 
 kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads,
@@ -162,7 +165,7 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
     int workers = 0;
-    st = max_workers(&workers);
+    st = max_workers(g, &workers);
     if (st != KVQ_OK) return st;
     const WsLayout l = ws_layout(c, B, g, workers);
     if (workspace_bytes < l.total)

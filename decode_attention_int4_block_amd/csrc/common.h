@@ -104,13 +104,13 @@ struct DecodeArgs {
     int32_t max_workers, min_units;
     int64_t *ws_header;     // [0] total units, [1] effective workers
     int64_t *ws_prefix;     // [B] exclusive prefix of per-row units (all KV heads)
-    float *ws_piece;        // [(max_workers + B*H)][g][kPieceStride]
+    float *ws_piece;        // [max_workers + B*H][g][kPieceStride] per-worker pieces
     float *out;
     float *lse;
 };
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream);
-hipError_t decode_max_workers(int *out);
+hipError_t decode_max_workers(int g, int *out);
 
 }  // namespace kvq

@@ -171,7 +171,8 @@ size_t kv_decode_attn_workspace_bytes(const kvq_cache *cache, int32_t B, int32_t
  *   lse          fp32 [B][num_q_heads] (device) or NULL: natural-log
  *                log-sum-exp of the scaled scores; -inf when L == 0.
  *   workspace    device scratch of at least kv_decode_attn_workspace_bytes();
- *                contents need no initialization and are overwritten.
+ *                contents need no initialization and are overwritten.  Calls
+ *                sharing one workspace must be ordered (same stream).
  */
 kvq_status kv_decode_attn(const kvq_cache *cache,
                           const uint16_t *q, int32_t num_q_heads,

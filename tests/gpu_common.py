@@ -33,11 +33,16 @@ def check_workload_invariants(wl):
     assert np.all((wl.slots >= 0) & (wl.slots < wl.num_slots))
 
 
-def make_device_workload(cfg, keep=(), gen_device="cpu", prefill=True):
+def make_device_workload(cfg, keep=(), gen_device="cpu", prefill=True, poison=False):
+    """Build and fill a workload's cache.  poison=True first fills both pools with
+    0xFF bytes (fp16 NaN) so that any read of never-written cache bytes shows."""
     from decode_attention_int4_block_amd.harness import DeviceWorkload
     wl = build_workload(cfg)
     check_workload_invariants(wl)
     dw = DeviceWorkload(wl, device="cuda", gen_device=gen_device, keep_host=keep)
+    if poison:
+        dw.cache.int4_pool.fill_(0xFF)
+        dw.cache.int8_pool.fill_(0xFF)
     if prefill:
         dw.prefill()
         dw.append_step()
@@ -119,6 +124,7 @@ def compare_attention(dw, rows, report_unquantized=False):
         k, v = dw.host_kv[b]
         kb, vb = bf16_bits(k), bf16_bits(v)
         ref, ref_lse = attend(qb[b], quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent))
+        assert np.isfinite(out[b]).all() and np.isfinite(lse[b]).all(), f"non-finite output in row {b}"
         worst = max(worst, float(np.abs(out[b] - ref).max()))
         worst_lse = max(worst_lse, float(np.abs(lse[b] - ref_lse).max()))
         if report_unquantized:

@@ -111,6 +111,20 @@ def test_page_sizes_and_empty_rows():
         assert err <= ATOL and err_lse <= ATOL
 
 
+@pytest.mark.parametrize("g,Hkv", [(1, 4), (4, 2), (8, 2), (16, 1)])
+def test_unwritten_cache_bytes_never_reach_the_output(g, Hkv):
+    """Pools pre-filled with fp16 NaN patterns: positions past each row's context
+    share subblocks with valid ones and must be masked, never multiplied by 0."""
+    cfg = small_config([1, 5, 17, 33, 50, 97, 130, 301], Hq=g * Hkv, Hkv=Hkv, h=128, s=4, w=32, seed=700 + g)
+    rows = list(range(cfg.batch))
+    dw = make_device_workload(cfg, keep=rows, poison=True)
+    dw.decode_step()
+    torch.cuda.synchronize()
+    err, err_lse, _ = compare_attention(dw, rows)
+    _report(f"poisoned pools g={g}", max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
+    assert err <= ATOL and err_lse <= ATOL
+
+
 def test_bulk_append_equals_token_by_token():
     """Ordering independence: one bulk append vs one call per position."""
     from decode_attention_int4_block_amd import kv_quant_append
