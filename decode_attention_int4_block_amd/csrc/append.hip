@@ -141,8 +141,10 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
             ((size_t)((int64_t)slot * a.H + hk) * a.nr8 + esub) * kSub8Bytes;
         const QParams kp = qparams(kmn, kmx, 255.0f);
         const QParams vp = qparams(vmn, vmx, 255.0f);
-        const uint32_t kc = qcode(x0, kp, 255.0f) | (qcode(x1, kp, 255.0f) << 8);
-        *reinterpret_cast<uint16_t *>(base8 + kSub8K + ee * 128 + 2 * lane) = (uint16_t)kc;
+        // dims 2l (even) and 2l+1 (odd) of group j = l/4: bytes 8j + l%4 and 8j + 4 + l%4
+        uint8_t *krow8 = base8 + kSub8K + ee * 128 + 8 * (lane >> 2) + (lane & 3);
+        krow8[0] = (uint8_t)qcode(x0, kp, 255.0f);
+        krow8[4] = (uint8_t)qcode(x1, kp, 255.0f);
         const int G = ee >> 2, r = ee & 3;
         base8[kSub8V + 4 * ((G * 16 + vn) * 8 + 2 * vc) + r] = (uint8_t)qcode(v0, vp, 255.0f);
         base8[kSub8V + 4 * ((G * 16 + vn) * 8 + 2 * vc + 1) + r] = (uint8_t)qcode(v1, vp, 255.0f);

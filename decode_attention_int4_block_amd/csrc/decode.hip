@@ -174,7 +174,7 @@ struct SegCtx {
     static constexpr int kQ = kPacked ? 1 : 2;     // query operand sets per chunk
     int lane, G, n, col;
     int g;
-    half8 q4[kQ][4], q8[kQ][4];   // query operands, INT4 and INT8 element orders
+    half8 q4[kQ][4];    // query operands (INT4 nibble order; INT8 keys are split into nibbles)
     float K1;           // 2^(24 - e) * log2(e) / sqrt(128)
     float K2;           // sum(q~) * log2(e) / sqrt(128) of head col % GP
     float m, lsum, zsum;
@@ -295,25 +295,17 @@ __device__ inline void build_query(const DecodeArgs &a, int b, int hk, SegCtx<GP
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float *y = x + 8 * i;
-        uint32_t h[4], l[4], h8[4], l8[4];
-        // INT4 order: dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
+        uint32_t h[4], l[4];
+        // nibble order of a code dword: dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
         split2(y[0] * sc, y[4] * sc, h[0], l[0]);
         split2(y[1] * sc * 0.0625f, y[5] * sc * 0.0625f, h[1], l[1]);
         split2(y[2] * sc, y[6] * sc, h[2], l[2]);
         split2(y[3] * sc * 0.0625f, y[7] * sc * 0.0625f, h[3], l[3]);
-        // INT8 order: dims 0,2 | 1,3 | 4,6 | 5,7
-        split2(y[0] * sc, y[2] * sc, h8[0], l8[0]);
-        split2(y[1] * sc, y[3] * sc, h8[1], l8[1]);
-        split2(y[4] * sc, y[6] * sc, h8[2], l8[2]);
-        split2(y[5] * sc, y[7] * sc, h8[3], l8[3]);
         if constexpr (SegCtx<GP>::kPacked) {
             c.q4[0][i] = lo_part ? pack8(l[0], l[1], l[2], l[3]) : pack8(h[0], h[1], h[2], h[3]);
-            c.q8[0][i] = lo_part ? pack8(l8[0], l8[1], l8[2], l8[3]) : pack8(h8[0], h8[1], h8[2], h8[3]);
         } else {
             c.q4[0][i] = pack8(h[0], h[1], h[2], h[3]);
             c.q4[1][i] = pack8(l[0], l[1], l[2], l[3]);
-            c.q8[0][i] = pack8(h8[0], h8[1], h8[2], h8[3]);
-            c.q8[1][i] = pack8(l8[0], l8[1], l8[2], l8[3]);
         }
     }
 }
@@ -514,18 +506,28 @@ __device__ inline void compute_step8(SegCtx<GP> &c, const StepRegs &r, int e0, i
     floatx4 d[kQ];
 #pragma unroll
     for (int q = 0; q < kQ; ++q) d[q] = zero4;
-    const uint32_t M8 = 0x00FF00FFu;
+    floatx4 dh[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) dh[q] = zero4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // dims 32G + 8i .. +8: dwords 2i, 2i+1 of the lane's 32 bytes
-        const uint32_t x = i < 2 ? r.kA[2 * i] : r.kB[2 * i - 4];
-        const uint32_t y = i < 2 ? r.kA[2 * i + 1] : r.kB[2 * i - 3];
-        const half8 ak = pack8(x & M8, (x >> 8) & M8, y & M8, (y >> 8) & M8);
+        // dims 32G + 8i .. +8: dwords 2i (even dims) and 2i+1 (odd dims); the
+        // low and high nibbles of the 8 codes form two INT4-ordered dwords
+        const uint32_t x0 = i < 2 ? r.kA[2 * i] : r.kB[2 * i - 4];
+        const uint32_t x1 = i < 2 ? r.kA[2 * i + 1] : r.kB[2 * i - 3];
+        const uint32_t xl = (x0 & 0x0F0F0F0Fu) | ((x1 & 0x0F0F0F0Fu) << 4);
+        const uint32_t xh = ((x0 >> 4) & 0x0F0F0F0Fu) | (x1 & 0xF0F0F0F0u);
+        const uint32_t l8 = xl >> 8, h8 = xh >> 8;
+        const half8 al = pack8(xl & 0x000F000Fu, xl & 0x00F000F0u, l8 & 0x000F000Fu, l8 & 0x00F000F0u);
+        const half8 ah = pack8(xh & 0x000F000Fu, xh & 0x00F000F0u, h8 & 0x000F000Fu, h8 & 0x00F000F0u);
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) d[q] = mfma16(ak, c.q8[q][i], d[q]);
+        for (int q = 0; q < kQ; ++q) {
+            d[q] = mfma16(al, c.q4[q][i], d[q]);
+            dh[q] = mfma16(ah, c.q4[q][i], dh[q]);
+        }
     }
-    floatx4 s4 = d[0];
-    if constexpr (kQ == 2) s4 += d[1];
+    floatx4 s4 = d[0] + 16.0f * dh[0];
+    if constexpr (kQ == 2) s4 += d[1] + 16.0f * dh[1];
     s4 = combine_cols<GP>(s4);
     float sc[8];
     bool valid[8];
@@ -543,6 +545,7 @@ __device__ inline void compute_step8(SegCtx<GP> &c, const StepRegs &r, int e0, i
     }
     half8 pop[2];
     softmax_step<GP, false>(c, sc, r.vpA, r.vpB, valid, pop);
+    const uint32_t M8 = 0x00FF00FFu;
     // odd value tiles accumulate 16x (matching the INT4 high-nibble scaling)
     const half8 sixteen = {16, 16, 16, 16, 16, 16, 16, 16};
 #pragma unroll

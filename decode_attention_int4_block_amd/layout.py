@@ -53,7 +53,11 @@ def decode_sub8(blocks: np.ndarray, ent) -> dict:
     e = np.asarray(ent, dtype=np.int64).reshape(-1)
     N = blocks.shape[0]
     rows = np.arange(N)[:, None]
-    kc = blocks[rows, 128 * e[:, None] + np.arange(128)[None, :]]
+    raw = blocks[rows, 128 * e[:, None] + np.arange(128)[None, :]]
+    kc = np.empty((N, 128), np.uint8)
+    for j in range(16):             # 8-dim groups stored even dims first
+        kc[:, 8 * j + 0:8 * j + 8:2] = raw[:, 8 * j:8 * j + 4]
+        kc[:, 8 * j + 1:8 * j + 8:2] = raw[:, 8 * j + 4:8 * j + 8]
     G, r = e // 4, e % 4
     n = np.arange(16)
     vc = np.empty((N, 128), np.uint8)

@@ -77,7 +77,10 @@
  *   entries; subblock j starts at byte
  *       ((slot * num_kv_heads + kv_head) * NR + j) * 4224
  *   and holds entries e = 0..15 (ring entry 16 j + e):
- *     [   0, 2048) key codes, entry-major: byte 128 e + d = code of rotated dim d;
+ *     [   0, 2048) key codes, entry-major, each group of 8 rotated dims
+ *                  8j..8j+7 stored even dims first: byte 128 e + 8 j + i holds
+ *                  dim 8j + 2i and byte 128 e + 8 j + 4 + i dim 8j + 2i + 1
+ *                  (i = 0..3);
  *     [2048, 4096) value codes, entry-fastest: with G = e / 4, r = e % 4,
  *                  byte 4 * ((G * 16 + n) * 8 + c) + r = code of value dim
  *                  16 c + n, for n = 0..15, c = 0..7;
