@@ -103,15 +103,49 @@ def cpu_baseline(wl, dw, budget_s=12.0):
                        f"(oracle quantization of the row + fp64 attention), {t_total:.1f} s, 1 thread")
 
 
-def traffic_from_profile(kernel_src_hash):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
-    p = os.path.join(ROOT, "profiles", "decode_split_qwen3_8b_async_256_pmc.json")
+def decode_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "decode_attention_int4_block_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per kv_decode_attn launch from the committed FETCH_SIZE / WRITE_SIZE
+    counter runs, or None when they were taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"kv_decode_attn_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("source_sha256") != kernel_src_hash:
+    if d.get("source_sha256") != decode_source_hash():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def device_copy_rate(torch, calibration=False, nbytes=1 << 30, reps=5):
+    """Bytes read + written per second by the runtime's device-to-device copy of
+    1 GiB: a measured ceiling for streaming kernels on this device, as context.
+    With calibration=True, one 256 MiB copy runs first (its counters calibrate
+    the HBM traffic figures)."""
+    if calibration:
+        a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return round(2 * nbytes / sec / 1e9, 1)
 
 
 def main():
@@ -122,6 +156,9 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_async_256")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="before warm-up, run one untimed 256 MiB device-to-device copy whose "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the decode kernel's")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -164,6 +201,7 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    copy_gbps = device_copy_rate(torch, calibration=args.calibration_copy)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -186,8 +224,7 @@ def main():
     dec_avg_s = float(dec_ms.mean()) / 1e3
     achieved = db["total"] / dec_avg_s / 1e9
 
-    src = open(os.path.join(ROOT, "decode_attention_int4_block_amd", "csrc", "decode.hip"), "rb").read()
-    traffic = traffic_from_profile(hashlib.sha256(src).hexdigest())
+    traffic = traffic_from_profile(cfg.name)
 
     rec = {
         "metric": METRIC,
@@ -206,7 +243,7 @@ def main():
             "workload": cfg.name, "batch": cfg.batch, "num_q_heads": cfg.num_q_heads,
             "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "page_size": wl.page_size,
             "had_block": cfg.had_block, "sink": cfg.sink, "recent": cfg.recent,
-            "lengths": "pareto(xm=512, alpha=1.5) clipped at 32768", "total_tokens": int(wl.lengths.sum()),
+            "lengths": f"{cfg.lengths}{tuple(cfg.length_args)}", "total_tokens": int(wl.lengths.sum()),
             "rotating_cache_copies": args.layers,
         },
         "tokens_heads_per_s": round(tok_heads / step_s, 1),
@@ -219,6 +256,7 @@ def main():
         "decode_algorithmic_bytes": db["total"],
         "append_algorithmic_bytes": ab,
         "bf16_equiv_GBps_decode": round(db["bf16_equiv"] / dec_avg_s / 1e9, 1),
+        "device_copy_GBps_context": copy_gbps,
         "roofline": {
             "bound": "hbm",
             "kernel": "kv_decode_attn (decode_split_kernel + decode_combine_kernel)",
