@@ -141,13 +141,15 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
             ((size_t)((int64_t)slot * a.H + hk) * a.nr8 + esub) * kSub8Bytes;
         const QParams kp = qparams(kmn, kmx, 255.0f);
         const QParams vp = qparams(vmn, vmx, 255.0f);
-        // dims 2l (even) and 2l+1 (odd) of group j = l/4: bytes 8j + l%4 and 8j + 4 + l%4
-        uint8_t *krow8 = base8 + kSub8K + ee * 128 + 8 * (lane >> 2) + (lane & 3);
-        krow8[0] = (uint8_t)qcode(x0, kp, 255.0f);
-        krow8[4] = (uint8_t)qcode(x1, kp, 255.0f);
+        // low / high nibble planes, each in the INT4 subblock layout
+        const uint32_t k0 = qcode(x0, kp, 255.0f), k1 = qcode(x1, kp, 255.0f);
+        base8[kSub8KLo + ee * 64 + lane] = (uint8_t)((k0 & 15u) | ((k1 & 15u) << 4));
+        base8[kSub8KHi + ee * 64 + lane] = (uint8_t)((k0 >> 4) | ((k1 >> 4) << 4));
+        const uint32_t c0 = qcode(v0, vp, 255.0f), c1 = qcode(v1, vp, 255.0f);
         const int G = ee >> 2, r = ee & 3;
-        base8[kSub8V + 4 * ((G * 16 + vn) * 8 + 2 * vc) + r] = (uint8_t)qcode(v0, vp, 255.0f);
-        base8[kSub8V + 4 * ((G * 16 + vn) * 8 + 2 * vc + 1) + r] = (uint8_t)qcode(v1, vp, 255.0f);
+        const int vo = 4 * ((G * 16 + vn) * 4 + vc) + r;
+        base8[kSub8VLo + vo] = (uint8_t)((c0 & 15u) | ((c1 & 15u) << 4));
+        base8[kSub8VHi + vo] = (uint8_t)((c0 >> 4) | ((c1 >> 4) << 4));
         if (lane == 0) {
             *reinterpret_cast<uint32_t *>(base8 + kSub8KP + 4 * ee) = qparam_word(kp);
             *reinterpret_cast<uint32_t *>(base8 + kSub8VP + 4 * ee) = qparam_word(vp);

@@ -16,10 +16,13 @@ constexpr int kSub4V = 1024;
 constexpr int kSub4KP = 2048;
 constexpr int kSub4VP = 2112;
 
-// INT8 subblock: 16 entries x (128 B key codes + 128 B value codes + 4 + 4 B params)
+// INT8 subblock: 16 entries x (128 B key codes + 128 B value codes + 4 + 4 B params),
+// the codes as a low-nibble and a high-nibble plane in the INT4 code layouts
 constexpr int kSub8Bytes = 4224;
-constexpr int kSub8K = 0;
-constexpr int kSub8V = 2048;
+constexpr int kSub8KLo = 0;
+constexpr int kSub8KHi = 1024;
+constexpr int kSub8VLo = 2048;
+constexpr int kSub8VHi = 3072;
 constexpr int kSub8KP = 4096;
 constexpr int kSub8VP = 4160;
 

@@ -24,11 +24,14 @@
 //   acc[row][dim]   += P[row][tok] * vcodes[tok][dim] (A = p, B = codes)
 // The query and p*scale_v are split into f16 hi + lo parts so products keep
 // fp32 accuracy.  With a query group g <= 8 the hi and lo parts share one MFMA:
-// hi in columns (rows) [0, G), lo in [G, 2G) of the 16 the instruction has, and
-// the two halves are added afterwards.  4-bit and 8-bit codes become f16 values
-// exactly by masking them into the mantissa of a subnormal (code * 2^-24, or
-// code * 2^-20 for the high nibble of a byte, compensated in the other operand
-// or the accumulator).
+// hi in columns (rows) [0, GP), lo in [GP, 2GP) of the 16 the instruction has.
+// 4-bit and 8-bit codes become f16 values exactly by masking them into the
+// mantissa of a subnormal (code * 2^-24, or code * 2^-20 for the high nibble of
+// a byte, compensated in the other operand or the accumulator).
+//
+// The softmax runs on a dense layout: the GP x 32 scores of a step are spread
+// over the 64 lanes (GP / 2 per lane) by DPP moves inside 16-lane rows, and the
+// p * scale_v products are gathered back into the MFMA row layout the same way.
 #include <hip/hip_fp16.h>
 
 #include "common.h"
@@ -43,9 +46,29 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 constexpr int kStageBytes = 4352;       // 4 x 1 KB codes + 256 B params
 constexpr int kDmaPerStep = 5;
+
+// Stage layout of the params (INT4: tokens 0..31 of the step; INT8: entries 0..15).
+constexpr int kStKP = 4096;             // key (scale, zero) of token t at kStKP + 4 t
+constexpr int kStVP = 4224;             // value (scale, zero) of token t at kStVP + 4 t
+
+// Per group class GP (query heads per hi/lo half of the MFMA columns).
+template <int GP>
+struct GC {
+    static constexpr bool kPacked = GP <= 8;
+    static constexpr int kQ = kPacked ? 1 : 2;      // query operand sets per chunk
+    static constexpr int kNP = GP / 4;              // score pairs per lane and step
+    static constexpr int kNE = 2 * kNP;             // scores per lane and step
+    static constexpr int kParts = 16 / GP;          // lanes of a 16-lane row sharing a head
+    static constexpr int kVPL = 2 * GP;             // query values per lane (GP x 128 / 64)
+    // The running max used for exp2 is raised only when a step's max exceeds it
+    // by more than kTau (log2 units), so p <= 2^kTau; the hi rows of p*s_v then
+    // hold pv / kHiScale so that they stay inside the f16 range.
+    static constexpr float kTau = kPacked ? 8.0f : 0.0f;
+    static constexpr int kHiScale = kPacked ? 256 : 1;
+};
 
 __device__ inline floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -63,15 +86,24 @@ __device__ inline uint32_t f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// hi = f16(x), lo = f16(x - hi) for a pair: hi + lo carries ~21 bits of x.
-__device__ inline void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    hi = f16x2(a, b);
-    const half2v h = __builtin_bit_cast(half2v, hi);
-    lo = f16x2(a - (float)h[0], b - (float)h[1]);
-}
-
 __device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half2v, w)[0]; }
 __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half2v, w)[1]; }
+
+// hi = f16(a / S, b / S), lo = f16(a - S hi, b - S hi): S hi + lo carries ~21
+// bits of a and b, and lo keeps absolute steps of 2^-24 for small values.
+// lo must be taken against the very f16 values packed into hi: the compiler
+// would otherwise re-derive them from a and b (e.g. by fusing the product that
+// formed a into a single-rounding f16 conversion), and where the two roundings
+// differ, hi + lo misses a by one f16 step of hi.  The empty asm makes the
+// packed word opaque.
+template <int S>
+__device__ inline void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    constexpr float inv = 1.0f / S;
+    hi = f16x2(a * inv, b * inv);
+    uint32_t h = hi;
+    __asm__("" : "+v"(h));
+    lo = f16x2(fmaf(h_lo(h), -(float)S, a), fmaf(h_hi(h), -(float)S, b));
+}
 
 __device__ inline float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -95,35 +127,106 @@ __device__ inline int ldc(const int32_t *p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t *)p)[i];
 }
 
-// Cross-lane moves (VALU, no LDS): values of the lane 16 / 32 apart, and DPP
-// shifts inside 16-lane rows.
-__device__ inline float xor16(float x, int lane) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+// ---------------------------------------------------------------------------
+// Cross-lane moves (VALU, no LDS).  DPP controls inside 16-lane rows:
+// row_shl:n (lane i <- i + n), row_shr:n (lane i <- i - n), row_ror:n
+// (lane i <- (i - n) mod 16); the bank mask selects which groups of 4 lanes of
+// each row are written, the others keep `old`.
+constexpr int kRowShl = 0x100, kRowShr = 0x110, kRowRor = 0x120;
+
+template <int CTRL, int BANKS = 0xF>
+__device__ inline uint32_t dpp(uint32_t old, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANKS, false);
 }
-__device__ inline float xor32(float x, int lane) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+template <int CTRL, int BANKS = 0xF>
+__device__ inline float dppf(float old, float src) {
+    return __uint_as_float(dpp<CTRL, BANKS>(__float_as_uint(old), __float_as_uint(src)));
 }
+
+// (r0, r1) of permlane16_swap(a, b): rows [a0 b0 a2 b2] and [a1 b1 a3 b3].
+__device__ inline void swap16(float a, float b, float &r0, float &r1) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    r0 = __uint_as_float(r[0]);
+    r1 = __uint_as_float(r[1]);
+}
+// (r0, r1) of permlane32_swap(a, b): rows [a0 a1 b0 b1] and [a2 a3 b2 b3].
+__device__ inline void swap32(float a, float b, float &r0, float &r1) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    r0 = __uint_as_float(r[0]);
+    r1 = __uint_as_float(r[1]);
+}
+
 __device__ inline float max_rows(float x) {      // max over lanes l, l^16, l^32, l^48
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    float r0, r1;
+    swap32(x, x, r0, r1);
+    x = fmaxf(r0, r1);
+    swap16(x, x, r0, r1);
+    return fmaxf(r0, r1);
 }
 __device__ inline float sum_rows(float x) {      // sum over lanes l, l^16, l^32, l^48
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    float r0, r1;
+    swap32(x, x, r0, r1);
+    x = r0 + r1;
+    swap16(x, x, r0, r1);
+    return r0 + r1;
 }
-template <int N>
-__device__ inline float row_shl(float x) {        // lane i <- lane i + N (same row; 0 past the edge)
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
+
+// Max / sum over the lanes that hold the same query head in the dense layout
+// (lanes l with equal l % GP: kParts per row, four rows).
+template <int GP>
+__device__ inline float head_max(float x) {
+    if constexpr (GP <= 8) x = fmaxf(x, dppf<kRowRor + 8>(0.0f, x));
+    if constexpr (GP == 4) x = fmaxf(x, dppf<kRowRor + 4>(0.0f, x));
+    return max_rows(x);
 }
-template <int N>
-__device__ inline uint32_t row_shr(uint32_t x) {  // lane i <- lane i - N
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + N, 0xF, 0xF, true);
+template <int GP>
+__device__ inline float head_sum(float x) {
+    if constexpr (GP <= 8) x += dppf<kRowRor + 8>(0.0f, x);
+    if constexpr (GP == 4) x += dppf<kRowRor + 4>(0.0f, x);
+    return sum_rows(x);
+}
+
+// Hadamard butterfly between lanes l and l ^ X: the lower lane ends with
+// (its value) + (partner's), the upper with (partner's) - (its value).
+template <int X>
+__device__ inline float butterfly(float x, int lane) {
+    const float sgn = (lane & X) ? -1.0f : 1.0f;
+    if constexpr (X == 16 || X == 32) {
+        float r0, r1;
+        if constexpr (X == 16) swap16(x, x, r0, r1);
+        else swap32(x, x, r0, r1);
+        // lower rows: r0 = own, r1 = partner; upper rows: r0 = partner, r1 = own
+        return fmaf(r1, sgn, r0);
+    } else {
+        float p;
+        if constexpr (X == 8) {
+            p = dppf<kRowRor + 8>(0.0f, x);
+        } else {
+            p = dppf<kRowShl + X, 0x5>(x, x);        // banks 0, 2 read lane + 4
+            p = dppf<kRowShr + X, 0xA>(p, x);        // banks 1, 3 read lane - 4
+        }
+        return fmaf(x, sgn, p);
+    }
+}
+
+// Slot J (0..3) of the packed MFMA rows: lanes with column c < GP take the hi
+// word of head c, columns [GP, 2GP) the lo word of head c - GP, both from the
+// dense lane of the same head holding slot J (part J / kNP of the row; the
+// caller passes that lane's words of local slot J % kNP).
+template <int GP, int J>
+__device__ inline uint32_t gather_slot(uint32_t hi, uint32_t lo) {
+    constexpr int NP = GC<GP>::kNP;
+    constexpr int qs = J / NP;
+    constexpr int BH = GP == 4 ? 0x1 : 0x3;
+    constexpr int BL = GP == 4 ? 0x2 : 0xC;
+    if constexpr (qs == 0) {
+        return dpp<kRowShr + GP, BL>(hi, lo);
+    } else if constexpr (qs == 1) {
+        return dpp<kRowShl + GP, BH>(lo, hi);
+    } else {
+        const uint32_t r = dpp<kRowShl + GP * qs, BH>(0u, hi);
+        return dpp<kRowShl + GP * (qs - 1), BL>(r, lo);
+    }
 }
 
 // 16 bytes per lane from global memory (uniform base + per-lane offset) into
@@ -142,10 +245,10 @@ __device__ inline void dma16(const uint8_t *base, uint32_t off, uint8_t *dst_lds
 
 __device__ inline void wait_vm_steps(int steps_after) {
     // outstanding DMA instructions allowed = kDmaPerStep * steps_after
-    static_assert(kStages == 4 && kDmaPerStep == 5, "wait table assumes 4 stages x 5 loads");
+    static_assert(kStages <= 4 && kDmaPerStep == 5, "wait table covers up to 4 stages x 5 loads");
     if (steps_after <= 0) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(0));
-    else if (steps_after == 1) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(5));
-    else if (steps_after == 2) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(10));
+    else if (steps_after == 1 || kStages == 2) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(5));
+    else if (steps_after == 2 || kStages == 3) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(10));
     else __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(15));
     KVQ_FENCE();
 }
@@ -156,28 +259,54 @@ __device__ inline void wait_lgkm0() {
 }
 
 // ---------------------------------------------------------------------------
+// Dense layout.  Lane (G, c) of a step holds kNP pairs of scores of head
+// c % GP: pair j = kNP (c / GP) + p (p < kNP) is tokens (j & 1) + 2 ee, ee in
+// {0, 1}, of rows 4G.. of subblock j >> 1 -- the k order [A0 A2 | A1 A3 | B0 B2
+// | B1 B3] of the value MFMA, one dword of f16 pairs per j.
+template <int GP>
+struct LaneCtx {
+    int lane, G, n, part, head;
+    uint32_t offKP;                             // stage byte offset of this lane's first key params
+    int tok4[GC<GP>::kNE];                      // token (entry) of each dense score within the step
+};
+
+template <int GP>
+__device__ inline LaneCtx<GP> lane_ctx(int lane) {
+    constexpr int NP = GC<GP>::kNP;
+    LaneCtx<GP> L;
+    L.lane = lane;
+    L.G = lane >> 4;
+    L.n = lane & 15;
+    L.part = L.n / GP;
+    L.head = L.n % GP;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int j = NP * L.part + p;
+#pragma unroll
+        for (int ee = 0; ee < 2; ++ee) L.tok4[2 * p + ee] = 16 * (j >> 1) + 4 * L.G + (j & 1) + 2 * ee;
+    }
+    const int j0 = NP * L.part;
+    L.offKP = kStKP + 4 * (16 * (j0 >> 1) + 4 * L.G + (j0 & 1));
+    return L;
+}
+
 // Data of one step as read from its LDS stage.
+template <int GP>
 struct StepRegs {
     u32x4 kA, kB;       // INT4: key codes of token l%16 (A/B), dims 32G..+32
                         // INT8: key bytes of entry l%16, dims 32G..+16 (kA) and +16..+32 (kB)
     u32x4 vA, vB;       // INT4: value codes, dims n + 32c / n + 16 + 32c, tokens 4G..4G+3
                         // INT8: value bytes, tiles 0..3 (vA) and 4..7 (vB), entries 4G..4G+3
-    u32x4 kpA, kpB;     // key params of tokens 4G..4G+3 (INT8: kpA only)
-    u32x4 vpA, vpB;     // value params
+    uint32_t kp[GC<GP>::kNE], vp[GC<GP>::kNE];   // params of this lane's dense scores
 };
 
-// GP: columns (rows) per hi/lo half -- 4 or 8 packs hi and lo into one MFMA,
-// 16 uses separate MFMAs for hi and lo.
 template <int GP>
 struct SegCtx {
-    static constexpr bool kPacked = GP <= 8;
-    static constexpr int kQ = kPacked ? 1 : 2;     // query operand sets per chunk
-    int lane, G, n, col;
-    int g;
-    half8 q4[kQ][4];    // query operands (INT4 nibble order; INT8 keys are split into nibbles)
-    float K1;           // 2^(24 - e) * log2(e) / sqrt(128)
-    float K2;           // sum(q~) * log2(e) / sqrt(128) of head col % GP
-    float m, lsum, zsum;
+    half8 q4[GC<GP>::kQ][4];   // query operands (INT4 nibble order; INT8 keys are split into nibbles)
+    float K1;           // 2^(24 - e) * log2(e) / sqrt(128), wave-uniform
+    float Rh;           // sum(q~ of this lane's head) * 2^(e - 24)
+    float mK;           // running max of this lane's head (log2 units)
+    float lsum, zsum;   // sums of p and of p * zero_v over this lane's scores
     floatx4 O[8];       // acc[row 4G+i][16 t + n], odd tiles scaled by 16
 };
 
@@ -201,38 +330,96 @@ __device__ inline void cursor_next(const DecodeArgs &a, Cursor &c) {
     }
 }
 
-// Block table entries and slot the producer needs for the step at a cursor;
-// looked up one step ahead so the scalar loads overlap the compute.
+// Block-table entries of the producer's steps, gathered 16 units at a time
+// a whole half-batch before they are used.  The gather goes straight into LDS
+// (one dword per lane through the direct global->LDS path), so no VGPR holds a
+// load in flight across steps; the in-order vector-memory counter the stage
+// waits already use covers it.  pg[h][0][j] / pg[h][1][j] are the pages of
+// subblocks A / B of unit hb + j (INT8 units: the slot in [0]).
+constexpr int kPgHalf = 16;
+constexpr int kPgBytes = 2 * 2 * kPgHalf * 4;
+
+// Wave-uniform row walk of the half-batches: the row holding the next
+// half-batch's first unit and that row's first unit.
+struct BatchCursor {
+    int b;
+    int64_t pre;
+};
+
+__device__ inline void fetch_pages(const DecodeArgs &a, int64_t hb, int64_t u_end, BatchCursor &bc, int lane,
+                                   uint32_t *pg_half) {
+    const int64_t u = hb + (lane & (kPgHalf - 1));
+    const int64_t lim = min(hb + kPgHalf, u_end);
+    int myL = 0, myslot = 0;
+    int64_t mypre = 0;
+    bool mine = false;
+    int b = bc.b;
+    int64_t pre = bc.pre;
+    while (b < a.B) {
+        const int L = ldc(a.ctx_len, b);
+        const int64_t rowu = (int64_t)row_plan(L, a.s, a.w).cost * a.H;
+        if (pre + rowu > hb && rowu > 0) {
+            const int sl = ldc(a.slot, b);
+            if (u >= pre && u < pre + rowu) {
+                mine = true;
+                mypre = pre;
+                myL = L;
+                myslot = sl;
+            }
+        }
+        if (pre + rowu >= lim) break;
+        pre += rowu;
+        ++b;
+    }
+    bc.b = b;
+    bc.pre = pre;
+    const int32_t *src = nullptr;
+    uint32_t val = 0;
+    if (mine && u < u_end) {
+        const RowPlan rp = row_plan(myL, a.s, a.w);
+        const uint32_t off = (uint32_t)(u - mypre);
+        const uint32_t hk = off / (uint32_t)rp.cost;
+        const int r = (int)(off - hk * (uint32_t)rp.cost);
+        if (r < rp.n4) {
+            const int pos0 = (rp.k0 + r) * 32;
+            // lanes kPgHalf.. take subblock B (the producer ignores it past the INT4 region)
+            const int pos = (lane >= kPgHalf && pos0 + 16 < rp.hi4) ? pos0 + 16 : pos0;
+            src = a.block_table + (int64_t)myslot * a.bt_stride + (pos >> a.logP);
+        } else {
+            val = (uint32_t)myslot;
+        }
+    }
+    // lanes [0, kPgHalf) fill pa, [kPgHalf, 2 kPgHalf) pb; the others write nothing
+    if (lane < 2 * kPgHalf) {
+        if (src != nullptr)
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)pg_half, 4, 0, 0);
+        else
+            pg_half[lane] = val;
+    }
+}
+
 struct Lookup {
     int slot, pageA, pageB;
 };
 
-__device__ inline Lookup lookup(const DecodeArgs &a, const Cursor &c) {
-    Lookup k;
-    k.slot = ldc(a.slot, c.b);
-    k.pageA = 0;
-    k.pageB = 0;
-    if (c.r < c.rp.n4) {
-        const int pos0 = (c.rp.k0 + c.r) * 32;
-        const int32_t *bt = a.block_table + (int64_t)k.slot * a.bt_stride;
-        k.pageA = ldc(bt, pos0 >> a.logP);
-        k.pageB = (pos0 + 16 < c.rp.hi4) ? ldc(bt, (pos0 + 16) >> a.logP) : k.pageA;
-    }
-    return k;
-}
-
+// ---------------------------------------------------------------------------
+// Query of one segment: load, block Hadamard rotation (SAW-INT4, section 2),
+// power-of-two scaling, hi/lo split, and the MFMA B operands.
+//
+// Lane (G, c) rotates head c % GP, dims 32 G + kVPL (c / GP) + e (e < kVPL):
+// Hadamard strides below kVPL stay inside the lane, a stride s at or above it
+// pairs lanes l and l ^ (s / 2).  The B operand of chunk i (dims 32 G + 8 i ..)
+// for column c is then gathered from the lane of part i / (kVPL / 8).
 template <int GP>
-__device__ inline void build_query(const DecodeArgs &a, int b, int hk, SegCtx<GP> &c) {
-    // lane column col: head col % GP, part hi (col < GP) or lo (GP <= col < 2GP);
-    // unpacked: every column < g carries its head in both operand sets.
-    const int head = SegCtx<GP>::kPacked ? (c.col % GP) : c.col;
-    const bool live = (SegCtx<GP>::kPacked ? c.col < 2 * GP : true) && head < c.g;
-    float x[32];
-    if (live) {
-        const uint16_t *qp = a.q + ((int64_t)b * a.Hq + (int64_t)hk * c.g + head) * kHeadDim + 32 * c.G;
+__device__ inline void build_query(const DecodeArgs &a, int b, int hk, const LaneCtx<GP> &L, SegCtx<GP> &c) {
+    constexpr int V = GC<GP>::kVPL;
+    constexpr int CPL = V / 8;            // chunks of 8 dims per lane (= kNP)
+    float x[V];
+    if (L.head < a.g) {
+        const uint16_t *qp = a.q + ((int64_t)b * a.Hq + (int64_t)hk * a.g + L.head) * kHeadDim + 32 * L.G + V * L.part;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            u32x4 w = ldg<u32x4>(qp + 8 * v);
+        for (int v = 0; v < V / 8; ++v) {
+            const u32x4 w = ldg<u32x4>(qp + 8 * v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 x[8 * v + 2 * e] = bf16f(w[e] & 0xFFFFu);
@@ -241,155 +428,187 @@ __device__ inline void build_query(const DecodeArgs &a, int b, int hk, SegCtx<GP
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+        for (int i = 0; i < V; ++i) x[i] = 0.0f;
     }
-    // block Hadamard (orthonormal) of the query; in-lane strides 1..16
 #pragma unroll
-    for (int len = 1; len < 32; len <<= 1) {
+    for (int len = 1; len < V; len <<= 1) {
         if (len < a.h) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < V; ++i) {
                 if ((i & len) == 0) {
-                    float u = x[i], v = x[i + len];
+                    const float u = x[i], v = x[i + len];
                     x[i] = u + v;
                     x[i + len] = u - v;
                 }
             }
         }
     }
-    // strides 32 and 64 cross lanes (lane groups G differ in bit 0 / bit 1)
-    if (32 < a.h) {
-        const bool upper = (c.lane & 16) != 0;
+    if constexpr (V <= 8) {
+        if (8 < a.h) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float p = xor16(x[i], c.lane);
-            x[i] = upper ? (p - x[i]) : (x[i] + p);
+            for (int i = 0; i < V; ++i) x[i] = butterfly<4>(x[i], L.lane);
         }
     }
-    if (64 < a.h) {
-        const bool upper = (c.lane & 32) != 0;
+    if constexpr (V <= 16) {
+        if (16 < a.h) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float p = xor32(x[i], c.lane);
-            x[i] = upper ? (p - x[i]) : (x[i] + p);
+            for (int i = 0; i < V; ++i) x[i] = butterfly<8>(x[i], L.lane);
         }
+    }
+    if (32 < a.h) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) x[i] = butterfly<16>(x[i], L.lane);
+    }
+    if (64 < a.h) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) x[i] = butterfly<32>(x[i], L.lane);
     }
     float sum = 0.0f, amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        x[i] *= a.inv_sqrt_h;
+    for (int i = 0; i < V; ++i) {
         sum += x[i];
         amax = fmaxf(amax, fabsf(x[i]));
     }
-    sum = sum_rows(sum);
+    sum = head_sum<GP>(sum) * a.inv_sqrt_h;
+    amax = max_rows(amax);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax = __int_as_float(uni(__float_as_int(amax))) * a.inv_sqrt_h;
     int E = 0;
     (void)frexpf(amax, &E);
     const int e = amax > 0.0f ? 14 - E : 0;      // |q * 2^e| < 2^14
-    const float sc = ldexpf(1.0f, e);
+    const float sc = a.inv_sqrt_h * ldexpf(1.0f, e);
+    const float s16 = sc * 0.0625f;
     const float c0 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
     c.K1 = ldexpf(c0, 24 - e);
-    c.K2 = sum * c0;
-    const bool lo_part = SegCtx<GP>::kPacked && c.col >= GP;
+    c.Rh = ldexpf(sum, e - 24);
+    // chunks of 8 dims in the nibble order of a code dword:
+    // dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
+    uint32_t H[CPL][4], Lo[CPL][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float *y = x + 8 * i;
-        uint32_t h[4], l[4];
-        // nibble order of a code dword: dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
-        split2(y[0] * sc, y[4] * sc, h[0], l[0]);
-        split2(y[1] * sc * 0.0625f, y[5] * sc * 0.0625f, h[1], l[1]);
-        split2(y[2] * sc, y[6] * sc, h[2], l[2]);
-        split2(y[3] * sc * 0.0625f, y[7] * sc * 0.0625f, h[3], l[3]);
-        if constexpr (SegCtx<GP>::kPacked) {
-            c.q4[0][i] = lo_part ? pack8(l[0], l[1], l[2], l[3]) : pack8(h[0], h[1], h[2], h[3]);
-        } else {
-            c.q4[0][i] = pack8(h[0], h[1], h[2], h[3]);
-            c.q4[1][i] = pack8(l[0], l[1], l[2], l[3]);
+    for (int k = 0; k < CPL; ++k) {
+        const float *y = x + 8 * k;
+        split2<1>(y[0] * sc, y[4] * sc, H[k][0], Lo[k][0]);
+        split2<1>(y[1] * s16, y[5] * s16, H[k][1], Lo[k][1]);
+        split2<1>(y[2] * sc, y[6] * sc, H[k][2], Lo[k][2]);
+        split2<1>(y[3] * s16, y[7] * s16, H[k][3], Lo[k][3]);
+    }
+    if constexpr (GC<GP>::kPacked) {
+        uint32_t w[4][4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            w[0][d] = gather_slot<GP, 0>(H[0][d], Lo[0][d]);
+            w[1][d] = gather_slot<GP, 1>(H[1 % CPL][d], Lo[1 % CPL][d]);
+            w[2][d] = gather_slot<GP, 2>(H[2 % CPL][d], Lo[2 % CPL][d]);
+            w[3][d] = gather_slot<GP, 3>(H[3 % CPL][d], Lo[3 % CPL][d]);
         }
-    }
-}
-
-// Raw score sums of the 4 tokens of one subblock (packed mode: hi + lo columns).
-template <int GP>
-__device__ inline floatx4 combine_cols(floatx4 d) {
-    if constexpr (GP <= 8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] += row_shl<GP>(d[i]);
-    }
-    return d;
-}
-
-// Online-softmax update for this lane's 8 scores (tokens 4G+i of subblocks A,
-// B) and the value MFMA A operands (rows = heads, k = [A0 A2 A1 A3 B0 B2 B1 B3]).
-template <int GP, bool FULL>
-__device__ inline void softmax_step(SegCtx<GP> &c, float sc[8], const u32x4 &vpA, const u32x4 &vpB,
-                                    const bool valid[8], half8 pop[2]) {
-    float mstep = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mstep = fmaxf(mstep, sc[i]);
-    mstep = max_rows(mstep);
-    const float mnew = fmaxf(c.m, mstep);
-    const bool head_lane = (SegCtx<GP>::kPacked ? c.col < GP : true) && c.col < c.g;
-    const bool grow = head_lane && mnew > c.m;
-    if (__any(grow)) {
-        const float alpha = grow ? (c.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(c.m - mnew)) : 1.0f;
-        c.lsum *= alpha;
-        c.zsum *= alpha;
-        const int rb = 4 * (c.lane >> 4);
+        for (int i = 0; i < 4; ++i) c.q4[0][i] = pack8(w[i][0], w[i][1], w[i][2], w[i][3]);
+    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = rb + i;
-            const float ar = __shfl(alpha, SegCtx<GP>::kPacked ? row % GP : row, 64);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) c.O[t][i] *= ar;
+            c.q4[0][i] = pack8(H[i][0], H[i][1], H[i][2], H[i][3]);
+            c.q4[1][i] = pack8(Lo[i][0], Lo[i][1], Lo[i][2], Lo[i][3]);
         }
-        if (grow) c.m = mnew;
-    }
-    const float m = c.m;
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t vp = i < 4 ? vpA[i] : vpB[i - 4];
-        const float p = __builtin_amdgcn_exp2f(sc[i] - m);
-        if (FULL) {
-            c.lsum += p;
-            c.zsum = fmaf(p, h_hi(vp), c.zsum);
-            pv[i] = p * h_lo(vp);
-        } else {
-            // params of positions past the written context are arbitrary bytes
-            // (possibly NaN as fp16): select, never multiply by zero
-            c.lsum += valid[i] ? p : 0.0f;
-            c.zsum = valid[i] ? fmaf(p, h_hi(vp), c.zsum) : c.zsum;
-            pv[i] = valid[i] ? p * h_lo(vp) : 0.0f;
-        }
-    }
-    uint32_t h[4], l[4];
-    split2(pv[0], pv[2], h[0], l[0]);
-    split2(pv[1], pv[3], h[1], l[1]);
-    split2(pv[4], pv[6], h[2], l[2]);
-    split2(pv[5], pv[7], h[3], l[3]);
-    if constexpr (SegCtx<GP>::kPacked) {
-        // rows [GP, 2GP) take the lo part of head row - GP
-        const bool lo_row = c.col >= GP;
-        uint32_t o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t s = row_shr<GP>(l[k]);
-            o[k] = lo_row ? s : h[k];
-        }
-        pop[0] = pack8(o[0], o[1], o[2], o[3]);
-    } else {
-        pop[0] = pack8(h[0], h[1], h[2], h[3]);
-        pop[1] = pack8(l[0], l[1], l[2], l[3]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Producer: issue the 5 direct-to-LDS loads of the step at cursor c into stage st.
+// Score sums of the step in the MFMA layout -> dense layout.
+// s[0..3]: tokens 4G + i of subblock A, s[4..7]: of subblock B, valid in the
+// lanes of columns c < GP (hi + lo already added).
+template <int GP>
+__device__ inline void spread(const float s[8], float d[GC<GP>::kNE]) {
+    constexpr int NP = GC<GP>::kNP;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+        for (int ee = 0; ee < 2; ++ee) {
+            // part 0 lanes keep their own value of pair p
+            float v = s[4 * (p >> 1) + (p & 1) + 2 * ee];
+            if constexpr (GP == 4) {
+                v = dppf<kRowShr + 4, 0x2>(v, s[1 + 2 * ee]);     // part 1: pair 1
+                v = dppf<kRowShr + 8, 0x4>(v, s[4 + 2 * ee]);     // part 2: pair 2
+                v = dppf<kRowShr + 12, 0x8>(v, s[5 + 2 * ee]);    // part 3: pair 3
+            } else if constexpr (GP == 8) {
+                v = dppf<kRowShr + 8, 0xC>(v, s[4 + p + 2 * ee]); // part 1: pair 2 + p
+            }
+            d[2 * p + ee] = v;
+        }
+    }
+}
+
+// score (log2 units / K1) of one token from its raw code dot product d
+__device__ inline float tscore(float d, uint32_t kp, float Rh) {
+    return fmaf(d, h_lo(kp), h_hi(kp) * Rh);
+}
+
+// Online-softmax update on the dense scores t (-inf where invalid, with the
+// value params of invalid tokens zeroed); returns the value MFMA A operand(s):
+// rows = query heads (packed: hi rows then lo rows), k = the step's 32 tokens
+// in pair order.
+template <int GP>
+__device__ inline void softmax_dense(SegCtx<GP> &c, const LaneCtx<GP> &L, const float t[GC<GP>::kNE],
+                                     const uint32_t vp[GC<GP>::kNE], half8 pop[GC<GP>::kQ]) {
+    constexpr int NE = GC<GP>::kNE, NP = GC<GP>::kNP;
+    constexpr int HS = GC<GP>::kHiScale;
+    float ml = t[0];
+#pragma unroll
+    for (int e = 1; e < NE; ++e) ml = fmaxf(ml, t[e]);
+    // lanes of one head share mK, so a lane-local test finds every head whose
+    // max must move; the head-wide max is taken only then
+    if (__any(ml * c.K1 > c.mK + GC<GP>::kTau)) {
+        const float mt = head_max<GP>(ml) * c.K1;
+        const bool grow = mt > c.mK + GC<GP>::kTau;
+        const float mnew = grow ? mt : c.mK;
+        const float alpha = c.mK == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(c.mK - mnew);
+        c.lsum *= alpha;
+        c.zsum *= alpha;
+        c.mK = mnew;
+        // accumulator row 4G + i holds head (4G + i) % GP (unpacked: head 4G + i)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ar;
+            if constexpr (GP == 4) {
+                ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
+            } else if constexpr (GP == 8) {
+                const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
+                const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + i));
+                ar = (L.G & 1) ? a1 : a0;
+            } else {
+                ar = __shfl(alpha, 4 * L.G + i, 64);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) c.O[tt][i] *= ar;
+        }
+    }
+    const float nm = -c.mK;
+    float pv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(t[e], c.K1, nm));
+        c.lsum += p;
+        c.zsum = fmaf(p, h_hi(vp[e]), c.zsum);
+        pv[e] = p * h_lo(vp[e]);
+    }
+    uint32_t H[NP], Lw[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) split2<HS>(pv[2 * p], pv[2 * p + 1], H[p], Lw[p]);
+    if constexpr (GC<GP>::kPacked) {
+        pop[0] = pack8(gather_slot<GP, 0>(H[0], Lw[0]), gather_slot<GP, 1>(H[1 % NP], Lw[1 % NP]),
+                       gather_slot<GP, 2>(H[2 % NP], Lw[2 % NP]), gather_slot<GP, 3>(H[3 % NP], Lw[3 % NP]));
+    } else {
+        pop[0] = pack8(H[0], H[1 % NP], H[2 % NP], H[3 % NP]);
+        pop[1] = pack8(Lw[0], Lw[1 % NP], Lw[2 % NP], Lw[3 % NP]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Producer: issue the 5 direct-to-LDS loads of the step at cursor c into stage
+// st.  Both kinds of step leave key params at stage offset 4096 + 4 t and value
+// params at 4224 + 4 t for token (entry) t.
 __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lookup &k, uint8_t *st,
-                                  uint32_t offK4, uint32_t offV4, uint32_t offP4,
-                                  uint32_t offK8, uint32_t offV8, uint32_t offP8, int lane) {
+                                  uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8, int lane) {
     if (c.r < c.rp.n4) {
         const int pos0 = (c.rp.k0 + c.r) * 32;
         const int subs = a.P >> 4;
@@ -399,51 +618,76 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
         const uint8_t *baseB = (pos0 + 16 < c.rp.hi4)
             ? a.int4_pool + ((size_t)((int64_t)k.pageB * a.H + c.hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSub4Bytes
             : baseA;
-        dma16(baseA, offK4, st + 0);
-        dma16(baseB, offK4, st + 1024);
-        dma16(baseA, offV4, st + 2048);
-        dma16(baseB, offV4, st + 3072);
+        dma16(baseA + kSub4K, offK, st + 0);
+        dma16(baseB + kSub4K, offK, st + 1024);
+        dma16(baseA + kSub4V, offV, st + 2048);
+        dma16(baseB + kSub4V, offV, st + 3072);
         if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP4, st + 4096);
     } else {
+        // the low-nibble planes take the place of subblock A, the high-nibble
+        // planes that of subblock B
         const int sub = c.r - c.rp.n4;
         const uint8_t *base = a.int8_pool + ((size_t)((int64_t)k.slot * a.H + c.hk) * a.nr8 + sub) * kSub8Bytes;
-        dma16(base, offK8, st + 0);
-        dma16(base, offK8 + 16, st + 1024);
-        dma16(base, offV8, st + 2048);
-        dma16(base, offV8 + 16, st + 3072);
-        if (lane < 8) dma16(base, offP8, st + 4096);
+        dma16(base + kSub8KLo, offK, st + 0);
+        dma16(base + kSub8KHi, offK, st + 1024);
+        dma16(base + kSub8VLo, offV, st + 2048);
+        dma16(base + kSub8VHi, offV, st + 3072);
+        if (lane < 16 && (lane & 4) == 0) dma16(base, offP8, st + 4096);
     }
 }
 
-__device__ inline StepRegs read_stage(const uint8_t *st, bool int4, int lane) {
-    StepRegs r;
-    const int G = lane >> 4;
+__device__ inline uint32_t lds32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+template <int GP>
+__device__ inline StepRegs<GP> read_stage(const uint8_t *st, const LaneCtx<GP> &L) {
+    StepRegs<GP> r;
+    const int lane = L.lane;
     r.kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
     r.kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
     r.vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
     r.vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
-    r.kpA = *reinterpret_cast<const u32x4 *>(st + 4096 + G * 16);
-    if (int4) {
-        r.kpB = *reinterpret_cast<const u32x4 *>(st + 4160 + G * 16);
-        r.vpA = *reinterpret_cast<const u32x4 *>(st + 4224 + G * 16);
-        r.vpB = *reinterpret_cast<const u32x4 *>(st + 4288 + G * 16);
+    const uint8_t *kp = st + L.offKP;
+    const uint8_t *vp = st + L.offKP + (kStVP - kStKP);
+    if constexpr (GP == 4) {
+        // tokens t0, t0 + 2
+        r.kp[0] = lds32(kp);
+        r.kp[1] = lds32(kp + 8);
+        r.vp[0] = lds32(vp);
+        r.vp[1] = lds32(vp + 8);
     } else {
-        r.vpA = *reinterpret_cast<const u32x4 *>(st + 4160 + G * 16);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        r.kpB = z;
-        r.vpB = z;
+        // GP / 8 runs of 4 tokens (4G .. 4G + 3 of a subblock), pairs (0, 2), (1, 3)
+#pragma unroll
+        for (int s = 0; s < GP / 8; ++s) {
+            const u32x4 wk = *reinterpret_cast<const u32x4 *>(kp + 64 * s);
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(vp + 64 * s);
+            r.kp[4 * s + 0] = wk[0]; r.kp[4 * s + 1] = wk[2];
+            r.kp[4 * s + 2] = wk[1]; r.kp[4 * s + 3] = wk[3];
+            r.vp[4 * s + 0] = wv[0]; r.vp[4 * s + 1] = wv[2];
+            r.vp[4 * s + 2] = wv[1]; r.vp[4 * s + 3] = wv[3];
+        }
     }
     return r;
 }
 
-// score (log2 units) of one token from its raw code dot product d
-__device__ inline float score(float d, uint32_t kp, float K1, float K2) {
-    return fmaf(d, h_lo(kp) * K1, h_hi(kp) * K2);
+// Hi + lo query columns of a score MFMA result.
+template <int GP>
+__device__ inline floatx4 combine_cols(floatx4 d) {
+    if constexpr (GP <= 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] += dppf<kRowShl + GP>(0.0f, d[i]);
+    }
+    return d;
 }
 
-template <int GP, bool FULL>
-__device__ inline void compute_step4(SegCtx<GP> &c, const StepRegs &r, int pos0, int lo4, int hi4) {
-    constexpr int kQ = SegCtx<GP>::kQ;
+// One step: an INT4 step of 32 positions (subblocks A and B) or an INT8 step
+// of the 16 ring entries of one subblock, whose low- and high-nibble planes
+// stand in for A and B: the key dot products add as lo + 16 hi, and the value
+// MFMA weighs the B half of k by 16 p.  Token t of the step is valid iff
+// lo <= base + t < hi.
+template <int GP>
+__device__ inline void compute_step(SegCtx<GP> &c, const LaneCtx<GP> &L, const StepRegs<GP> &r, bool int8,
+                                    int base, int lo, int hi) {
+    constexpr int kQ = GC<GP>::kQ, NE = GC<GP>::kNE;
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
     floatx4 dA[kQ], dB[kQ];
 #pragma unroll
@@ -465,25 +709,38 @@ __device__ inline void compute_step4(SegCtx<GP> &c, const StepRegs &r, int pos0,
         sA += dA[1];
         sB += dB[1];
     }
+    const float f8 = int8 ? 16.0f : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sA[i] = fmaf(sB[i], f8, sA[i]);
     sA = combine_cols<GP>(sA);
     sB = combine_cols<GP>(sB);
-    float sc[8];
-    bool valid[8];
+    const float s8[8] = {sA[0], sA[1], sA[2], sA[3], sB[0], sB[1], sB[2], sB[3]};
+    float d[NE], t[NE];
+    uint32_t vp[NE];
+    spread<GP>(s8, d);
+    const uint32_t off = (uint32_t)(base - lo), span = (uint32_t)(hi - lo);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t kp = i < 4 ? r.kpA[i] : r.kpB[i - 4];
-        const float s = score(i < 4 ? sA[i] : sB[i - 4], kp, c.K1, c.K2);
-        if (FULL) {
-            valid[i] = true;
-            sc[i] = s;
-        } else {
-            const int p = pos0 + (i < 4 ? 0 : 16) + 4 * c.G + (i & 3);
-            valid[i] = p >= lo4 && p < hi4;
-            sc[i] = valid[i] ? s : kNegInf;
+    for (int e = 0; e < NE; ++e) {
+        // params of positions past the written context are arbitrary bytes
+        // (possibly NaN as fp16): select, never multiply by zero
+        const bool ok = (uint32_t)L.tok4[e] + off < span;
+        t[e] = ok ? tscore(d[e], r.kp[e], c.Rh) : kNegInf;
+        vp[e] = ok ? r.vp[e] : 0u;
+    }
+    half8 pop[kQ];
+    softmax_dense<GP>(c, L, t, vp, pop);
+    // INT8: k slots 2, 3 (the high-nibble plane) weigh 16 p of slots 0, 1; the
+    // INT4 slots 2, 3 (subblock B) are kept by weight 1 and weight 0 on the
+    // copy of slots 0, 1
+    {
+        const _Float16 wb = int8 ? (_Float16)0.0f : (_Float16)1.0f;
+        const _Float16 wa = int8 ? (_Float16)16.0f : (_Float16)0.0f;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pop[q][4 + k] = pop[q][4 + k] * wb + pop[q][k] * wa;
         }
     }
-    half8 pop[2];
-    softmax_step<GP, FULL>(c, sc, r.vpA, r.vpB, valid, pop);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
         const uint32_t x = r.vA[cc], x8 = x >> 8, y = r.vB[cc], y8 = y >> 8;
@@ -497,130 +754,107 @@ __device__ inline void compute_step4(SegCtx<GP> &c, const StepRegs &r, int pos0,
     }
 }
 
-// One INT8 subblock of 16 ring entries starting at e0 (the B half of the value
-// MFMA is zero).
+// ---------------------------------------------------------------------------
+// End of a segment.  Per-head l, z totals, and the accumulator rows of each
+// head brought together: R[t][k] is dims 16 t + n of head seg_head(k).
 template <int GP>
-__device__ inline void compute_step8(SegCtx<GP> &c, const StepRegs &r, int e0, int n8e) {
-    constexpr int kQ = SegCtx<GP>::kQ;
-    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 d[kQ];
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) d[q] = zero4;
-    floatx4 dh[kQ];
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) dh[q] = zero4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // dims 32G + 8i .. +8: dwords 2i (even dims) and 2i+1 (odd dims); the
-        // low and high nibbles of the 8 codes form two INT4-ordered dwords
-        const uint32_t x0 = i < 2 ? r.kA[2 * i] : r.kB[2 * i - 4];
-        const uint32_t x1 = i < 2 ? r.kA[2 * i + 1] : r.kB[2 * i - 3];
-        const uint32_t xl = (x0 & 0x0F0F0F0Fu) | ((x1 & 0x0F0F0F0Fu) << 4);
-        const uint32_t xh = ((x0 >> 4) & 0x0F0F0F0Fu) | (x1 & 0xF0F0F0F0u);
-        const uint32_t l8 = xl >> 8, h8 = xh >> 8;
-        const half8 al = pack8(xl & 0x000F000Fu, xl & 0x00F000F0u, l8 & 0x000F000Fu, l8 & 0x00F000F0u);
-        const half8 ah = pack8(xh & 0x000F000Fu, xh & 0x00F000F0u, h8 & 0x000F000Fu, h8 & 0x00F000F0u);
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-            d[q] = mfma16(al, c.q4[q][i], d[q]);
-            dh[q] = mfma16(ah, c.q4[q][i], dh[q]);
-        }
-    }
-    floatx4 s4 = d[0] + 16.0f * dh[0];
-    if constexpr (kQ == 2) s4 += d[1] + 16.0f * dh[1];
-    s4 = combine_cols<GP>(s4);
-    float sc[8];
-    bool valid[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (i < 4) {
-            const int e = e0 + 4 * c.G + i;
-            valid[i] = e < n8e;
-            const float s = score(s4[i], r.kpA[i], c.K1, c.K2);
-            sc[i] = valid[i] ? s : kNegInf;
-        } else {
-            valid[i] = false;
-            sc[i] = kNegInf;
-        }
-    }
-    half8 pop[2];
-    softmax_step<GP, false>(c, sc, r.vpA, r.vpB, valid, pop);
-    const uint32_t M8 = 0x00FF00FFu;
-    // odd value tiles accumulate 16x (matching the INT4 high-nibble scaling)
-    const half8 sixteen = {16, 16, 16, 16, 16, 16, 16, 16};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const uint32_t x = t < 4 ? r.vA[t] : r.vB[t - 4];
-        const half8 vv = pack8(x & M8, (x >> 8) & M8, 0u, 0u);
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) c.O[t] = mfma16((t & 1) ? pop[q] * sixteen : pop[q], vv, c.O[t]);
-    }
-}
+struct SegOut {
+    static constexpr int kK = GC<GP>::kPacked ? 2 : 4;
+    float R[8][kK];
+    int head[kK];       // query head of R[.][k] in this lane, or -1
+};
 
-// End of a segment: per-head l, z totals over the four lane rows, and in
-// packed mode the hi and lo accumulator rows added (hi rows keep the sum).
 template <int GP>
-__device__ inline void reduce_segment(SegCtx<GP> &c) {
-    c.lsum = sum_rows(c.lsum);
-    c.zsum = sum_rows(c.zsum);
+__device__ inline SegOut<GP> reduce_segment(SegCtx<GP> &c, const LaneCtx<GP> &L, int g) {
+    constexpr float HS = (float)GC<GP>::kHiScale;
+    c.lsum = head_sum<GP>(c.lsum);
+    c.zsum = head_sum<GP>(c.zsum);
+    SegOut<GP> s;
     if constexpr (GP == 4) {
+        // rows 0-3 (G = 0) hi, 4-7 (G = 1) lo of heads 0-3: row 0 gets heads
+        // k, row 1 heads k + 2
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c.O[t][i] += xor16(c.O[t][i], c.lane);
+            for (int k = 0; k < 2; ++k) {
+                float r0, r1;
+                swap16(c.O[t][k], c.O[t][k + 2], r0, r1);
+                s.R[t][k] = fmaf(r0, HS, r1);
+            }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int hd = k + 2 * L.G;
+            s.head[k] = (L.G < 2 && hd < g) ? hd : -1;
+        }
     } else if constexpr (GP == 8) {
+        // rows 0-7 (G = 0, 1) hi, 8-15 (G = 2, 3) lo of heads 0-7
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c.O[t][i] += xor32(c.O[t][i], c.lane);
+            for (int k = 0; k < 2; ++k) {
+                float r0, r1;
+                swap32(c.O[t][k], c.O[t][k + 2], r0, r1);
+                s.R[t][k] = fmaf(r0, HS, r1);
+            }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int hd = k + 4 * (L.G & 1) + 2 * (L.G >> 1);
+            s.head[k] = hd < g ? hd : -1;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s.R[t][k] = c.O[t][k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int hd = 4 * L.G + k;
+            s.head[k] = hd < g ? hd : -1;
+        }
     }
-}
-
-// Head held by accumulator row 4G + i, or -1 (lo rows in packed mode, rows >= g).
-template <int GP>
-__device__ inline int row_head(const SegCtx<GP> &c, int i) {
-    const int row = 4 * c.G + i;
-    return (row < GP && row < c.g) ? row : -1;
+    return s;
 }
 
 // Output of a segment that one worker attended completely: straight from registers.
 template <int GP>
-__device__ inline void finalize_regs(const DecodeArgs &a, const SegCtx<GP> &c, int b, int hk) {
-    float *ob = a.out + ((int64_t)b * a.Hq + (int64_t)hk * c.g) * kHeadDim;
+__device__ inline void finalize_regs(const DecodeArgs &a, const SegCtx<GP> &c, const LaneCtx<GP> &L,
+                                     const SegOut<GP> &s, int b, int hk) {
+    float *ob = a.out + ((int64_t)b * a.Hq + (int64_t)hk * a.g) * kHeadDim;
+    const float rl = 1.0f / c.lsum;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = row_head(c, i);
-        const float zr = __shfl(c.zsum, r < 0 ? 0 : r, 64);
-        const float lr = __shfl(c.lsum, r < 0 ? 0 : r, 64);
-        if (r >= 0) {
-            const float inv = 1.0f / lr;
+    for (int k = 0; k < SegOut<GP>::kK; ++k) {
+        const int hd = s.head[k];
+        const float zr = __shfl(c.zsum, hd < 0 ? 0 : hd, 64);
+        const float ir = __shfl(rl, hd < 0 ? 0 : hd, 64);
+        if (hd >= 0) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const float sc = (t & 1) ? 1048576.0f : 16777216.0f;   // 2^20 / 2^24
-                ob[r * kHeadDim + 16 * t + c.n] = (c.O[t][i] * sc + zr) * inv;
+                ob[hd * kHeadDim + 16 * t + L.n] = fmaf(s.R[t][k], sc, zr) * ir;
             }
         }
     }
-    if (a.lse && c.lane < c.g && c.lane < GP)
-        a.lse[(int64_t)b * a.Hq + (int64_t)hk * c.g + c.lane] = (c.m + __log2f(c.lsum)) / kLog2e;
+    if (a.lse && L.lane < a.g && L.lane < GP)
+        a.lse[(int64_t)b * a.Hq + (int64_t)hk * a.g + L.lane] = (c.mK + __log2f(c.lsum)) / kLog2e;
 }
 
 // Partial statistics of a segment: per query head m, l and the unnormalised acc[128].
 template <int GP>
-__device__ inline void write_piece(const SegCtx<GP> &c, float *pp) {
-    if (c.lane < c.g && c.lane < GP) {
-        pp[c.lane * kPieceStride + 0] = c.m;
-        pp[c.lane * kPieceStride + 1] = c.lsum;
+__device__ inline void write_piece(const DecodeArgs &a, const SegCtx<GP> &c, const LaneCtx<GP> &L,
+                                   const SegOut<GP> &s, float *pp) {
+    if (L.lane < a.g && L.lane < GP) {
+        pp[L.lane * kPieceStride + 0] = c.mK;
+        pp[L.lane * kPieceStride + 1] = c.lsum;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = row_head(c, i);
-        const float zr = __shfl(c.zsum, r < 0 ? 0 : r, 64);
-        if (r >= 0) {
+    for (int k = 0; k < SegOut<GP>::kK; ++k) {
+        const int hd = s.head[k];
+        const float zr = __shfl(c.zsum, hd < 0 ? 0 : hd, 64);
+        if (hd >= 0) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const float sc = (t & 1) ? 1048576.0f : 16777216.0f;
-                pp[r * kPieceStride + 4 + 16 * t + c.n] = c.O[t][i] * sc + zr;
+                pp[hd * kPieceStride + 4 + 16 * t + L.n] = fmaf(s.R[t][k], sc, zr);
             }
         }
     }
@@ -636,9 +870,9 @@ __device__ inline int64_t total_units(const DecodeArgs &a, int lane) {
 }
 
 template <int GP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void decode_split_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + kPgBytes];
     const int lane = threadIdx.x;
     const int64_t wid = blockIdx.x;
     const int64_t total = total_units(a, lane);
@@ -690,31 +924,66 @@ void decode_split_kernel(DecodeArgs a) {
     start.r = (int)(u_begin - pre0 - (int64_t)start.hk * start.rp.cost);
     start.u = u_begin;
 
+    const LaneCtx<GP> L = lane_ctx<GP>(lane);
     SegCtx<GP> c;
-    c.lane = lane;
-    c.G = lane >> 4;
-    c.n = lane & 15;
-    c.col = lane & 15;
-    c.g = a.g;
+    c.lsum = 0.0f;
+    c.zsum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) c.O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // per-lane source offsets of the direct-to-LDS loads (see issue_step)
-    const uint32_t offK4 = kSub4K + c.n * 64 + c.G * 16;
-    const uint32_t offV4 = kSub4V + lane * 16;
+    const uint32_t offK = L.n * 64 + L.G * 16;
+    const uint32_t offV = lane * 16;
     const uint32_t offP4 = ((lane & 8) ? kSub4VP : kSub4KP) + (lane & 3) * 16;
-    const uint32_t offK8 = kSub8K + c.n * 128 + c.G * 32;
-    const uint32_t offV8 = kSub8V + lane * 32;
-    const uint32_t offP8 = ((lane & 4) ? kSub8VP : kSub8KP) + (lane & 3) * 16;
+    const uint32_t offP8 = ((lane & 8) ? kSub8VP : kSub8KP) + (lane & 3) * 16;
 
     Cursor P = start, C = start;
     int issued = 0;
-    Lookup look = lookup(a, P);
+    // page half-batches in LDS: the half of unit hb + j is (hb / 32) & 1
+    uint32_t *pg = reinterpret_cast<uint32_t *>(smem + kStages * kStageBytes);
+    BatchCursor bc = {b0, pre0};
+    int64_t hb = u_begin;                     // first unit of the producer's current half
+    int hcur = 0;                             // its half index
+    fetch_pages(a, hb, u_end, bc, lane, pg);
+    if (hb + kPgHalf < u_end) fetch_pages(a, hb + kPgHalf, u_end, bc, lane, pg + 2 * kPgHalf);
+    __builtin_amdgcn_s_waitcnt(0);            // both halves landed (nothing else is in flight yet)
+    KVQ_FENCE();
+    // pages of the producer's next step (LDS reads; waited with the stage reads)
+    auto read_pages = [&](const Cursor &c) {
+        int j = (int)(c.u - hb);
+        int h = hcur;
+        if (j >= kPgHalf) {
+            j -= kPgHalf;
+            h ^= 1;
+        }
+        Lookup k;
+        k.pageA = (int)pg[(2 * h) * kPgHalf + j];
+        k.pageB = (int)pg[(2 * h + 1) * kPgHalf + j];
+        return k;
+    };
+    // after the producer leaves the current half, refill it with the units 64 ahead
+    auto advance_half = [&](const Cursor &c) {
+        if (c.u - hb >= kPgHalf) {
+            hb += kPgHalf;
+            if (hb + kPgHalf < u_end) fetch_pages(a, hb + kPgHalf, u_end, bc, lane, pg + 2 * hcur * kPgHalf);
+            hcur ^= 1;
+        }
+    };
+    auto uniform = [](const Lookup &k) {
+        Lookup u;
+        u.pageA = uni(k.pageA);
+        u.pageB = uni(k.pageB);
+        u.slot = u.pageA;
+        return u;
+    };
 #pragma unroll
     for (int s = 0; s < kStages; ++s) {
         if (P.u < u_end) {
-            issue_step(a, P, look, smem + s * kStageBytes, offK4, offV4, offP4, offK8, offV8, offP8, lane);
+            const Lookup look = uniform(read_pages(P));
+            issue_step(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
             cursor_next(a, P);
             ++issued;
-            if (P.u < u_end) look = lookup(a, P);
+            advance_half(P);
         }
     }
     bool open = false;
@@ -722,40 +991,38 @@ void decode_split_kernel(DecodeArgs a) {
         wait_vm_steps(issued - i - 1);
         uint8_t *st = smem + (i % kStages) * kStageBytes;
         const bool int4 = C.r < C.rp.n4;
-        const StepRegs r = read_stage(st, int4, lane);
+        const StepRegs<GP> r = read_stage<GP>(st, L);
+        Lookup look = {0, 0, 0};
+        if (P.u < u_end) look = read_pages(P);
         wait_lgkm0();
         if (P.u < u_end) {
-            issue_step(a, P, look, st, offK4, offV4, offP4, offK8, offV8, offP8, lane);
+            issue_step(a, P, uniform(look), st, offK, offV, offP4, offP8, lane);
             cursor_next(a, P);
             ++issued;
-            if (P.u < u_end) look = lookup(a, P);
+            advance_half(P);
         }
         if (!open) {
-            build_query<GP>(a, C.b, C.hk, c);
-            c.m = kNegInf;
-            c.lsum = 0.0f;
-            c.zsum = 0.0f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) c.O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            // a segment's first step finds mK = -inf and scales O, lsum and
+            // zsum (finite leftovers of the previous segment) by 0
+            build_query<GP>(a, C.b, C.hk, L, c);
+            c.mK = kNegInf;
             open = true;
         }
-        if (int4) {
-            const int pos0 = (C.rp.k0 + C.r) * 32;
-            if (pos0 >= C.rp.lo4 && pos0 + 32 <= C.rp.hi4)
-                compute_step4<GP, true>(c, r, pos0, C.rp.lo4, C.rp.hi4);
-            else
-                compute_step4<GP, false>(c, r, pos0, C.rp.lo4, C.rp.hi4);
-        } else {
-            compute_step8<GP>(c, r, 16 * (C.r - C.rp.n4), C.rp.n8e);
+        {
+            const int e0 = 16 * (C.r - C.rp.n4);
+            const int sbase = int4 ? (C.rp.k0 + C.r) * 32 : e0;
+            const int slo = int4 ? C.rp.lo4 : 0;
+            const int shi = int4 ? C.rp.hi4 : min(C.rp.n8e, e0 + 16);
+            compute_step<GP>(c, L, r, !int4, sbase, slo, shi);
         }
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) {
-            reduce_segment<GP>(c);
+            const SegOut<GP> so = reduce_segment<GP>(c, L, a.g);
             const int64_t c0 = C.u - C.r;
             const bool whole = worker_of(c0, total, W) == worker_of(c0 + C.rp.cost - 1, total, W);
             if (whole)
-                finalize_regs<GP>(a, c, C.b, C.hk);
+                finalize_regs<GP>(a, c, L, so, C.b, C.hk);
             else
-                write_piece<GP>(c, a.ws_piece + (wid + (int64_t)C.b * a.H + C.hk) * (int64_t)c.g * kPieceStride);
+                write_piece<GP>(a, c, L, so, a.ws_piece + (wid + (int64_t)C.b * a.H + C.hk) * (int64_t)a.g * kPieceStride);
             open = false;
         }
         cursor_next(a, C);
@@ -848,6 +1115,19 @@ hipError_t decode_max_workers(int g, int *out) {
     const void *fn = group_class(g) == 4 ? split_fn<4>() : (group_class(g) == 8 ? split_fn<8>() : split_fn<16>());
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
     if (e != hipSuccess) return e;
+    // The split kernel relies on every worker being resident at once (a worker
+    // that starts late finishes late).  Measured on MI355X, a workgroup's LDS
+    // is handed out in blocks larger than the occupancy query assumes (13.3 KB
+    // per workgroup admits 11, not 12, per CU), so bound the count by 160 KB of
+    // LDS per CU in 2 KB blocks as well.
+    hipFuncAttributes attr;
+    e = hipFuncGetAttributes(&attr, fn);
+    if (e != hipSuccess) return e;
+    const size_t lds = (attr.sharedSizeBytes + 2047) & ~(size_t)2047;
+    if (lds > 0) {
+        const int by_lds = (int)((160u * 1024u) / lds);
+        if (by_lds < per_cu) per_cu = by_lds;
+    }
     if (per_cu < 1) per_cu = 1;
     *out = cus * per_cu;
     return hipSuccess;

@@ -47,23 +47,34 @@ def decode_sub4(blocks: np.ndarray, tok) -> dict:
     return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])
 
 
+def _nibbles_k(blocks, rows, base, e):
+    raw = blocks[rows, base + 64 * e[:, None] + np.arange(64)[None, :]]
+    out = np.empty((raw.shape[0], 128), np.uint8)
+    out[:, 0::2] = raw & 0x0F
+    out[:, 1::2] = raw >> 4
+    return out
+
+
+def _nibbles_v(blocks, rows, base, e):
+    G, r = e // 4, e % 4
+    n = np.arange(16)
+    out = np.empty((e.shape[0], 128), np.uint8)
+    for c in range(4):
+        byte = blocks[rows, base + 4 * ((G[:, None] * 16 + n[None, :]) * 4 + c) + r[:, None]]
+        out[:, 32 * c + n] = byte & 0x0F
+        out[:, 32 * c + 16 + n] = byte >> 4
+    return out
+
+
 def decode_sub8(blocks: np.ndarray, ent) -> dict:
-    """Codes and fp16 params of entry `ent` (0..15) of each INT8 subblock [N, 4224]."""
+    """Codes and fp16 params of entry `ent` (0..15) of each INT8 subblock [N, 4224]
+    (codes stored as a low-nibble and a high-nibble plane)."""
     blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, SUB8_BYTES)
     e = np.asarray(ent, dtype=np.int64).reshape(-1)
     N = blocks.shape[0]
     rows = np.arange(N)[:, None]
-    raw = blocks[rows, 128 * e[:, None] + np.arange(128)[None, :]]
-    kc = np.empty((N, 128), np.uint8)
-    for j in range(16):             # 8-dim groups stored even dims first
-        kc[:, 8 * j + 0:8 * j + 8:2] = raw[:, 8 * j:8 * j + 4]
-        kc[:, 8 * j + 1:8 * j + 8:2] = raw[:, 8 * j + 4:8 * j + 8]
-    G, r = e // 4, e % 4
-    n = np.arange(16)
-    vc = np.empty((N, 128), np.uint8)
-    for c in range(8):
-        off = 2048 + 4 * ((G[:, None] * 16 + n[None, :]) * 8 + c) + r[:, None]
-        vc[:, 16 * c + n] = blocks[rows, off]
+    kc = _nibbles_k(blocks, rows, 0, e) | (_nibbles_k(blocks, rows, 1024, e) << 4)
+    vc = _nibbles_v(blocks, rows, 2048, e) | (_nibbles_v(blocks, rows, 3072, e) << 4)
     kp = blocks[rows, 4096 + 4 * e[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
     vp = blocks[rows, 4160 + 4 * e[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
     return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])

@@ -76,14 +76,16 @@
  *   Each (slot, kv_head) owns NR = ceil((s + w) / 16) subblocks of 16 ring
  *   entries; subblock j starts at byte
  *       ((slot * num_kv_heads + kv_head) * NR + j) * 4224
- *   and holds entries e = 0..15 (ring entry 16 j + e):
- *     [   0, 2048) key codes, entry-major, each group of 8 rotated dims
- *                  8j..8j+7 stored even dims first: byte 128 e + 8 j + i holds
- *                  dim 8j + 2i and byte 128 e + 8 j + 4 + i dim 8j + 2i + 1
- *                  (i = 0..3);
- *     [2048, 4096) value codes, entry-fastest: with G = e / 4, r = e % 4,
- *                  byte 4 * ((G * 16 + n) * 8 + c) + r = code of value dim
- *                  16 c + n, for n = 0..15, c = 0..7;
+ *   and holds entries e = 0..15 (ring entry 16 j + e).  Each 8-bit code c is
+ *   split into its low nibble c & 15 and high nibble c >> 4, and each nibble
+ *   plane is laid out like the codes of an INT4 subblock:
+ *     [   0, 1024) key low nibbles:  byte 64 e + i holds rotated dims 2i (low
+ *                  nibble of the byte) and 2i + 1 (high nibble of the byte);
+ *     [1024, 2048) key high nibbles, same arrangement;
+ *     [2048, 3072) value low nibbles: with G = e / 4 and r = e % 4, byte
+ *                  4 * ((G * 16 + n) * 4 + c) + r holds value dims 32 c + n
+ *                  (low nibble of the byte) and 32 c + 16 + n (high nibble);
+ *     [3072, 4096) value high nibbles, same arrangement;
  *     [4096, 4160) key   (scale, zero) fp16 pairs, 4 bytes per entry;
  *     [4160, 4224) value (scale, zero) fp16 pairs, 4 bytes per entry.
  *
