@@ -77,6 +77,38 @@ __host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_
     return w < max_workers ? w : max_workers;
 }
 
+// Two-phase split of the units: workers [0, w1) share units [0, u1) evenly and
+// workers [w1, w1 + w2) share [u1, total).  With fewer units than all
+// w1max + w2max workers can take, one even split over the workers needed.
+struct Partition {
+    int64_t total, u1, w1, w2;
+};
+
+__host__ __device__ inline Partition make_partition(int64_t total, int64_t w1max, int64_t w2max, int64_t share_q16,
+                                                    int64_t min_units) {
+    Partition p;
+    p.total = total;
+    p.w1 = effective_workers(total, w1max + w2max, min_units);
+    p.u1 = total;
+    p.w2 = 0;
+    if (w1max > 0 && w2max > 0 && p.w1 == w1max + w2max) {
+        p.w1 = w1max;
+        p.u1 = (total * share_q16) >> 16;
+        p.w2 = w2max;
+    }
+    return p;
+}
+
+__host__ __device__ inline int64_t part_begin(const Partition &p, int64_t w) {
+    if (w <= p.w1) return worker_begin(w, p.u1, p.w1);
+    return p.u1 + worker_begin(w - p.w1, p.total - p.u1, p.w2);
+}
+
+__host__ __device__ inline int64_t part_of(const Partition &p, int64_t u) {
+    if (u < p.u1) return worker_of(u, p.u1, p.w1);
+    return p.w1 + worker_of(u - p.u1, p.total - p.u1, p.w2);
+}
+
 struct AppendArgs {
     const uint16_t *k;
     const uint16_t *v;
@@ -104,8 +136,10 @@ struct DecodeArgs {
     const uint8_t *int8_pool;
     int32_t H, P, logP, h, s, w, nr8;
     float inv_sqrt_h;
-    int32_t max_workers, min_units;
-    int64_t *ws_header;     // [0] total units, [1] effective workers
+    int32_t max_workers, min_units;     // first-phase workers
+    int32_t extra_workers;              // second-phase workers
+    int32_t share_q16;                  // fraction of the units in the first phase, x 2^16
+    int64_t *ws_header;     // [0] total units, [1] u1, [2] w1, [3] w2 (the Partition)
     int64_t *ws_prefix;     // [B] exclusive prefix of per-row units (all KV heads)
     float *ws_piece;        // [max_workers + B*H][g][kPieceStride] per-worker pieces
     float *out;

@@ -318,14 +318,49 @@ struct Cursor {
     int64_t u;          // global unit
 };
 
-__device__ inline void cursor_next(const DecodeArgs &a, Cursor &c) {
+// ---------------------------------------------------------------------------
+// Row table.  The lengths and slots of rows [0, kResRows) stay in VGPRs for the
+// whole kernel (lane l holds rows l + 64 k), so the wave-uniform row walks read
+// them with v_readlane instead of a memory round trip; rows beyond are read
+// from memory.
+constexpr int kResRows = 256;
+
+struct RowRegs {
+    int L[4], S[4];
+};
+
+__device__ inline RowRegs load_rows(const DecodeArgs &a, int lane) {
+    RowRegs R;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = lane + 64 * k;
+        R.L[k] = b < a.B ? a.ctx_len[b] : 0;
+        R.S[k] = b < a.B ? a.slot[b] : 0;
+    }
+    return R;
+}
+
+__device__ inline int pick4(const int (&v)[4], int k) {
+    return k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
+}
+// ctx_len and slot of the wave-uniform row b
+__device__ inline int row_len(const DecodeArgs &a, const RowRegs &R, int b) {
+    if (b < kResRows) return __builtin_amdgcn_readlane(pick4(R.L, b >> 6), b & 63);
+    return ldc(a.ctx_len, b);
+}
+__device__ inline int row_slot(const DecodeArgs &a, const RowRegs &R, int b) {
+    if (b < kResRows) return __builtin_amdgcn_readlane(pick4(R.S, b >> 6), b & 63);
+    return ldc(a.slot, b);
+}
+
+__device__ inline void cursor_next(const DecodeArgs &a, const RowRegs &R, Cursor &c) {
     ++c.u;
     if (++c.r < c.rp.cost) return;
     c.r = 0;
     if (++c.hk < a.H) return;
     c.hk = 0;
     for (++c.b; c.b < a.B; ++c.b) {
-        c.rp = row_plan(ldc(a.ctx_len, c.b), a.s, a.w);
+        c.rp = row_plan(row_len(a, R, c.b), a.s, a.w);
         if (c.rp.cost > 0) return;
     }
 }
@@ -346,8 +381,8 @@ struct BatchCursor {
     int64_t pre;
 };
 
-__device__ inline void fetch_pages(const DecodeArgs &a, int64_t hb, int64_t u_end, BatchCursor &bc, int lane,
-                                   uint32_t *pg_half) {
+__device__ inline void fetch_pages(const DecodeArgs &a, const RowRegs &R, int64_t hb, int64_t u_end,
+                                   BatchCursor &bc, int lane, uint32_t *pg_half) {
     const int64_t u = hb + (lane & (kPgHalf - 1));
     const int64_t lim = min(hb + kPgHalf, u_end);
     int myL = 0, myslot = 0;
@@ -356,10 +391,10 @@ __device__ inline void fetch_pages(const DecodeArgs &a, int64_t hb, int64_t u_en
     int b = bc.b;
     int64_t pre = bc.pre;
     while (b < a.B) {
-        const int L = ldc(a.ctx_len, b);
+        const int L = row_len(a, R, b);
         const int64_t rowu = (int64_t)row_plan(L, a.s, a.w).cost * a.H;
         if (pre + rowu > hb && rowu > 0) {
-            const int sl = ldc(a.slot, b);
+            const int sl = row_slot(a, R, b);
             if (u >= pre && u < pre + rowu) {
                 mine = true;
                 mypre = pre;
@@ -410,16 +445,44 @@ struct Lookup {
 // Hadamard strides below kVPL stay inside the lane, a stride s at or above it
 // pairs lanes l and l ^ (s / 2).  The B operand of chunk i (dims 32 G + 8 i ..)
 // for column c is then gathered from the lane of part i / (kVPL / 8).
+// The bf16 query values of lane (G, c) -- head c % GP, dims 32 G + kVPL (c / GP)
+// .. + kVPL -- are copied into LDS by the producer together with the first step
+// of the segment (kVPL / 8 direct loads of 16 bytes per lane), so no load into
+// registers is in flight across steps.  Lanes of heads past g copy head 0.
 template <int GP>
-__device__ inline void build_query(const DecodeArgs &a, int b, int hk, const LaneCtx<GP> &L, SegCtx<GP> &c) {
+struct QRing {
+    static constexpr int kLoads = GC<GP>::kVPL / 8;     // 16-byte loads per lane
+    static constexpr int kBytes = kLoads * 1024;        // bytes per slot
+    u32x4 w[kLoads];
+};
+
+template <int GP>
+__device__ inline void issue_query(const DecodeArgs &a, int b, int hk, const LaneCtx<GP> &L, uint8_t *slot) {
+    constexpr int V = GC<GP>::kVPL;
+    const int head = L.head < a.g ? L.head : 0;
+    const uint16_t *qp = a.q + ((int64_t)b * a.Hq + (int64_t)hk * a.g + head) * kHeadDim + 32 * L.G + V * L.part;
+#pragma unroll
+    for (int v = 0; v < QRing<GP>::kLoads; ++v)
+        __builtin_amdgcn_global_load_lds(qp + 8 * v, (lds_ptr)(slot + 1024 * v), 16, 0, 0);
+}
+
+template <int GP>
+__device__ inline QRing<GP> read_query(const uint8_t *slot, int lane) {
+    QRing<GP> q;
+#pragma unroll
+    for (int v = 0; v < QRing<GP>::kLoads; ++v) q.w[v] = *reinterpret_cast<const u32x4 *>(slot + 1024 * v + 16 * lane);
+    return q;
+}
+
+template <int GP>
+__device__ inline void build_query(const DecodeArgs &a, const QRing<GP> &qr, const LaneCtx<GP> &L, SegCtx<GP> &c) {
     constexpr int V = GC<GP>::kVPL;
     constexpr int CPL = V / 8;            // chunks of 8 dims per lane (= kNP)
     float x[V];
     if (L.head < a.g) {
-        const uint16_t *qp = a.q + ((int64_t)b * a.Hq + (int64_t)hk * a.g + L.head) * kHeadDim + 32 * L.G + V * L.part;
 #pragma unroll
         for (int v = 0; v < V / 8; ++v) {
-            const u32x4 w = ldg<u32x4>(qp + 8 * v);
+            const u32x4 w = qr.w[v];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 x[8 * v + 2 * e] = bf16f(w[e] & 0xFFFFu);
@@ -860,58 +923,140 @@ __device__ inline void write_piece(const DecodeArgs &a, const SegCtx<GP> &c, con
     }
 }
 
-// Units of all rows: each wave sums the per-row costs (all KV heads).
-__device__ inline int64_t total_units(const DecodeArgs &a, int lane) {
-    int64_t tot = 0;
-    for (int b = lane; b < a.B; b += 64) tot += (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H;
+// LDS of one wave: the stage ring, the page half-batches and the query ring
+// (one slot per stage).  The request is padded to 1/kWavesPerCU of a CU's
+// 160 KB: random 2 KB reads from more waves per CU lose HBM efficiency
+// (measured on MI355X: 8 waves per CU stream random 2176-byte subblocks ~25%
+// faster than 12).
+constexpr int kWavesPerCU = 8;
+
+template <int GP>
+struct SmemLayout {
+    static constexpr int kPages = kStages * kStageBytes;
+    static constexpr int kQ = kPages + kPgBytes;
+    static constexpr int kNeed = kQ + kStages * QRing<GP>::kBytes;
+    static constexpr int kPad = 160 * 1024 / kWavesPerCU;
+    static constexpr int kRequest = kNeed > kPad ? kNeed : kPad;
+};
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ inline int64_t wave_scan(int64_t x, int lane) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
-    return uni64(tot);
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t t = __shfl_up(x, o, 64);
+        if (lane >= o) x += t;
+    }
+    return x;
+}
+
+// Inclusive prefix sum over the 64 lanes in 32 bits with DPP moves: shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then the total of row 0 (2) is added to
+// row 1 (3) and that of rows 0-1 to rows 2-3.
+__device__ inline uint32_t wave_scan32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
+
+__device__ inline int64_t readlane64(int64_t x, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)x >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 template <int GP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + kPgBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SmemLayout<GP>::kRequest];
     const int lane = threadIdx.x;
     const int64_t wid = blockIdx.x;
-    const int64_t total = total_units(a, lane);
-    const int64_t W = effective_workers(total, a.max_workers, a.min_units);
-    if (wid == 0 && lane == 0) {
-        a.ws_header[0] = total;
-        a.ws_header[1] = W;
+
+    // Exclusive prefix of the row costs (units of all KV heads of a row).  The
+    // rows of the register table take one load round trip and four
+    // independent lane scans; rows beyond it are summed from memory.
+    const RowRegs R = load_rows(a, lane);
+    int64_t cost[4], excl[4];
+    int64_t res_total = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cost[k] = lane + 64 * k < a.B ? (int64_t)row_plan(R.L[k], a.s, a.w).cost * a.H : 0;
+    // 32-bit DPP scans when 256 row costs cannot reach 2^31 (every realistic
+    // batch), 64-bit shuffle scans otherwise
+    const bool small = !__any(cost[0] >= (1 << 22) || cost[1] >= (1 << 22) || cost[2] >= (1 << 22) ||
+                              cost[3] >= (1 << 22));
+    if (small) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t inc = wave_scan32((uint32_t)cost[k]);
+            excl[k] = res_total + (int64_t)(inc - (uint32_t)cost[k]);
+            res_total += (int64_t)(uint32_t)__builtin_amdgcn_readlane(inc, 63);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t inc = wave_scan(cost[k], lane);
+            excl[k] = res_total + inc - cost[k];
+            res_total += readlane64(inc, 63);
+        }
     }
-    const int64_t u_begin = wid < W ? worker_begin(wid, total, W) : 0;
-    const int64_t u_end = wid < W ? worker_begin(wid + 1, total, W) : 0;
+    int64_t total = res_total;
+    if (a.B > kResRows) {
+        int64_t rest = 0;
+        for (int b = kResRows + lane; b < a.B; b += 64) rest += (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) rest += __shfl_xor(rest, o, 64);
+        total += uni64(rest);
+    }
+    const Partition part = make_partition(total, a.max_workers, a.extra_workers, a.share_q16, a.min_units);
+    const int64_t W = part.w1 + part.w2;
+    if (wid == 0 && lane == 0) {
+        a.ws_header[0] = part.total;
+        a.ws_header[1] = part.u1;
+        a.ws_header[2] = part.w1;
+        a.ws_header[3] = part.w2;
+    }
+    const int64_t u_begin = wid < W ? part_begin(part, wid) : 0;
+    const int64_t u_end = wid < W ? part_begin(part, wid + 1) : 0;
     const bool active = wid < W && u_begin < u_end;
     if (!active && wid != 0) return;
 
-    // Exclusive prefix of row costs; block 0 stores all of it for the combine
-    // kernel, every active wave finds the row holding its first unit.
+    // Block 0 stores the prefix for the combine kernel; every active wave finds
+    // the row holding its first unit.
     int b0 = -1;
     int64_t pre0 = 0;
-    int64_t base = 0;
-    for (int cb = 0; cb < a.B; cb += 64) {
-        const int b = cb + lane;
-        const int64_t cost = b < a.B ? (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H : 0;
-        int64_t incl = cost;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int64_t t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
+    for (int k = 0; k < 4; ++k) {
+        const int b = lane + 64 * k;
+        if (wid == 0 && b < a.B) a.ws_prefix[b] = excl[k];
+        const uint64_t mk = __ballot(active && cost[k] > 0 && excl[k] <= u_begin && u_begin < excl[k] + cost[k]);
+        if (mk) {
+            const int src = uni(__ffsll((unsigned long long)mk) - 1);
+            b0 = 64 * k + src;
+            pre0 = readlane64(excl[k], src);
         }
-        const int64_t excl = base + incl - cost;
-        if (wid == 0 && b < a.B) a.ws_prefix[b] = excl;
-        if (active && b0 < 0) {
-            const uint64_t mk = __ballot(b < a.B && cost > 0 && excl <= u_begin && u_begin < excl + cost);
-            if (mk) {
-                const int src = uni(__ffsll((unsigned long long)mk) - 1);
-                b0 = uni(cb + src);
-                pre0 = uni64(__shfl(excl, src, 64));
-                if (wid != 0) break;
+    }
+    if (a.B > kResRows && (wid == 0 || b0 < 0)) {
+        int64_t base = res_total;
+        for (int cb = kResRows; cb < a.B; cb += 64) {
+            const int b = cb + lane;
+            const int64_t c = b < a.B ? (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H : 0;
+            const int64_t incl = wave_scan(c, lane);
+            const int64_t ex = base + incl - c;
+            if (wid == 0 && b < a.B) a.ws_prefix[b] = ex;
+            if (active && b0 < 0) {
+                const uint64_t mk = __ballot(b < a.B && c > 0 && ex <= u_begin && u_begin < ex + c);
+                if (mk) {
+                    const int src = uni(__ffsll((unsigned long long)mk) - 1);
+                    b0 = uni(cb + src);
+                    pre0 = readlane64(ex, src);
+                    if (wid != 0) break;
+                }
             }
+            base = uni64(base + readlane64(incl, 63));
         }
-        base = uni64(base + __shfl(incl, 63, 64));
     }
     if (!active) return;
     b0 = uni(b0);
@@ -919,7 +1064,7 @@ void decode_split_kernel(DecodeArgs a) {
 
     Cursor start;
     start.b = b0;
-    start.rp = row_plan(ldc(a.ctx_len, b0), a.s, a.w);
+    start.rp = row_plan(row_len(a, R, b0), a.s, a.w);
     start.hk = (int)((u_begin - pre0) / start.rp.cost);
     start.r = (int)(u_begin - pre0 - (int64_t)start.hk * start.rp.cost);
     start.u = u_begin;
@@ -940,12 +1085,13 @@ void decode_split_kernel(DecodeArgs a) {
     Cursor P = start, C = start;
     int issued = 0;
     // page half-batches in LDS: the half of unit hb + j is (hb / 32) & 1
-    uint32_t *pg = reinterpret_cast<uint32_t *>(smem + kStages * kStageBytes);
+    uint32_t *pg = reinterpret_cast<uint32_t *>(smem + SmemLayout<GP>::kPages);
+    uint8_t *qring = smem + SmemLayout<GP>::kQ;
     BatchCursor bc = {b0, pre0};
     int64_t hb = u_begin;                     // first unit of the producer's current half
     int hcur = 0;                             // its half index
-    fetch_pages(a, hb, u_end, bc, lane, pg);
-    if (hb + kPgHalf < u_end) fetch_pages(a, hb + kPgHalf, u_end, bc, lane, pg + 2 * kPgHalf);
+    fetch_pages(a, R, hb, u_end, bc, lane, pg);
+    if (hb + kPgHalf < u_end) fetch_pages(a, R, hb + kPgHalf, u_end, bc, lane, pg + 2 * kPgHalf);
     __builtin_amdgcn_s_waitcnt(0);            // both halves landed (nothing else is in flight yet)
     KVQ_FENCE();
     // pages of the producer's next step (LDS reads; waited with the stage reads)
@@ -965,7 +1111,7 @@ void decode_split_kernel(DecodeArgs a) {
     auto advance_half = [&](const Cursor &c) {
         if (c.u - hb >= kPgHalf) {
             hb += kPgHalf;
-            if (hb + kPgHalf < u_end) fetch_pages(a, hb + kPgHalf, u_end, bc, lane, pg + 2 * hcur * kPgHalf);
+            if (hb + kPgHalf < u_end) fetch_pages(a, R, hb + kPgHalf, u_end, bc, lane, pg + 2 * hcur * kPgHalf);
             hcur ^= 1;
         }
     };
@@ -980,31 +1126,37 @@ void decode_split_kernel(DecodeArgs a) {
     for (int s = 0; s < kStages; ++s) {
         if (P.u < u_end) {
             const Lookup look = uniform(read_pages(P));
+            if (P.r == 0 || P.u == u_begin) issue_query<GP>(a, P.b, P.hk, L, qring + s * QRing<GP>::kBytes);
             issue_step(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
-            cursor_next(a, P);
+            cursor_next(a, R, P);
             ++issued;
             advance_half(P);
         }
     }
     bool open = false;
     for (int i = 0; C.u < u_end; ++i) {
+        // (a query copy issued with a later step only makes this wait stricter)
         wait_vm_steps(issued - i - 1);
         uint8_t *st = smem + (i % kStages) * kStageBytes;
+        uint8_t *qs = qring + (i % kStages) * QRing<GP>::kBytes;
         const bool int4 = C.r < C.rp.n4;
         const StepRegs<GP> r = read_stage<GP>(st, L);
+        QRing<GP> qr;
+        if (!open) qr = read_query<GP>(qs, lane);
         Lookup look = {0, 0, 0};
         if (P.u < u_end) look = read_pages(P);
         wait_lgkm0();
         if (P.u < u_end) {
+            if (P.r == 0 || P.u == u_begin) issue_query<GP>(a, P.b, P.hk, L, qs);
             issue_step(a, P, uniform(look), st, offK, offV, offP4, offP8, lane);
-            cursor_next(a, P);
+            cursor_next(a, R, P);
             ++issued;
             advance_half(P);
         }
         if (!open) {
             // a segment's first step finds mK = -inf and scales O, lsum and
             // zsum (finite leftovers of the previous segment) by 0
-            build_query<GP>(a, C.b, C.hk, L, c);
+            build_query<GP>(a, qr, L, c);
             c.mK = kNegInf;
             open = true;
         }
@@ -1017,73 +1169,108 @@ void decode_split_kernel(DecodeArgs a) {
         }
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) {
             const SegOut<GP> so = reduce_segment<GP>(c, L, a.g);
-            const int64_t c0 = C.u - C.r;
-            const bool whole = worker_of(c0, total, W) == worker_of(c0 + C.rp.cost - 1, total, W);
+            // this wave covers [u_begin, u_end) in order: it holds the whole
+            // segment iff it has just done the segment's last unit and also did its first
+            const bool whole = C.r == C.rp.cost - 1 && C.u - C.r >= u_begin;
             if (whole)
                 finalize_regs<GP>(a, c, L, so, C.b, C.hk);
             else
                 write_piece<GP>(a, c, L, so, a.ws_piece + (wid + (int64_t)C.b * a.H + C.hk) * (int64_t)a.g * kPieceStride);
             open = false;
         }
-        cursor_next(a, C);
+        cursor_next(a, R, C);
     }
 }
 
 // Log-sum-exp combine of the pieces of one (row, KV head) segment that several
 // workers share; one wave per segment, lane l handles query head 4k + l/16 and
-// dims 8 (l % 16) .. +8.  Also writes the rows with no context.
+// dims 8 (l % 16) .. +8.  Also writes the rows with no context.  The pieces are
+// read kCombBatch at a time with all their loads in flight together, and the
+// running (max, sum, acc) is rescaled once per batch.
+constexpr int kCombBatch = 4;
+
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int64_t seg = blockIdx.x;
     const int b = (int)(seg / a.H), hk = (int)(seg % a.H);
-    const RowPlan rp = row_plan(a.ctx_len[b], a.s, a.w);
     const int g = a.g;
     const int part = lane & 15;
+    // independent scalar loads, one round trip
+    const int Lb = ldc(a.ctx_len, b);
+    Partition pt;
+    pt.total = a.ws_header[0];
+    pt.u1 = a.ws_header[1];
+    pt.w1 = a.ws_header[2];
+    pt.w2 = a.ws_header[3];
+    const int64_t prefix = a.ws_prefix[b];
+    const RowPlan rp = row_plan(Lb, a.s, a.w);
     if (rp.cost == 0) {
         for (int i = lane; i < g * kHeadDim; i += 64) a.out[((int64_t)b * a.Hq + (int64_t)hk * g) * kHeadDim + i] = 0.0f;
         if (a.lse && lane < g) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + lane] = kNegInf;
         return;
     }
-    const int64_t total = a.ws_header[0];
-    const int64_t W = a.ws_header[1];
-    const int64_t c0 = a.ws_prefix[b] + (int64_t)hk * rp.cost;
-    const int64_t wf = worker_of(c0, total, W);
-    const int64_t wl = worker_of(c0 + rp.cost - 1, total, W);
+    const int64_t c0 = prefix + (int64_t)hk * rp.cost;
+    const int64_t wf = part_of(pt, c0);
+    const int64_t wl = part_of(pt, c0 + rp.cost - 1);
     if (wf == wl) return;           // finished by its only worker
     const float *basep = a.ws_piece + seg * (int64_t)g * kPieceStride;
     for (int hg = 0; hg < g; hg += 4) {
         const int j = hg + (lane >> 4);
-        if (j >= g) continue;
-        float M = kNegInf;
-        for (int64_t w = wf; w <= wl; ++w) M = fmaxf(M, basep[(w * g + j) * kPieceStride]);
-        float Ls = 0.0f;
+        const bool on = j < g;
+        float M = kNegInf, Ls = 0.0f;
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-        for (int64_t w = wf; w <= wl; ++w) {
-            const float *pp = basep + (w * g + j) * kPieceStride;
-            const float m = pp[0];
-            const float f = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-            Ls = fmaf(pp[1], f, Ls);
-            const u32x4 v0 = ldg<u32x4>(pp + 4 + 8 * part);
-            const u32x4 v1 = ldg<u32x4>(pp + 8 + 8 * part);
+        for (int64_t w0 = wf; w0 <= wl; w0 += kCombBatch) {
+            float m[kCombBatch], l[kCombBatch];
+            u32x4 v0[kCombBatch], v1[kCombBatch];
+#pragma unroll
+            for (int k = 0; k < kCombBatch; ++k) {
+                const float *pp = basep + ((w0 + k) * g + (on ? j : 0)) * kPieceStride;
+                if (w0 + k <= wl) {
+                    m[k] = pp[0];
+                    l[k] = pp[1];
+                    v0[k] = ldg<u32x4>(pp + 4 + 8 * part);
+                    v1[k] = ldg<u32x4>(pp + 8 + 8 * part);
+                } else {
+                    m[k] = kNegInf;
+                    l[k] = 0.0f;
+                    v0[k] = u32x4{0u, 0u, 0u, 0u};
+                    v1[k] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            float Mn = M;
+#pragma unroll
+            for (int k = 0; k < kCombBatch; ++k) Mn = fmaxf(Mn, m[k]);
+            const float fr = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+            Ls *= fr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= fr;
+#pragma unroll
+            for (int k = 0; k < kCombBatch; ++k) {
+                const float f = m[k] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m[k] - Mn);
+                Ls = fmaf(l[k], f, Ls);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[e] = fmaf(__uint_as_float(v0[k][e]), f, acc[e]);
+                    acc[4 + e] = fmaf(__uint_as_float(v1[k][e]), f, acc[4 + e]);
+                }
+            }
+            M = Mn;
+        }
+        if (on) {
+            float *o = a.out + ((int64_t)b * a.Hq + (int64_t)hk * g + j) * kHeadDim + 8 * part;
+            const float inv = 1.0f / Ls;
+            u32x4 w0, w1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[e] = fmaf(__uint_as_float(v0[e]), f, acc[e]);
-                acc[4 + e] = fmaf(__uint_as_float(v1[e]), f, acc[4 + e]);
+                w0[e] = __float_as_uint(acc[e] * inv);
+                w1[e] = __float_as_uint(acc[4 + e] * inv);
             }
+            *reinterpret_cast<u32x4 *>(o) = w0;
+            *reinterpret_cast<u32x4 *>(o + 4) = w1;
+            if (a.lse && part == 0) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + j] = (M + __log2f(Ls)) / kLog2e;
         }
-        float *o = a.out + ((int64_t)b * a.Hq + (int64_t)hk * g + j) * kHeadDim + 8 * part;
-        const float inv = 1.0f / Ls;
-        u32x4 w0, w1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            w0[e] = __float_as_uint(acc[e] * inv);
-            w1[e] = __float_as_uint(acc[4 + e] * inv);
-        }
-        *reinterpret_cast<u32x4 *>(o) = w0;
-        *reinterpret_cast<u32x4 *>(o + 4) = w1;
-        if (a.lse && part == 0) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + j] = (M + __log2f(Ls)) / kLog2e;
     }
 }
 
