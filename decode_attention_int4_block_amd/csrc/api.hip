@@ -31,9 +31,10 @@ kvq_status ok() {
 constexpr int kMinUnitsPerWorker = 8;
 // Work split over the resident waves (two per SIMD).  The SIMD's issue
 // arbitration favours the wave dispatched first -- workgroups [0, W/2) -- which
-// streams ~18% faster than the later one (measured on MI355X), so the first
-// half of the workers gets kFirstShareQ16 / 2^16 of the units.
-constexpr int kFirstShareQ16 = 36700;   // 0.56
+// streams ~27% faster than the later one (measured on MI355X); a parity split
+// by XCD measured no better.  Weights: {first half, even w}, {first, odd},
+// {second, even}, {second, odd}.
+constexpr int32_t kPartWeights[4] = {128, 128, 100, 100};
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_max_workers[kMaxDevices][3];   // per group class g <= 4, <= 8, <= 16
 
@@ -76,13 +77,15 @@ kvq_status max_workers(int g, int *out) {
 }
 
 struct WsLayout {
-    size_t prefix_off, piece_off, total;
+    size_t first_off, last_off, piece_off, total;
 };
 
 WsLayout ws_layout(const kvq_cache *c, int B, int g, int workers) {
     WsLayout l;
-    l.prefix_off = kvq::kWsHeaderBytes;
-    l.piece_off = align256(l.prefix_off + (size_t)B * sizeof(int64_t));
+    const size_t segs = (size_t)B * c->num_kv_heads;
+    l.first_off = 0;
+    l.last_off = align256(segs * sizeof(int32_t));
+    l.piece_off = align256(l.last_off + segs * sizeof(int32_t));
     const size_t pieces = (size_t)workers + (size_t)B * c->num_kv_heads;
     l.total = align256(l.piece_off + pieces * g * kvq::kPieceStride * sizeof(float));
     return l;
@@ -195,12 +198,11 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     a.w = c->recent;
     a.nr8 = nr8_of(c);
     a.inv_sqrt_h = inv_sqrt(c->had_block);
-    a.max_workers = workers / 2;
+    a.max_workers = workers;
     a.min_units = kMinUnitsPerWorker;
-    a.extra_workers = workers - workers / 2;
-    a.share_q16 = kFirstShareQ16;
-    a.ws_header = reinterpret_cast<int64_t *>(ws);
-    a.ws_prefix = reinterpret_cast<int64_t *>(ws + l.prefix_off);
+    for (int i = 0; i < 4; ++i) a.part_wt[i] = kPartWeights[i];
+    a.ws_first = reinterpret_cast<int32_t *>(ws + l.first_off);
+    a.ws_last = reinterpret_cast<int32_t *>(ws + l.last_off);
     a.ws_piece = reinterpret_cast<float *>(ws + l.piece_off);
     a.out = out;
     a.lse = lse;

@@ -77,36 +77,59 @@ __host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_
     return w < max_workers ? w : max_workers;
 }
 
-// Two-phase split of the units: workers [0, w1) share units [0, u1) evenly and
-// workers [w1, w1 + w2) share [u1, total).  With fewer units than all
-// w1max + w2max workers can take, one even split over the workers needed.
+// Weighted split of the units over W workers: worker w takes a share in
+// proportion to wt[2 r + (w & 1)], where r = (w >= W / 2), so that waves of
+// different measured speed finish together.  With fewer units than W full
+// workers need, an even split over the workers needed.
 struct Partition {
-    int64_t total, u1, w1, w2;
+    int64_t total, W, half;
+    int64_t wt[4];
+    int64_t csum;           // cumulative weight of all W workers
 };
 
-__host__ __device__ inline Partition make_partition(int64_t total, int64_t w1max, int64_t w2max, int64_t share_q16,
+__host__ __device__ inline int64_t count_even(int64_t a, int64_t b) { return (b + 1) / 2 - (a + 1) / 2; }
+
+// Cumulative weight of the workers [0, w).
+__host__ __device__ inline int64_t part_cum(const Partition &p, int64_t w) {
+    const int64_t w0 = w < p.half ? w : p.half;
+    const int64_t e0 = count_even(0, w0);
+    int64_t c = e0 * p.wt[0] + (w0 - e0) * p.wt[1];
+    if (w > p.half) {
+        const int64_t e1 = count_even(p.half, w);
+        c += e1 * p.wt[2] + (w - p.half - e1) * p.wt[3];
+    }
+    return c;
+}
+
+__host__ __device__ inline Partition make_partition(int64_t total, int64_t max_workers, const int32_t *wt,
                                                     int64_t min_units) {
     Partition p;
     p.total = total;
-    p.w1 = effective_workers(total, w1max + w2max, min_units);
-    p.u1 = total;
-    p.w2 = 0;
-    if (w1max > 0 && w2max > 0 && p.w1 == w1max + w2max) {
-        p.w1 = w1max;
-        p.u1 = (total * share_q16) >> 16;
-        p.w2 = w2max;
-    }
+    p.W = effective_workers(total, max_workers, min_units);
+    p.half = p.W / 2;
+    const bool weighted = p.W == max_workers && p.W >= 2;
+    for (int i = 0; i < 4; ++i) p.wt[i] = weighted ? wt[i] : 1;
+    p.csum = part_cum(p, p.W);
     return p;
 }
 
+// First unit of worker w (w <= W).
 __host__ __device__ inline int64_t part_begin(const Partition &p, int64_t w) {
-    if (w <= p.w1) return worker_begin(w, p.u1, p.w1);
-    return p.u1 + worker_begin(w - p.w1, p.total - p.u1, p.w2);
+    return p.total * part_cum(p, w) / p.csum;
 }
 
+// The worker whose unit range contains unit u (u < total); workers with empty
+// ranges are never returned.
 __host__ __device__ inline int64_t part_of(const Partition &p, int64_t u) {
-    if (u < p.u1) return worker_of(u, p.u1, p.w1);
-    return p.w1 + worker_of(u - p.u1, p.total - p.u1, p.w2);
+    // invert the cumulative weight, then correct the rounding
+    const int64_t c = u * p.csum / p.total;
+    const int64_t ch = part_cum(p, p.half);
+    int64_t w = c < ch ? 2 * c / (p.wt[0] + p.wt[1]) : p.half + 2 * (c - ch) / (p.wt[2] + p.wt[3]);
+    if (w > p.W - 1) w = p.W - 1;
+    if (w < 0) w = 0;
+    while (w > 0 && part_begin(p, w) > u) --w;
+    while (w < p.W - 1 && part_begin(p, w + 1) <= u) ++w;
+    return w;
 }
 
 struct AppendArgs {
@@ -136,11 +159,10 @@ struct DecodeArgs {
     const uint8_t *int8_pool;
     int32_t H, P, logP, h, s, w, nr8;
     float inv_sqrt_h;
-    int32_t max_workers, min_units;     // first-phase workers
-    int32_t extra_workers;              // second-phase workers
-    int32_t share_q16;                  // fraction of the units in the first phase, x 2^16
-    int64_t *ws_header;     // [0] total units, [1] u1, [2] w1, [3] w2 (the Partition)
-    int64_t *ws_prefix;     // [B] exclusive prefix of per-row units (all KV heads)
+    int32_t max_workers, min_units;
+    int32_t part_wt[4];                 // worker weights (Partition)
+    int32_t *ws_first;      // [B*H] worker that attended the segment's first unit
+    int32_t *ws_last;       // [B*H] worker that attended the segment's last unit
     float *ws_piece;        // [max_workers + B*H][g][kPieceStride] per-worker pieces
     float *out;
     float *lse;

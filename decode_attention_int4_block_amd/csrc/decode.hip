@@ -1010,27 +1010,18 @@ void decode_split_kernel(DecodeArgs a) {
         for (int o = 32; o >= 1; o >>= 1) rest += __shfl_xor(rest, o, 64);
         total += uni64(rest);
     }
-    const Partition part = make_partition(total, a.max_workers, a.extra_workers, a.share_q16, a.min_units);
-    const int64_t W = part.w1 + part.w2;
-    if (wid == 0 && lane == 0) {
-        a.ws_header[0] = part.total;
-        a.ws_header[1] = part.u1;
-        a.ws_header[2] = part.w1;
-        a.ws_header[3] = part.w2;
-    }
+    const Partition part = make_partition(total, a.max_workers, a.part_wt, a.min_units);
+    const int64_t W = part.W;
     const int64_t u_begin = wid < W ? part_begin(part, wid) : 0;
     const int64_t u_end = wid < W ? part_begin(part, wid + 1) : 0;
     const bool active = wid < W && u_begin < u_end;
-    if (!active && wid != 0) return;
+    if (!active) return;
 
-    // Block 0 stores the prefix for the combine kernel; every active wave finds
-    // the row holding its first unit.
+    // The row holding this wave's first unit.
     int b0 = -1;
     int64_t pre0 = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int b = lane + 64 * k;
-        if (wid == 0 && b < a.B) a.ws_prefix[b] = excl[k];
         const uint64_t mk = __ballot(active && cost[k] > 0 && excl[k] <= u_begin && u_begin < excl[k] + cost[k]);
         if (mk) {
             const int src = uni(__ffsll((unsigned long long)mk) - 1);
@@ -1038,27 +1029,23 @@ void decode_split_kernel(DecodeArgs a) {
             pre0 = readlane64(excl[k], src);
         }
     }
-    if (a.B > kResRows && (wid == 0 || b0 < 0)) {
+    if (a.B > kResRows && b0 < 0) {
         int64_t base = res_total;
         for (int cb = kResRows; cb < a.B; cb += 64) {
             const int b = cb + lane;
             const int64_t c = b < a.B ? (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H : 0;
             const int64_t incl = wave_scan(c, lane);
             const int64_t ex = base + incl - c;
-            if (wid == 0 && b < a.B) a.ws_prefix[b] = ex;
-            if (active && b0 < 0) {
-                const uint64_t mk = __ballot(b < a.B && c > 0 && ex <= u_begin && u_begin < ex + c);
-                if (mk) {
-                    const int src = uni(__ffsll((unsigned long long)mk) - 1);
-                    b0 = uni(cb + src);
-                    pre0 = readlane64(ex, src);
-                    if (wid != 0) break;
-                }
+            const uint64_t mk = __ballot(b < a.B && c > 0 && ex <= u_begin && u_begin < ex + c);
+            if (mk) {
+                const int src = uni(__ffsll((unsigned long long)mk) - 1);
+                b0 = uni(cb + src);
+                pre0 = readlane64(ex, src);
+                break;
             }
             base = uni64(base + readlane64(incl, 63));
         }
     }
-    if (!active) return;
     b0 = uni(b0);
     pre0 = uni64(pre0);
 
@@ -1169,13 +1156,20 @@ void decode_split_kernel(DecodeArgs a) {
         }
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) {
             const SegOut<GP> so = reduce_segment<GP>(c, L, a.g);
-            // this wave covers [u_begin, u_end) in order: it holds the whole
-            // segment iff it has just done the segment's last unit and also did its first
-            const bool whole = C.r == C.rp.cost - 1 && C.u - C.r >= u_begin;
-            if (whole)
+            // this wave covers [u_begin, u_end) in order: it did the segment's
+            // first unit iff that lies in its range, its last iff r is the last
+            // index; with both it holds the whole segment.  The combine kernel
+            // finds a split segment's workers from the two records.
+            const bool first = C.u - C.r >= u_begin, last = C.r == C.rp.cost - 1;
+            const int64_t seg = (int64_t)C.b * a.H + C.hk;
+            if (lane == 0) {
+                if (first) a.ws_first[seg] = (int32_t)wid;
+                if (last) a.ws_last[seg] = (int32_t)wid;
+            }
+            if (first && last)
                 finalize_regs<GP>(a, c, L, so, C.b, C.hk);
             else
-                write_piece<GP>(a, c, L, so, a.ws_piece + (wid + (int64_t)C.b * a.H + C.hk) * (int64_t)a.g * kPieceStride);
+                write_piece<GP>(a, c, L, so, a.ws_piece + (wid + seg) * (int64_t)a.g * kPieceStride);
             open = false;
         }
         cursor_next(a, R, C);
@@ -1197,21 +1191,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     const int part = lane & 15;
     // independent scalar loads, one round trip
     const int Lb = ldc(a.ctx_len, b);
-    Partition pt;
-    pt.total = a.ws_header[0];
-    pt.u1 = a.ws_header[1];
-    pt.w1 = a.ws_header[2];
-    pt.w2 = a.ws_header[3];
-    const int64_t prefix = a.ws_prefix[b];
+    const int64_t wf = ldc(a.ws_first, seg), wl = ldc(a.ws_last, seg);
     const RowPlan rp = row_plan(Lb, a.s, a.w);
     if (rp.cost == 0) {
         for (int i = lane; i < g * kHeadDim; i += 64) a.out[((int64_t)b * a.Hq + (int64_t)hk * g) * kHeadDim + i] = 0.0f;
         if (a.lse && lane < g) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + lane] = kNegInf;
         return;
     }
-    const int64_t c0 = prefix + (int64_t)hk * rp.cost;
-    const int64_t wf = part_of(pt, c0);
-    const int64_t wl = part_of(pt, c0 + rp.cost - 1);
     if (wf == wl) return;           // finished by its only worker
     const float *basep = a.ws_piece + seg * (int64_t)g * kPieceStride;
     for (int hg = 0; hg < g; hg += 4) {
