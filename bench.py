@@ -148,6 +148,71 @@ def device_copy_rate(torch, calibration=False, nbytes=1 << 30, reps=5):
     return round(2 * nbytes / sec / 1e9, 1)
 
 
+# Protection-budget and rotation variants the KV4-RL page compares against
+# ("Main Findings": KV8, KV4 without a side cache, the 16/128 sink/recent split of a
+# 144-position budget and its all-sink / all-recent ablations) and the SAW-INT4
+# page's naive INT4 (no rotation, h = 1).  Same lengths, seeds and kernels.
+def budget_variants(cfg, max_len):
+    return [
+        ("workload (s=%d, w=%d, h=%d)" % (cfg.sink, cfg.recent, cfg.had_block), {}),
+        ("KV4 only (s=0, w=0)", dict(sink=0, recent=0)),
+        ("naive INT4 (h=1)", dict(had_block=1)),
+        ("budget 16/128", dict(sink=16, recent=128)),
+        ("budget 144/0 (all sink)", dict(sink=144, recent=0)),
+        ("budget 0/144 (all recent)", dict(sink=0, recent=144)),
+        ("KV8 everywhere (s+w >= L)", dict(sink=cfg.sink, recent=max(max_len - cfg.sink, cfg.recent))),
+    ]
+
+
+def measure_variants(torch, cfg, steps, warmup):
+    """Decode and append time of each budget variant, caches rotated like the main
+    measurement (one copy when a copy alone is far beyond the 256 MB Infinity Cache)."""
+    from decode_attention_int4_block_amd import QuantKVCache
+    from decode_attention_int4_block_amd.harness import DeviceWorkload
+    from workloads import build_workload
+
+    base = build_workload(cfg)
+    res = []
+    for tag, kw in budget_variants(cfg, int(base.lengths.max())):
+        vcfg = cfg.scaled(**kw)
+        wl = build_workload(vcfg)
+        dw = DeviceWorkload(wl, device="cuda", gen_device="cuda")
+        dw.prefill()
+        db = decode_bytes(wl)
+        copies = [dw.cache]
+        if db["total"] < (2 << 30):
+            for _ in range(3):
+                c2 = QuantKVCache(vcfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
+                                  vcfg.had_block, vcfg.sink, vcfg.recent)
+                c2.int4_pool.copy_(dw.cache.int4_pool)
+                c2.int8_pool.copy_(dw.cache.int8_pool)
+                copies.append(c2)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(warmup + steps):
+            dw.cache = copies[i % len(copies)]
+            ev = evs[i - warmup] if i >= warmup else None
+            if ev:
+                ev[0].record()
+            dw.append_step()
+            if ev:
+                ev[1].record()
+            dw.decode_step()
+            if ev:
+                ev[2].record()
+        torch.cuda.synchronize()
+        dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+        app = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+        us = float(np.median(dec))
+        res.append(dict(variant=tag, sink=vcfg.sink, recent=vcfg.recent, had_block=vcfg.had_block,
+                        decode_algorithmic_bytes=db["total"], decode_us=round(us, 2),
+                        append_us=round(float(np.median(app)), 2),
+                        GBps=round(db["total"] / us / 1e3, 1), hbm_frac=round(db["total"] / us / 1e3 / HBM_PEAK_GBPS, 4)))
+        print(f"[bench] variant {tag}: decode {us:.1f} us, {db['total'] / 1e6:.1f} MB", file=sys.stderr, flush=True)
+        del dw, copies
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +221,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_async_256")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the protection-budget / rotation variants (s, w, h) on the same lengths")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="before warm-up, run one untimed 256 MiB device-to-device copy whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the decode kernel's")
@@ -269,6 +336,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, dw)
+    if args.variants:
+        del layers
+        dw.cache = None
+        torch.cuda.empty_cache()
+        rec["variants"] = measure_variants(torch, cfg, steps=20, warmup=3)
     print(json.dumps(rec), flush=True)
 
 
