@@ -29,12 +29,13 @@ kvq_status ok() {
 }
 
 constexpr int kMinUnitsPerWorker = 8;
-// Work split over the resident waves (two per SIMD).  The SIMD's issue
-// arbitration favours the wave dispatched first -- workgroups [0, W/2) -- which
-// streams ~27% faster than the later one (measured on MI355X); a parity split
-// by XCD measured no better.  Weights: {first half, even w}, {first, odd},
-// {second, even}, {second, odd}.
-constexpr int32_t kPartWeights[4] = {128, 128, 100, 100};
+// Work split over the resident waves (two per SIMD), weighted by their measured
+// speed on MI355X (per-wave timestamps over the Qwen3-8B batch, four boxes):
+// the SIMD's issue arbitration favours the wave dispatched first -- workgroups
+// [0, W/2) -- by ~30%, and workgroups are dispatched round-robin over the 8
+// XCDs, of which the odd-numbered ones (odd w) stream ~6% slower.  Weights:
+// {first half, even w}, {first, odd}, {second, even}, {second, odd}.
+constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_max_workers[kMaxDevices][3];   // per group class g <= 4, <= 8, <= 16
 

@@ -79,7 +79,7 @@ __host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_
 
 // Weighted split of the units over W workers: worker w takes a share in
 // proportion to wt[2 r + (w & 1)], where r = (w >= W / 2), so that waves of
-// different measured speed finish together.  With fewer units than W full
+// different measured speed (dispatch order, XCD) finish together.  With fewer units than W full
 // workers need, an even split over the workers needed.
 struct Partition {
     int64_t total, W, half;
