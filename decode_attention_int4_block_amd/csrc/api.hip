@@ -78,15 +78,21 @@ kvq_status max_workers(int g, int *out) {
 }
 
 struct WsLayout {
-    size_t first_off, last_off, piece_off, total;
+    size_t first_off, last_off, wseg_off, count_off, l2_off, piece_off, total;
 };
+
+size_t l2_slots(size_t segs, int workers) { return (size_t)workers / kvq::kChunkPieces + 1 + segs; }
 
 WsLayout ws_layout(const kvq_cache *c, int B, int g, int workers) {
     WsLayout l;
     const size_t segs = (size_t)B * c->num_kv_heads;
-    l.first_off = 0;
-    l.last_off = align256(segs * sizeof(int32_t));
-    l.piece_off = align256(l.last_off + segs * sizeof(int32_t));
+    const size_t piece_bytes = (size_t)g * kvq::kPieceStride * sizeof(float);
+    l.first_off = kvq::kWsHeaderBytes;
+    l.last_off = align256(l.first_off + segs * sizeof(int32_t));
+    l.wseg_off = align256(l.last_off + segs * sizeof(int32_t));
+    l.count_off = align256(l.wseg_off + 2 * (size_t)workers * sizeof(int32_t));
+    l.l2_off = align256(l.count_off + segs * sizeof(int32_t));
+    l.piece_off = align256(l.l2_off + l2_slots(segs, workers) * piece_bytes);
     const size_t pieces = (size_t)workers + (size_t)B * c->num_kv_heads;
     l.total = align256(l.piece_off + pieces * g * kvq::kPieceStride * sizeof(float));
     return l;
@@ -202,7 +208,11 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     a.max_workers = workers;
     a.min_units = kMinUnitsPerWorker;
     for (int i = 0; i < 4; ++i) a.part_wt[i] = kPartWeights[i];
+    a.ws_header = reinterpret_cast<int32_t *>(ws);
     a.ws_first = reinterpret_cast<int32_t *>(ws + l.first_off);
+    a.ws_wseg = reinterpret_cast<int32_t *>(ws + l.wseg_off);
+    a.ws_count = reinterpret_cast<int32_t *>(ws + l.count_off);
+    a.ws_l2 = reinterpret_cast<float *>(ws + l.l2_off);
     a.ws_last = reinterpret_cast<int32_t *>(ws + l.last_off);
     a.ws_piece = reinterpret_cast<float *>(ws + l.piece_off);
     a.out = out;

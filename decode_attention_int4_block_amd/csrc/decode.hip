@@ -747,14 +747,32 @@ __device__ inline floatx4 combine_cols(floatx4 d) {
 // stand in for A and B: the key dot products add as lo + 16 hi, and the value
 // MFMA weighs the B half of k by 16 p.  Token t of the step is valid iff
 // lo <= base + t < hi.
+//
+// The step is split so that the main loop can overlap consecutive steps of a
+// segment: the key MFMAs of step i are issued, then the softmax and value MFMAs
+// of step i - 1 run while they complete, then step i's scores are formed
+// (kpart_mfma, vpart, kpart_tail).  KOut carries what vpart needs.
 template <int GP>
-__device__ inline void compute_step(SegCtx<GP> &c, const LaneCtx<GP> &L, const StepRegs<GP> &r, bool int8,
-                                    int base, int lo, int hi) {
-    constexpr int kQ = GC<GP>::kQ, NE = GC<GP>::kNE;
+struct KOut {
+    float t[GC<GP>::kNE];       // scaled scores (log2 units / K1), -inf where invalid
+    uint32_t vp[GC<GP>::kNE];   // value (scale, zero) of those positions, 0 where invalid
+    u32x4 vA, vB;               // value codes
+    bool int8;
+};
+
+// Key MFMAs of a step: raw accumulators of subblocks A and B.
+template <int GP>
+struct KAcc {
+    floatx4 dA[GC<GP>::kQ], dB[GC<GP>::kQ];
+};
+
+template <int GP>
+__device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r) {
+    constexpr int kQ = GC<GP>::kQ;
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 dA[kQ], dB[kQ];
+    KAcc<GP> k;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) dA[q] = dB[q] = zero4;
+    for (int q = 0; q < kQ; ++q) k.dA[q] = k.dB[q] = zero4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t x = r.kA[i], x8 = x >> 8;
@@ -763,14 +781,23 @@ __device__ inline void compute_step(SegCtx<GP> &c, const LaneCtx<GP> &L, const S
         const half8 bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            dA[q] = mfma16(ak, c.q4[q][i], dA[q]);
-            dB[q] = mfma16(bk, c.q4[q][i], dB[q]);
+            k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
+            k.dB[q] = mfma16(bk, c.q4[q][i], k.dB[q]);
         }
     }
-    floatx4 sA = dA[0], sB = dB[0];
+    return k;
+}
+
+// Scores of a step from its key accumulators: hi + lo columns, the dense
+// layout, scale/offset, validity.
+template <int GP>
+__device__ inline KOut<GP> kpart_tail(const SegCtx<GP> &c, const LaneCtx<GP> &L, const StepRegs<GP> &r,
+                                      const KAcc<GP> &ka, bool int8, int base, int lo, int hi) {
+    constexpr int kQ = GC<GP>::kQ, NE = GC<GP>::kNE;
+    floatx4 sA = ka.dA[0], sB = ka.dB[0];
     if constexpr (kQ == 2) {
-        sA += dA[1];
-        sB += dB[1];
+        sA += ka.dA[1];
+        sB += ka.dB[1];
     }
     const float f8 = int8 ? 16.0f : 0.0f;
 #pragma unroll
@@ -778,35 +805,46 @@ __device__ inline void compute_step(SegCtx<GP> &c, const LaneCtx<GP> &L, const S
     sA = combine_cols<GP>(sA);
     sB = combine_cols<GP>(sB);
     const float s8[8] = {sA[0], sA[1], sA[2], sA[3], sB[0], sB[1], sB[2], sB[3]};
-    float d[NE], t[NE];
-    uint32_t vp[NE];
+    float d[NE];
     spread<GP>(s8, d);
+    KOut<GP> k;
     const uint32_t off = (uint32_t)(base - lo), span = (uint32_t)(hi - lo);
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         // params of positions past the written context are arbitrary bytes
-        // (possibly NaN as fp16): select, never multiply by zero
+        // (possibly NaN as fp16): computed anyway, then dropped by a select
+        // (never multiplied by zero)
         const bool ok = (uint32_t)L.tok4[e] + off < span;
-        t[e] = ok ? tscore(d[e], r.kp[e], c.Rh) : kNegInf;
-        vp[e] = ok ? r.vp[e] : 0u;
+        const float ts = tscore(d[e], r.kp[e], c.Rh);
+        k.t[e] = ok ? ts : kNegInf;
+        k.vp[e] = ok ? r.vp[e] : 0u;
     }
+    k.vA = r.vA;
+    k.vB = r.vB;
+    k.int8 = int8;
+    return k;
+}
+
+template <int GP>
+__device__ inline void vpart(SegCtx<GP> &c, const LaneCtx<GP> &L, const KOut<GP> &k) {
+    constexpr int kQ = GC<GP>::kQ;
     half8 pop[kQ];
-    softmax_dense<GP>(c, L, t, vp, pop);
+    softmax_dense<GP>(c, L, k.t, k.vp, pop);
     // INT8: k slots 2, 3 (the high-nibble plane) weigh 16 p of slots 0, 1; the
     // INT4 slots 2, 3 (subblock B) are kept by weight 1 and weight 0 on the
     // copy of slots 0, 1
     {
-        const _Float16 wb = int8 ? (_Float16)0.0f : (_Float16)1.0f;
-        const _Float16 wa = int8 ? (_Float16)16.0f : (_Float16)0.0f;
+        const _Float16 wb = k.int8 ? (_Float16)0.0f : (_Float16)1.0f;
+        const _Float16 wa = k.int8 ? (_Float16)16.0f : (_Float16)0.0f;
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) pop[q][4 + k] = pop[q][4 + k] * wb + pop[q][k] * wa;
+            for (int j = 0; j < 4; ++j) pop[q][4 + j] = pop[q][4 + j] * wb + pop[q][j] * wa;
         }
     }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-        const uint32_t x = r.vA[cc], x8 = x >> 8, y = r.vB[cc], y8 = y >> 8;
+        const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
         const half8 ve = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
         const half8 vo = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
 #pragma unroll
@@ -1015,6 +1053,13 @@ void decode_split_kernel(DecodeArgs a) {
     const int64_t u_begin = wid < W ? part_begin(part, wid) : 0;
     const int64_t u_end = wid < W ? part_begin(part, wid + 1) : 0;
     const bool active = wid < W && u_begin < u_end;
+    if (lane == 0) {
+        if (wid == 0) a.ws_header[0] = (int32_t)W;
+        if (wid < W && !active) {                   // a worker without units leaves no pieces
+            a.ws_wseg[2 * wid] = -1;
+            a.ws_wseg[2 * wid + 1] = -1;
+        }
+    }
     if (!active) return;
 
     // The row holding this wave's first unit.
@@ -1120,7 +1165,34 @@ void decode_split_kernel(DecodeArgs a) {
             advance_half(P);
         }
     }
-    bool open = false;
+    int32_t wseg0 = -1, wseg1 = -1;     // segments of this wave's first / last piece
+    // End of the segment of the step at cursor E, once its value part is done.
+    auto end_segment = [&](const Cursor &E) {
+        const SegOut<GP> so = reduce_segment<GP>(c, L, a.g);
+        // this wave covers [u_begin, u_end) in order: it did the segment's
+        // first unit iff that lies in its range, its last iff r is the last
+        // index; with both it holds the whole segment.  The combine kernel
+        // finds a split segment's workers from the two records.
+        const bool first = E.u - E.r >= u_begin, last = E.r == E.rp.cost - 1;
+        const int64_t seg = (int64_t)E.b * a.H + E.hk;
+        if (lane == 0) {
+            if (first) {
+                a.ws_first[seg] = (int32_t)wid;
+                a.ws_count[seg] = 0;
+            }
+            if (last) a.ws_last[seg] = (int32_t)wid;
+        }
+        if (!first) wseg0 = (int32_t)seg;            // only the wave's first segment can start earlier
+        if (!last) wseg1 = (int32_t)seg;             // only its last one can go on after it
+        if (first && last)
+            finalize_regs<GP>(a, c, L, so, E.b, E.hk);
+        else
+            write_piece<GP>(a, c, L, so, a.ws_piece + (wid + seg) * (int64_t)a.g * kPieceStride);
+    };
+    bool open = false;          // the next step continues the current segment
+    bool pend = false;          // a step of the current segment awaits its value part
+    KOut<GP> kp;                // that step's scores and value codes
+    Cursor E = C;               // its cursor
     for (int i = 0; C.u < u_end; ++i) {
         // (a query copy issued with a later step only makes this wait stricter)
         wait_vm_steps(issued - i - 1);
@@ -1141,121 +1213,242 @@ void decode_split_kernel(DecodeArgs a) {
             advance_half(P);
         }
         if (!open) {
+            // this step starts a segment: finish the previous one first
+            if (pend) {
+                vpart<GP>(c, L, kp);
+                end_segment(E);
+                pend = false;
+            }
             // a segment's first step finds mK = -inf and scales O, lsum and
             // zsum (finite leftovers of the previous segment) by 0
             build_query<GP>(a, qr, L, c);
             c.mK = kNegInf;
             open = true;
         }
-        {
-            const int e0 = 16 * (C.r - C.rp.n4);
-            const int sbase = int4 ? (C.rp.k0 + C.r) * 32 : e0;
-            const int slo = int4 ? C.rp.lo4 : 0;
-            const int shi = int4 ? C.rp.hi4 : min(C.rp.n8e, e0 + 16);
-            compute_step<GP>(c, L, r, !int4, sbase, slo, shi);
-        }
-        if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) {
-            const SegOut<GP> so = reduce_segment<GP>(c, L, a.g);
-            // this wave covers [u_begin, u_end) in order: it did the segment's
-            // first unit iff that lies in its range, its last iff r is the last
-            // index; with both it holds the whole segment.  The combine kernel
-            // finds a split segment's workers from the two records.
-            const bool first = C.u - C.r >= u_begin, last = C.r == C.rp.cost - 1;
-            const int64_t seg = (int64_t)C.b * a.H + C.hk;
-            if (lane == 0) {
-                if (first) a.ws_first[seg] = (int32_t)wid;
-                if (last) a.ws_last[seg] = (int32_t)wid;
-            }
-            if (first && last)
-                finalize_regs<GP>(a, c, L, so, C.b, C.hk);
-            else
-                write_piece<GP>(a, c, L, so, a.ws_piece + (wid + seg) * (int64_t)a.g * kPieceStride);
-            open = false;
-        }
+        const int e0 = 16 * (C.r - C.rp.n4);
+        const int sbase = int4 ? (C.rp.k0 + C.r) * 32 : e0;
+        const int slo = int4 ? C.rp.lo4 : 0;
+        const int shi = int4 ? C.rp.hi4 : min(C.rp.n8e, e0 + 16);
+        const KAcc<GP> ka = kpart_mfma<GP>(c, r);
+        if (pend) vpart<GP>(c, L, kp);          // previous step, same segment
+        kp = kpart_tail<GP>(c, L, r, ka, !int4, sbase, slo, shi);
+        pend = true;
+        E = C;
+        if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
         cursor_next(a, R, C);
+    }
+    if (pend) {
+        vpart<GP>(c, L, kp);
+        end_segment(E);
+    }
+    if (lane == 0) {
+        a.ws_wseg[2 * wid] = wseg0;
+        a.ws_wseg[2 * wid + 1] = wseg1;
     }
 }
 
-// Log-sum-exp combine of the pieces of one (row, KV head) segment that several
-// workers share; one wave per segment, lane l handles query head 4k + l/16 and
-// dims 8 (l % 16) .. +8.  Also writes the rows with no context.  The pieces are
-// read kCombBatch at a time with all their loads in flight together, and the
-// running (max, sum, acc) is rescaled once per batch.
+// Log-sum-exp combine of the pieces of the (row, KV head) segments that several
+// workers share; also writes the rows with no context.
+//
+// Workgroups [0, B*H) take one segment each: rows without context, and
+// segments of at most kChunkPieces pieces, merged directly.  A longer segment
+// (a long row split over many workers) is folded in parallel by the helper
+// workgroups B*H + j, j = 0, 1, ...: helper j takes the pieces of workers
+// [j T, (j + 1) T), T = kChunkPieces, folds each long segment's share into a
+// chunk partial, and counts the folded pieces on the segment (an agent-scope
+// acquire-release add: the helpers run on different XCDs); the helper that
+// completes the count folds the chunk partials.  Pieces and chunks are folded in
+// worker order, so the result is the same whoever finishes last.
+//
+// Lane l handles query heads 8 k + l / 16 and 8 k + 4 + l / 16 and dims
+// 8 (l % 16) .. + 8 of a piece laid out as [head][m, l, 0, 0, acc[128]].
 constexpr int kCombBatch = 4;
 
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-    const int lane = threadIdx.x;
-    const int64_t seg = blockIdx.x;
-    const int b = (int)(seg / a.H), hk = (int)(seg % a.H);
-    const int g = a.g;
-    const int part = lane & 15;
-    // independent scalar loads, one round trip
-    const int Lb = ldc(a.ctx_len, b);
-    const int64_t wf = ldc(a.ws_first, seg), wl = ldc(a.ws_last, seg);
-    const RowPlan rp = row_plan(Lb, a.s, a.w);
-    if (rp.cost == 0) {
-        for (int i = lane; i < g * kHeadDim; i += 64) a.out[((int64_t)b * a.Hq + (int64_t)hk * g) * kHeadDim + i] = 0.0f;
-        if (a.lse && lane < g) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + lane] = kNegInf;
-        return;
-    }
-    if (wf == wl) return;           // finished by its only worker
-    const float *basep = a.ws_piece + seg * (int64_t)g * kPieceStride;
-    for (int hg = 0; hg < g; hg += 4) {
-        const int j = hg + (lane >> 4);
-        const bool on = j < g;
-        float M = kNegInf, Ls = 0.0f;
-        float acc[8];
+struct MergeAcc {
+    float M, Ls, acc[8];
+};
+
+__device__ inline void merge_init(MergeAcc &r) {
+    r.M = kNegInf;
+    r.Ls = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-        for (int64_t w0 = wf; w0 <= wl; w0 += kCombBatch) {
-            float m[kCombBatch], l[kCombBatch];
-            u32x4 v0[kCombBatch], v1[kCombBatch];
+    for (int e = 0; e < 8; ++e) r.acc[e] = 0.0f;
+}
+
+// Folds pieces ptr(0), ..., ptr(cnt - 1) (wave-uniform bases) for heads
+// jj[0] and, when two2, jj[1] (two head groups share each batch of loads).
+template <typename PtrFn>
+__device__ inline void fold_pieces(MergeAcc (&r)[2], PtrFn ptr, int cnt, const int (&jj)[2], bool two2, int part) {
+    for (int k0 = 0; k0 < cnt; k0 += kCombBatch) {
+        float m[2][kCombBatch], l[2][kCombBatch];
+        u32x4 v0[2][kCombBatch], v1[2][kCombBatch];
 #pragma unroll
-            for (int k = 0; k < kCombBatch; ++k) {
-                const float *pp = basep + ((w0 + k) * g + (on ? j : 0)) * kPieceStride;
-                if (w0 + k <= wl) {
-                    m[k] = pp[0];
-                    l[k] = pp[1];
-                    v0[k] = ldg<u32x4>(pp + 4 + 8 * part);
-                    v1[k] = ldg<u32x4>(pp + 8 + 8 * part);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < kCombBatch; ++t) {
+                if (k0 + t < cnt && (h == 0 || two2)) {
+                    const float *pp = ptr(k0 + t) + jj[h] * kPieceStride;
+                    m[h][t] = pp[0];
+                    l[h][t] = pp[1];
+                    v0[h][t] = ldg<u32x4>(pp + 4 + 8 * part);
+                    v1[h][t] = ldg<u32x4>(pp + 8 + 8 * part);
                 } else {
-                    m[k] = kNegInf;
-                    l[k] = 0.0f;
-                    v0[k] = u32x4{0u, 0u, 0u, 0u};
-                    v1[k] = u32x4{0u, 0u, 0u, 0u};
+                    m[h][t] = kNegInf;
+                    l[h][t] = 0.0f;
+                    v0[h][t] = u32x4{0u, 0u, 0u, 0u};
+                    v1[h][t] = u32x4{0u, 0u, 0u, 0u};
                 }
             }
-            float Mn = M;
 #pragma unroll
-            for (int k = 0; k < kCombBatch; ++k) Mn = fmaxf(Mn, m[k]);
-            const float fr = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-            Ls *= fr;
+        for (int h = 0; h < 2; ++h) {
+            float Mn = r[h].M;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] *= fr;
+            for (int t = 0; t < kCombBatch; ++t) Mn = fmaxf(Mn, m[h][t]);
+            const float fr = r[h].M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(r[h].M - Mn);
+            r[h].Ls *= fr;
 #pragma unroll
-            for (int k = 0; k < kCombBatch; ++k) {
-                const float f = m[k] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m[k] - Mn);
-                Ls = fmaf(l[k], f, Ls);
+            for (int e = 0; e < 8; ++e) r[h].acc[e] *= fr;
+#pragma unroll
+            for (int t = 0; t < kCombBatch; ++t) {
+                const float f = m[h][t] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m[h][t] - Mn);
+                r[h].Ls = fmaf(l[h][t], f, r[h].Ls);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[e] = fmaf(__uint_as_float(v0[k][e]), f, acc[e]);
-                    acc[4 + e] = fmaf(__uint_as_float(v1[k][e]), f, acc[4 + e]);
+                    r[h].acc[e] = fmaf(__uint_as_float(v0[h][t][e]), f, r[h].acc[e]);
+                    r[h].acc[4 + e] = fmaf(__uint_as_float(v1[h][t][e]), f, r[h].acc[4 + e]);
                 }
             }
-            M = Mn;
+            r[h].M = Mn;
         }
-        if (on) {
-            float *o = a.out + ((int64_t)b * a.Hq + (int64_t)hk * g + j) * kHeadDim + 8 * part;
-            const float inv = 1.0f / Ls;
-            u32x4 w0, w1;
+    }
+}
+
+// Normalized output (and lse) of head j from a fold.
+__device__ inline void merge_write(const DecodeArgs &a, const MergeAcc &r, int b, int hk, int j, int part) {
+    float *o = a.out + ((int64_t)b * a.Hq + (int64_t)hk * a.g + j) * kHeadDim + 8 * part;
+    const float inv = 1.0f / r.Ls;
+    u32x4 w0, w1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w0[e] = __float_as_uint(acc[e] * inv);
-                w1[e] = __float_as_uint(acc[4 + e] * inv);
-            }
-            *reinterpret_cast<u32x4 *>(o) = w0;
-            *reinterpret_cast<u32x4 *>(o + 4) = w1;
-            if (a.lse && part == 0) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + j] = (M + __log2f(Ls)) / kLog2e;
+    for (int e = 0; e < 4; ++e) {
+        w0[e] = __float_as_uint(r.acc[e] * inv);
+        w1[e] = __float_as_uint(r.acc[4 + e] * inv);
+    }
+    *reinterpret_cast<u32x4 *>(o) = w0;
+    *reinterpret_cast<u32x4 *>(o + 4) = w1;
+    if (a.lse && part == 0) a.lse[(int64_t)b * a.Hq + (int64_t)hk * a.g + j] = (r.M + __log2f(r.Ls)) / kLog2e;
+}
+
+// Raw fold (m, l, acc) of head j into a piece-shaped chunk partial.
+__device__ inline void merge_store(const MergeAcc &r, float *pp, int j, int part) {
+    float *ph = pp + j * kPieceStride;
+    if (part == 0) {
+        ph[0] = r.M;
+        ph[1] = r.Ls;
+    }
+    u32x4 w0, w1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        w0[e] = __float_as_uint(r.acc[e]);
+        w1[e] = __float_as_uint(r.acc[4 + e]);
+    }
+    *reinterpret_cast<u32x4 *>(ph + 4 + 8 * part) = w0;
+    *reinterpret_cast<u32x4 *>(ph + 8 + 8 * part) = w1;
+}
+
+__device__ inline int wave_min(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+    return uni(x);
+}
+
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int T = kChunkPieces;
+    const int lane = threadIdx.x;
+    const int g = a.g;
+    const int part = lane & 15;
+    const int64_t nseg = (int64_t)a.B * a.H;
+    const int64_t piece_elems = (int64_t)g * kPieceStride;
+    if ((int64_t)blockIdx.x < nseg) {
+        const int64_t seg = blockIdx.x;
+        const int b = (int)(seg / a.H), hk = (int)(seg % a.H);
+        // independent scalar loads, one round trip
+        const int Lb = ldc(a.ctx_len, b);
+        const int64_t wf = ldc(a.ws_first, seg), wl = ldc(a.ws_last, seg);
+        const RowPlan rp = row_plan(Lb, a.s, a.w);
+        if (rp.cost == 0) {
+            for (int i = lane; i < g * kHeadDim; i += 64)
+                a.out[((int64_t)b * a.Hq + (int64_t)hk * g) * kHeadDim + i] = 0.0f;
+            if (a.lse && lane < g) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + lane] = kNegInf;
+            return;
+        }
+        const int n = (int)(wl - wf + 1);
+        if (n == 1 || n > T) return;            // finished by its only worker / folded by the helpers
+        const float *basep = a.ws_piece + (wf + seg) * piece_elems;
+        for (int hg = 0; hg < g; hg += 8) {
+            const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
+            const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
+            MergeAcc r[2];
+            merge_init(r[0]);
+            merge_init(r[1]);
+            fold_pieces(r, [&](int k) { return basep + k * piece_elems; }, n, jj, hg + 4 < g, part);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if (j[h] < g) merge_write(a, r[h], b, hk, j[h], part);
+        }
+        return;
+    }
+    // helper: the pieces of workers [w0, w0 + T)
+    const int64_t jc = (int64_t)blockIdx.x - nseg;
+    const int64_t W = ldc(a.ws_header, 0);
+    const int64_t w0 = jc * T;
+    if (w0 >= W) return;
+    int v = -1;
+    if (lane < 2 * T && w0 + lane / 2 < W) v = a.ws_wseg[2 * w0 + lane];
+    if (v >= nseg) v = -1;
+    // keep the long segments among them (one round trip for all lanes)
+    if (v >= 0 && a.ws_last[v] - a.ws_first[v] + 1 <= T) v = -1;
+    int prev = -1;
+    for (;;) {
+        // the long segments of these workers' pieces, in increasing order
+        const int s = wave_min(v > prev ? v : 0x7fffffff);
+        if (s == 0x7fffffff) break;
+        prev = s;
+        const int64_t wf = ldc(a.ws_first, s), wl = ldc(a.ws_last, s);
+        const int n = (int)(wl - wf + 1);
+        const int b = s / a.H, hk = s % a.H;
+        const int64_t wa = w0 > wf ? w0 : wf;
+        const int64_t wb = (w0 + T - 1 < wl ? w0 + T - 1 : wl);
+        const float *basep = a.ws_piece + (wa + s) * piece_elems;
+        float *chunk = a.ws_l2 + (jc + s) * piece_elems;
+        for (int hg = 0; hg < g; hg += 8) {
+            const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
+            const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
+            MergeAcc r[2];
+            merge_init(r[0]);
+            merge_init(r[1]);
+            fold_pieces(r, [&](int k) { return basep + k * piece_elems; }, (int)(wb - wa + 1), jj, hg + 4 < g, part);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if (j[h] < g) merge_store(r[h], chunk, j[h], part);
+        }
+        int before = 0;
+        if (lane == 0)
+            before = __hip_atomic_fetch_add(a.ws_count + s, (int)(wb - wa + 1), __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        before = uni(before);
+        if (before + (int)(wb - wa + 1) != n) continue;
+        // the last helper of the segment folds its chunk partials
+        const int64_t jf = wf / T, jl = wl / T;
+        const float *c0 = a.ws_l2 + (jf + s) * piece_elems;
+        for (int hg = 0; hg < g; hg += 8) {
+            const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
+            const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
+            MergeAcc r[2];
+            merge_init(r[0]);
+            merge_init(r[1]);
+            fold_pieces(r, [&](int k) { return c0 + k * piece_elems; }, (int)(jl - jf + 1), jj, hg + 4 < g, part);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if (j[h] < g) merge_write(a, r[h], b, hk, j[h], part);
         }
     }
 }
@@ -1273,7 +1466,8 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H), dim3(64), 0, stream, a);
+    const int helpers = (grid + kChunkPieces - 1) / kChunkPieces;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H + helpers), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
