@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import KvqCache, KvqError
 
-__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "KvqError"]
+__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_append_decode_attn", "KvqError"]
 
 
 def _ptr(t):
@@ -89,9 +89,7 @@ def kv_quant_append(cache: QuantKVCache, k, v, slot, pos, block_table, len_after
     _lib.check(st, "kv_quant_append")
 
 
-def kv_decode_attn(cache: QuantKVCache, q, slot, block_table, ctx_len, out=None, lse=None,
-                   workspace=None, stream=None):
-    """Decode attention of q [B, H_q, 128] bf16; returns (out fp32 [B, H_q, 128], lse [B, H_q])."""
+def _decode_args(cache, q, slot, block_table, ctx_len, out, lse, workspace):
     _dev_bf16(q, "q")
     B, Hq, d = q.shape
     _dev_i32(slot, "slot")
@@ -105,8 +103,36 @@ def kv_decode_attn(cache: QuantKVCache, q, slot, block_table, ctx_len, out=None,
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = cache.new_workspace(B, Hq)
+    return out, lse, workspace
+
+
+def kv_decode_attn(cache: QuantKVCache, q, slot, block_table, ctx_len, out=None, lse=None,
+                   workspace=None, stream=None):
+    """Decode attention of q [B, H_q, 128] bf16; returns (out fp32 [B, H_q, 128], lse [B, H_q])."""
+    out, lse, workspace = _decode_args(cache, q, slot, block_table, ctx_len, out, lse, workspace)
+    B, Hq = q.shape[0], q.shape[1]
     st = cache.lib.kv_decode_attn(ctypes.byref(cache.desc), _ptr(q), Hq, _ptr(slot), _ptr(block_table),
                                   block_table.shape[1], _ptr(ctx_len), B, _ptr(out), _ptr(lse),
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "kv_decode_attn")
+    return out, lse
+
+
+def kv_append_decode_attn(cache: QuantKVCache, k, v, q, slot, block_table, ctx_len, out=None, lse=None,
+                          workspace=None, stream=None):
+    """Append k, v [B, H_kv, 128] bf16 at position ctx_len - 1 of each row, then attend q.
+
+    The same cache bytes and outputs as kv_quant_append followed by
+    kv_decode_attn, in one launch; returns (out, lse).
+    """
+    out, lse, workspace = _decode_args(cache, q, slot, block_table, ctx_len, out, lse, workspace)
+    B, Hq = q.shape[0], q.shape[1]
+    _dev_bf16(k, "k")
+    _dev_bf16(v, "v")
+    if k.shape != (B, cache.num_kv_heads, 128) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [{B}, {cache.num_kv_heads}, 128], got {tuple(k.shape)}, {tuple(v.shape)}")
+    st = cache.lib.kv_append_decode_attn(ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(q), Hq, _ptr(slot),
+                                         _ptr(block_table), block_table.shape[1], _ptr(ctx_len), B, _ptr(out),
+                                         _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+    _lib.check(st, "kv_append_decode_attn")
     return out, lse

@@ -37,7 +37,8 @@ constexpr int kMinUnitsPerWorker = 8;
 // {first half, even w}, {first, odd}, {second, even}, {second, odd}.
 constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_max_workers[kMaxDevices][3];   // per group class g <= 4, <= 8, <= 16
+// per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused append)
+std::atomic<int> g_max_workers[kMaxDevices][6];
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -62,14 +63,14 @@ float inv_sqrt(int h) { return (float)(1.0 / sqrt((double)h)); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-kvq_status max_workers(int g, int *out) {
+kvq_status max_workers(int g, bool fused, int *out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
-    const int cls = g <= 4 ? 0 : (g <= 8 ? 1 : 2);
+    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (fused ? 3 : 0);
     int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
-        hipError_t e = kvq::decode_max_workers(g, &v);
+        hipError_t e = kvq::decode_max_workers(g, fused, &v);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         g_max_workers[dev][cls].store(v, std::memory_order_relaxed);
     }
@@ -154,15 +155,23 @@ size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num
     if (check_cache(c) != KVQ_OK || B < 0 || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
     const int g = num_q_heads / c->num_kv_heads;
     if (g > 16) return 0;
-    int workers = 0;
-    if (max_workers(g, &workers) != KVQ_OK) return 0;
-    return ws_layout(c, B, g, workers).total;
+    // large enough for both kernels (attention only and fused append)
+    int workers = 0, workers_fused = 0;
+    if (max_workers(g, false, &workers) != KVQ_OK || max_workers(g, true, &workers_fused) != KVQ_OK) return 0;
+    const size_t a = ws_layout(c, B, g, workers).total, b = ws_layout(c, B, g, workers_fused).total;
+    return a > b ? a : b;
 }
 
-kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads,
-                          const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
-                          const int32_t *ctx_len, int32_t B, float *out, float *lse,
-                          void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Attention of a batch, or (fused) the append of each row's token followed by
+// the attention, in one split-kernel launch.
+kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, const uint16_t *v_new,
+                         const uint16_t *q, int32_t num_q_heads, const int32_t *slot, const int32_t *block_table,
+                         int32_t bt_stride, const int32_t *ctx_len, int32_t B, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream) {
     kvq_status st = check_cache(c);
     if (st != KVQ_OK) return st;
     if (B < 0) return fail(KVQ_ERR_SHAPE, "B = %d < 0", B);
@@ -173,14 +182,14 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     if (g > 16) return fail(KVQ_ERR_UNSUPPORTED, "query group %d > 16", g);
     if (B == 0) return ok();
     if ((int64_t)B * num_q_heads > ((int64_t)1 << 31) - 1) return fail(KVQ_ERR_SHAPE, "B * num_q_heads too large");
-    if (!q || !slot || !block_table || !ctx_len || !out)
+    if (!q || !slot || !block_table || !ctx_len || !out || (fused && (!k_new || !v_new)))
         return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
     int workers = 0;
-    st = max_workers(g, &workers);
+    st = max_workers(g, fused, &workers);
     if (st != KVQ_OK) return st;
     const WsLayout l = ws_layout(c, B, g, workers);
     if (workspace_bytes < l.total)
@@ -195,8 +204,10 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     a.bt_stride = bt_stride;
     a.ctx_len = ctx_len;
     a.B = B;
-    a.int4_pool = static_cast<const uint8_t *>(c->int4_pool);
-    a.int8_pool = static_cast<const uint8_t *>(c->int8_pool);
+    a.int4_pool = static_cast<uint8_t *>(c->int4_pool);
+    a.int8_pool = static_cast<uint8_t *>(c->int8_pool);
+    a.k_new = fused ? k_new : nullptr;
+    a.v_new = fused ? v_new : nullptr;
     a.H = c->num_kv_heads;
     a.P = c->page_size;
     a.logP = __builtin_ctz((unsigned)c->page_size);
@@ -220,6 +231,26 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
     hipError_t e = kvq::launch_decode(a, workers, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads,
+                          const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
+                          const int32_t *ctx_len, int32_t B, float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_launch(c, false, nullptr, nullptr, q, num_q_heads, slot, block_table, bt_stride, ctx_len, B, out, lse,
+                         workspace, workspace_bytes, stream);
+}
+
+kvq_status kv_append_decode_attn(const kvq_cache *c, const uint16_t *k, const uint16_t *v, const uint16_t *q,
+                                 int32_t num_q_heads, const int32_t *slot, const int32_t *block_table,
+                                 int32_t bt_stride, const int32_t *ctx_len, int32_t B, float *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_launch(c, true, k, v, q, num_q_heads, slot, block_table, bt_stride, ctx_len, B, out, lse, workspace,
+                         workspace_bytes, stream);
 }
 
 const char *kvq_status_string(kvq_status s) {

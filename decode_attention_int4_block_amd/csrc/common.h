@@ -41,6 +41,8 @@ struct RowPlan {
     int k0, n4;     // first 32-position step index and number of INT4 steps
     int n8e, n8;    // valid ring entries and INT8 steps
     int cost;       // n4 + n8 units
+    int rn, tn;     // the newest position L - 1: its unit, and its token (INT4 step)
+                    // or ring entry (INT8 step) inside that unit; rn = -1 when L = 0
 };
 
 __host__ __device__ inline RowPlan row_plan(int L, int s, int w) {
@@ -59,6 +61,20 @@ __host__ __device__ inline RowPlan row_plan(int L, int s, int w) {
     if (r.n8e < 0) r.n8e = 0;
     r.n8 = (r.n8e + 15) >> 4;
     r.cost = r.n4 + r.n8;
+    const int p = L - 1;
+    if (L <= 0) {
+        r.rn = -1;
+        r.tn = 0;
+    } else if (p < s || w > 0) {
+        // a sink, or the recent window (which always holds the newest
+        // position): ring entry p for a sink, else s + (p - s) mod w
+        const int e = p < s ? p : s + (p - s) % w;
+        r.rn = r.n4 + (e >> 4);
+        r.tn = e & 15;
+    } else {
+        r.rn = (p >> 5) - r.k0;
+        r.tn = p & 31;
+    }
     return r;
 }
 
@@ -156,8 +172,10 @@ struct DecodeArgs {
     int32_t bt_stride;
     const int32_t *ctx_len;
     int32_t B;
-    const uint8_t *int4_pool;
-    const uint8_t *int8_pool;
+    uint8_t *int4_pool;     // written only by the fused append
+    uint8_t *int8_pool;
+    const uint16_t *k_new;  // [B][H][128] bf16 key / value each row appends at
+    const uint16_t *v_new;  //   position ctx_len - 1 (fused append), or nullptr
     int32_t H, P, logP, h, s, w, nr8;
     float inv_sqrt_h;
     int32_t max_workers, min_units;
@@ -175,6 +193,6 @@ struct DecodeArgs {
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream);
-hipError_t decode_max_workers(int g, int *out);
+hipError_t decode_max_workers(int g, bool fused, int *out);
 
 }  // namespace kvq

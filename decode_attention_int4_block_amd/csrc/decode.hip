@@ -35,6 +35,8 @@
 #include <hip/hip_fp16.h>
 
 #include "common.h"
+#include "lanes.h"
+#include "quant.h"
 
 namespace kvq {
 
@@ -128,49 +130,6 @@ __device__ inline int ldc(const int32_t *p, int64_t i) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-lane moves (VALU, no LDS).  DPP controls inside 16-lane rows:
-// row_shl:n (lane i <- i + n), row_shr:n (lane i <- i - n), row_ror:n
-// (lane i <- (i - n) mod 16); the bank mask selects which groups of 4 lanes of
-// each row are written, the others keep `old`.
-constexpr int kRowShl = 0x100, kRowShr = 0x110, kRowRor = 0x120;
-
-template <int CTRL, int BANKS = 0xF>
-__device__ inline uint32_t dpp(uint32_t old, uint32_t src) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANKS, false);
-}
-template <int CTRL, int BANKS = 0xF>
-__device__ inline float dppf(float old, float src) {
-    return __uint_as_float(dpp<CTRL, BANKS>(__float_as_uint(old), __float_as_uint(src)));
-}
-
-// (r0, r1) of permlane16_swap(a, b): rows [a0 b0 a2 b2] and [a1 b1 a3 b3].
-__device__ inline void swap16(float a, float b, float &r0, float &r1) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    r0 = __uint_as_float(r[0]);
-    r1 = __uint_as_float(r[1]);
-}
-// (r0, r1) of permlane32_swap(a, b): rows [a0 a1 b0 b1] and [a2 a3 b2 b3].
-__device__ inline void swap32(float a, float b, float &r0, float &r1) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    r0 = __uint_as_float(r[0]);
-    r1 = __uint_as_float(r[1]);
-}
-
-__device__ inline float max_rows(float x) {      // max over lanes l, l^16, l^32, l^48
-    float r0, r1;
-    swap32(x, x, r0, r1);
-    x = fmaxf(r0, r1);
-    swap16(x, x, r0, r1);
-    return fmaxf(r0, r1);
-}
-__device__ inline float sum_rows(float x) {      // sum over lanes l, l^16, l^32, l^48
-    float r0, r1;
-    swap32(x, x, r0, r1);
-    x = r0 + r1;
-    swap16(x, x, r0, r1);
-    return r0 + r1;
-}
-
 // Max / sum over the lanes that hold the same query head in the dense layout
 // (lanes l with equal l % GP: kParts per row, four rows).
 template <int GP>
@@ -184,29 +143,6 @@ __device__ inline float head_sum(float x) {
     if constexpr (GP <= 8) x += dppf<kRowRor + 8>(0.0f, x);
     if constexpr (GP == 4) x += dppf<kRowRor + 4>(0.0f, x);
     return sum_rows(x);
-}
-
-// Hadamard butterfly between lanes l and l ^ X: the lower lane ends with
-// (its value) + (partner's), the upper with (partner's) - (its value).
-template <int X>
-__device__ inline float butterfly(float x, int lane) {
-    const float sgn = (lane & X) ? -1.0f : 1.0f;
-    if constexpr (X == 16 || X == 32) {
-        float r0, r1;
-        if constexpr (X == 16) swap16(x, x, r0, r1);
-        else swap32(x, x, r0, r1);
-        // lower rows: r0 = own, r1 = partner; upper rows: r0 = partner, r1 = own
-        return fmaf(r1, sgn, r0);
-    } else {
-        float p;
-        if constexpr (X == 8) {
-            p = dppf<kRowRor + 8>(0.0f, x);
-        } else {
-            p = dppf<kRowShl + X, 0x5>(x, x);        // banks 0, 2 read lane + 4
-            p = dppf<kRowShr + X, 0xA>(p, x);        // banks 1, 3 read lane - 4
-        }
-        return fmaf(x, sgn, p);
-    }
 }
 
 // Slot J (0..3) of the packed MFMA rows: lanes with column c < GP take the hi
@@ -961,6 +897,77 @@ __device__ inline void write_piece(const DecodeArgs &a, const SegCtx<GP> &c, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused append.  Each row appends one token at position L - 1 before it is
+// attended (KV4-RL, "Methodology in Plain English": the new K/V is quantized on
+// the fly as it enters the cache).  The worker whose range holds the unit that
+// attends position L - 1 (RowPlan::rn) quantizes the token, stores it into the
+// INT4 cache and, for a sink or recent position, the INT8 side cache, exactly
+// as the quantize-append kernel does, and patches the copy of the step already
+// in its LDS stage.  No other worker reads those bytes in this launch: the
+// unit is the only one covering that INT8 subblock (or, without a recent
+// window, that INT4 subblock); an INT4 step whose range ends before L - 1 may
+// copy the subblock holding it, but masks that position.
+//
+// The token's bf16 key and value (lanes 0-15 and 16-31, 16 bytes each) and the
+// block-table entry of its page come into an LDS slot with the step's own
+// copies, so the stage wait covers them.
+constexpr int kKvBytes = 528;           // 256 B key, 256 B value, page entry, pad
+constexpr int kKvPage = 512;
+
+__device__ inline void issue_new_token(const DecodeArgs &a, const RowRegs &R, const Cursor &c, uint8_t *slot,
+                                       int lane) {
+    const int64_t row = (int64_t)c.b * a.H + c.hk;
+    const uint16_t *src = (lane < 16 ? a.k_new : a.v_new) + row * kHeadDim + 8 * (lane & 15);
+    if (lane < 32) __builtin_amdgcn_global_load_lds(src, (lds_ptr)slot, 16, 0, 0);
+    const int p = row_len(a, R, c.b) - 1;
+    const int32_t *pe = a.block_table + (int64_t)row_slot(a, R, c.b) * a.bt_stride + (p >> a.logP);
+    if (lane == 0) __builtin_amdgcn_global_load_lds(pe, (lds_ptr)(slot + kKvPage), 4, 0, 0);
+}
+
+__device__ inline void append_new_token(const DecodeArgs &a, const RowRegs &R, const Cursor &c,
+                                        const uint8_t *kv, uint8_t *st, int lane) {
+    const int vd0 = 32 * (lane >> 4) + (lane & 15);
+    const uint32_t kw = lds32(kv + 4 * lane);
+    const uint32_t vlo = *reinterpret_cast<const uint16_t *>(kv + 256 + 2 * vd0);
+    const uint32_t vhi = *reinterpret_cast<const uint16_t *>(kv + 256 + 2 * (vd0 + 16));
+    const int page = uni((int)lds32(kv + kKvPage));
+    const TokenCodes tc = quantize_token(kw, vlo, vhi, a.h, a.inv_sqrt_h, lane);
+    const int p = row_len(a, R, c.b) - 1;
+    uint8_t *base4 = a.int4_pool +
+        ((size_t)((int64_t)page * a.H + c.hk) * (a.P >> 4) + ((p & (a.P - 1)) >> 4)) * kSub4Bytes;
+    const bool int8 = c.rp.rn >= c.rp.n4;
+    const int e = ((c.rp.rn - c.rp.n4) << 4) + c.rp.tn;
+    uint8_t *base8 = int8
+        ? a.int8_pool + ((size_t)((int64_t)row_slot(a, R, c.b) * a.H + c.hk) * a.nr8 + (e >> 4)) * kSub8Bytes
+        : nullptr;
+    store_token(tc, base4, p & 15, base8, e & 15, int8, lane);
+    // the stage holds the step as the cache was before this token.  Key bytes
+    // sit by lane (stage byte 256 (l / 16) + 16 t + l % 16 is subblock byte
+    // 64 t + l), value bytes as in the subblock, params at kStKP / kStVP + 4 t.
+    const int t = c.rp.tn;
+    if (int8) {
+        const int kq = 256 * (lane >> 4) + 16 * t + (lane & 15);
+        const int vq = 2048 + sub_v_byte(t, lane);
+        st[kq] = tc.k8lo;
+        st[kq + 1024] = tc.k8hi;
+        st[vq] = tc.v8lo;
+        st[vq + 1024] = tc.v8hi;
+        if (lane == 0) {
+            *reinterpret_cast<uint32_t *>(st + kStKP + 4 * t) = tc.kp8;
+            *reinterpret_cast<uint32_t *>(st + kStVP + 4 * t) = tc.vp8;
+        }
+    } else {
+        const int sb = t >> 4, tt = t & 15;
+        st[1024 * sb + 256 * (lane >> 4) + 16 * tt + (lane & 15)] = tc.k4;
+        st[2048 + 1024 * sb + sub_v_byte(tt, lane)] = tc.v4;
+        if (lane == 0) {
+            *reinterpret_cast<uint32_t *>(st + kStKP + 4 * t) = tc.kp4;
+            *reinterpret_cast<uint32_t *>(st + kStVP + 4 * t) = tc.vp4;
+        }
+    }
+}
+
 // LDS of one wave: the stage ring, the page half-batches and the query ring
 // (one slot per stage).  The request is padded to 1/kWavesPerCU of a CU's
 // 160 KB: random 2 KB reads from more waves per CU lose HBM efficiency
@@ -968,11 +975,12 @@ __device__ inline void write_piece(const DecodeArgs &a, const SegCtx<GP> &c, con
 // faster than 12).
 constexpr int kWavesPerCU = 8;
 
-template <int GP>
+template <int GP, bool APPEND>
 struct SmemLayout {
     static constexpr int kPages = kStages * kStageBytes;
     static constexpr int kQ = kPages + kPgBytes;
-    static constexpr int kNeed = kQ + kStages * QRing<GP>::kBytes;
+    static constexpr int kKv = kQ + kStages * QRing<GP>::kBytes;
+    static constexpr int kNeed = kKv + (APPEND ? kStages * kKvBytes : 0);
     static constexpr int kPad = 160 * 1024 / kWavesPerCU;
     static constexpr int kRequest = kNeed > kPad ? kNeed : kPad;
 };
@@ -1006,10 +1014,11 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int GP>
+template <int GP, bool APPEND>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SmemLayout<GP>::kRequest];
+    using SL = SmemLayout<GP, APPEND>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SL::kRequest];
     const int lane = threadIdx.x;
     const int64_t wid = blockIdx.x;
 
@@ -1117,8 +1126,9 @@ void decode_split_kernel(DecodeArgs a) {
     Cursor P = start, C = start;
     int issued = 0;
     // page half-batches in LDS: the half of unit hb + j is (hb / 32) & 1
-    uint32_t *pg = reinterpret_cast<uint32_t *>(smem + SmemLayout<GP>::kPages);
-    uint8_t *qring = smem + SmemLayout<GP>::kQ;
+    uint32_t *pg = reinterpret_cast<uint32_t *>(smem + SL::kPages);
+    uint8_t *qring = smem + SL::kQ;
+    uint8_t *kvring = smem + SL::kKv;        // fused append: one slot per stage
     BatchCursor bc = {b0, pre0};
     int64_t hb = u_begin;                     // first unit of the producer's current half
     int hcur = 0;                             // its half index
@@ -1159,6 +1169,9 @@ void decode_split_kernel(DecodeArgs a) {
         if (P.u < u_end) {
             const Lookup look = uniform(read_pages(P));
             if (P.r == 0 || P.u == u_begin) issue_query<GP>(a, P.b, P.hk, L, qring + s * QRing<GP>::kBytes);
+            if constexpr (APPEND) {
+                if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + s * kKvBytes, lane);
+            }
             issue_step(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
             cursor_next(a, R, P);
             ++issued;
@@ -1198,7 +1211,11 @@ void decode_split_kernel(DecodeArgs a) {
         wait_vm_steps(issued - i - 1);
         uint8_t *st = smem + (i % kStages) * kStageBytes;
         uint8_t *qs = qring + (i % kStages) * QRing<GP>::kBytes;
+        uint8_t *kvs = kvring + (i % kStages) * kKvBytes;
         const bool int4 = C.r < C.rp.n4;
+        if constexpr (APPEND) {
+            if (C.r == C.rp.rn) append_new_token(a, R, C, kvs, st, lane);
+        }
         const StepRegs<GP> r = read_stage<GP>(st, L);
         QRing<GP> qr;
         if (!open) qr = read_query<GP>(qs, lane);
@@ -1207,6 +1224,9 @@ void decode_split_kernel(DecodeArgs a) {
         wait_lgkm0();
         if (P.u < u_end) {
             if (P.r == 0 || P.u == u_begin) issue_query<GP>(a, P.b, P.hk, L, qs);
+            if constexpr (APPEND) {
+                if (P.r == P.rp.rn) issue_new_token(a, R, P, kvs, lane);
+            }
             issue_step(a, P, uniform(look), st, offK, offV, offP4, offP8, lane);
             cursor_next(a, R, P);
             ++issued;
@@ -1453,16 +1473,20 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     }
 }
 
-template <int GP>
-static const void *split_fn() { return reinterpret_cast<const void *>(&decode_split_kernel<GP>); }
+template <int GP, bool APPEND>
+static const void *split_fn() { return reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND>); }
 
 static int group_class(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
-    switch (group_class(a.g)) {
-        case 4: hipLaunchKernelGGL(decode_split_kernel<4>, dim3(grid), dim3(64), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL(decode_split_kernel<8>, dim3(grid), dim3(64), 0, stream, a); break;
-        default: hipLaunchKernelGGL(decode_split_kernel<16>, dim3(grid), dim3(64), 0, stream, a); break;
+    const bool fused = a.k_new != nullptr;
+    switch (group_class(a.g) + (fused ? 1 : 0)) {
+        case 4: hipLaunchKernelGGL((decode_split_kernel<4, false>), dim3(grid), dim3(64), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((decode_split_kernel<4, true>), dim3(grid), dim3(64), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<8, false>), dim3(grid), dim3(64), 0, stream, a); break;
+        case 9: hipLaunchKernelGGL((decode_split_kernel<8, true>), dim3(grid), dim3(64), 0, stream, a); break;
+        case 16: hipLaunchKernelGGL((decode_split_kernel<16, false>), dim3(grid), dim3(64), 0, stream, a); break;
+        default: hipLaunchKernelGGL((decode_split_kernel<16, true>), dim3(grid), dim3(64), 0, stream, a); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1471,7 +1495,7 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t decode_max_workers(int g, int *out) {
+hipError_t decode_max_workers(int g, bool fused, int *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -1479,7 +1503,9 @@ hipError_t decode_max_workers(int g, int *out) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     int per_cu = 0;
-    const void *fn = group_class(g) == 4 ? split_fn<4>() : (group_class(g) == 8 ? split_fn<8>() : split_fn<16>());
+    const int cls = group_class(g);
+    const void *fn = fused ? (cls == 4 ? split_fn<4, true>() : (cls == 8 ? split_fn<8, true>() : split_fn<16, true>()))
+                           : (cls == 4 ? split_fn<4, false>() : (cls == 8 ? split_fn<8, false>() : split_fn<16, false>()));
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
     if (e != hipSuccess) return e;
     // The split kernel relies on every worker being resident at once (a worker

@@ -10,7 +10,7 @@ import torch
 
 from workloads import Workload, seq_kv, seq_query
 
-from . import QuantKVCache, kv_decode_attn, kv_quant_append
+from . import QuantKVCache, kv_append_decode_attn, kv_decode_attn, kv_quant_append
 
 
 class DeviceWorkload:
@@ -108,6 +108,12 @@ class DeviceWorkload:
     def decode_step(self, stream=None):
         return kv_decode_attn(self.cache, self.q, self.slots, self.block_table, self.ctx_len,
                               out=self.out, lse=self.lse, workspace=self.workspace, stream=stream)
+
+    def fused_step(self, stream=None):
+        """append_step and decode_step in one launch (kv_append_decode_attn)."""
+        return kv_append_decode_attn(self.cache, self.step_k, self.step_v, self.q, self.slots, self.block_table,
+                                     self.ctx_len, out=self.out, lse=self.lse, workspace=self.workspace,
+                                     stream=stream)
 
     # --- inspection helpers (host copies of what the GPU wrote) ----------------
     def int4_subblocks(self, idx: np.ndarray) -> np.ndarray:

@@ -11,6 +11,8 @@
  *                      attends the INT4 region and the INT8 region as disjoint
  *                      sets and merges them by log-sum-exp.
  *
+ * kv_append_decode_attn does both for one new token per row in a single pass.
+ *
  * The method: KV4-RL ("Unlocking Faster Asynchronous Rollouts for RLVR with
  * INT4 KV Cache Quantization"), sections "Key Contributions" item 4 and
  * "Methodology in Plain English"; the block-diagonal Hadamard rotation of keys
@@ -153,8 +155,8 @@ kvq_status kv_quant_append(const kvq_cache *cache,
                            const int32_t *block_table, int32_t bt_stride,
                            const int32_t *len_after, void *stream);
 
-/* Workspace bytes kv_decode_attn needs for B rows and num_q_heads query heads
- * on the current HIP device (0 on bad input). */
+/* Workspace bytes kv_decode_attn and kv_append_decode_attn need for B rows and
+ * num_q_heads query heads on the current HIP device (0 on bad input). */
 size_t kv_decode_attn_workspace_bytes(const kvq_cache *cache, int32_t B, int32_t num_q_heads);
 
 /*
@@ -185,6 +187,36 @@ kvq_status kv_decode_attn(const kvq_cache *cache,
                           const int32_t *ctx_len, int32_t B,
                           float *out, float *lse,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kv_append_decode_attn -- one decode step with the append fused in: every
+ * row b with ctx_len[b] >= 1 first appends its new token (key k[b], value
+ * v[b]) at position ctx_len[b] - 1 of slot[b], quantized exactly as
+ * kv_quant_append does, then attends q[b] over positions [0, ctx_len[b]), in
+ * one pass over the cache (KV4-RL, "Methodology in Plain English": new K/V
+ * vectors are quantized on the fly inside the decode pipeline; "Key
+ * Contributions" item 4 for the attention).
+ *
+ * The cache bytes written and out / lse are the same as those of
+ * kv_quant_append(k, v, slot, pos = ctx_len - 1, T = B, len_after[slot[b]] =
+ * ctx_len[b]) followed by kv_decode_attn on the same stream (out / lse within
+ * float rounding of the split order; bit-identical when both kernels use the
+ * same number of workers).
+ *
+ *   k, v         bf16 [B][num_kv_heads][128] (device): the token each row
+ *                appends; rows with ctx_len == 0 append nothing.
+ *   slot         int32 [B] (device): distinct slots (each row owns its slot).
+ *   block_table  must map position ctx_len[b] - 1 of each row to its page.
+ *   the other arguments are those of kv_decode_attn; the workspace size is
+ *   kv_decode_attn_workspace_bytes(), which covers both entry points.
+ */
+kvq_status kv_append_decode_attn(const kvq_cache *cache,
+                                 const uint16_t *k, const uint16_t *v,
+                                 const uint16_t *q, int32_t num_q_heads,
+                                 const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
+                                 const int32_t *ctx_len, int32_t B,
+                                 float *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *kvq_status_string(kvq_status status);

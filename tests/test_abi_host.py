@@ -91,6 +91,18 @@ def test_decode_argument_checks(lib):
     assert lib.kv_decode_attn(ctypes.byref(d), p, 32, p, p, 4, p, 2, p, None, None, 1 << 30, None) == 4
 
 
+def test_fused_argument_checks(lib):
+    d = _desc(int4_pool=0x1000, int8_pool=0x2000)
+    p = ctypes.c_void_p(0x3000)
+    f = lib.kv_append_decode_attn
+    assert f(ctypes.byref(d), p, p, p, 32, p, p, 4, p, 0, p, None, p, 1 << 30, None) == 0
+    assert f(ctypes.byref(d), p, p, p, 256, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
+    assert f(ctypes.byref(d), None, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 1
+    assert f(ctypes.byref(d), p, None, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 1
+    assert f(ctypes.byref(d), p, p, p, 32, p, p, 4, p, 2, p, None, None, 1 << 30, None) == 4
+    assert f(None, p, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 1
+
+
 def test_status_strings(lib):
     for s in range(6):
         assert lib.kvq_status_string(s)
