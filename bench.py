@@ -1,8 +1,10 @@
 """Benchmark: one decode step of INT4/INT8 KV-cache quantize-append + decode attention.
 
 A step is the whole hot path over one batch: quantize-append of one new token
-per row (kv_quant_append) followed by decode attention over the quantized
-cache (kv_decode_attn).  The workload is the Qwen3-8B-shaped async-rollout
+per row followed by decode attention over the quantized cache.  By default it
+is one fused launch (kv_append_decode_attn); --path two-launch times
+kv_quant_append followed by kv_decode_attn instead (same bytes written, same
+outputs).  The workload is the Qwen3-8B-shaped async-rollout
 batch (256 slots, 32 query / 8 KV heads, Pareto(1.5) lengths from 512 clipped
 at 32K, 16-token pages, h = 128, s = 4, w = 128), with inputs resident in HBM.
 
@@ -103,17 +105,20 @@ def cpu_baseline(wl, dw, budget_s=12.0):
                        f"(oracle quantization of the row + fp64 attention), {t_total:.1f} s, 1 thread")
 
 
+KERNEL_SOURCES = ("decode.hip", "common.h", "quant.h", "lanes.h")
+
+
 def decode_source_hash():
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h"):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "decode_attention_int4_block_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def traffic_from_profile(workload):
-    """HBM bytes per kv_decode_attn launch from the committed FETCH_SIZE / WRITE_SIZE
-    counter runs, or None when they were taken on other kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"kv_decode_attn_{workload}_traffic.json")
+def traffic_from_profile(entry, workload):
+    """HBM bytes per launch of an entry point from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs, or None when they were taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"{entry}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -199,13 +204,20 @@ def measure_variants(torch, cfg, steps, warmup):
             dw.decode_step()
             if ev:
                 ev[2].record()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            dw.cache = copies[i % len(copies)]
+            fev[i][0].record()
+            dw.fused_step()
+            fev[i][1].record()
         torch.cuda.synchronize()
         dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
         app = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+        fus = np.array([e[0].elapsed_time(e[1]) for e in fev]) * 1e3
         us = float(np.median(dec))
         res.append(dict(variant=tag, sink=vcfg.sink, recent=vcfg.recent, had_block=vcfg.had_block,
                         decode_algorithmic_bytes=db["total"], decode_us=round(us, 2),
-                        append_us=round(float(np.median(app)), 2),
+                        append_us=round(float(np.median(app)), 2), fused_us=round(float(np.median(fus)), 2),
                         GBps=round(db["total"] / us / 1e3, 1), hbm_frac=round(db["total"] / us / 1e3 / HBM_PEAK_GBPS, 4)))
         print(f"[bench] variant {tag}: decode {us:.1f} us, {db['total'] / 1e6:.1f} MB", file=sys.stderr, flush=True)
         del dw, copies
@@ -220,6 +232,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_async_256")
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--path", choices=["fused", "two-launch"], default="fused",
+                    help="the timed step: one kv_append_decode_attn launch, or kv_quant_append + kv_decode_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
                     help="also time the protection-budget / rotation variants (s, w, h) on the same lengths")
@@ -257,31 +271,54 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] prefill + {args.layers} cache copies in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    def step(i, ev=None):
+    fused = args.path == "fused"
+
+    def step(i, path=None):
         dw.cache = layers[i % len(layers)]
-        if ev is not None:
-            ev[0].record()
-        dw.append_step()
-        if ev is not None:
-            ev[1].record()
-        dw.decode_step()
-        if ev is not None:
-            ev[2].record()
+        if (path or args.path) == "fused":
+            dw.fused_step()
+        else:
+            dw.append_step()
+            dw.decode_step()
 
     copy_gbps = device_copy_rate(torch, calibration=args.calibration_copy)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region: K steps back to back, HIP events (on the stream the kernels
+    # run on) only at its two ends so that no marker sits between launches
+    stream = torch.cuda.current_stream()
+    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
+    ev_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
+    ev_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    step_gpu_ms = ev_start.elapsed_time(ev_end) / args.steps
+
+    # untimed breakdown passes: each launch of the two-launch path between
+    # events, and the fused launch between events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        dw.cache = layers[i % len(layers)]
+        evs[i][0].record(stream)
+        dw.append_step()
+        evs[i][1].record(stream)
+        dw.decode_step()
+        evs[i][2].record(stream)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        dw.cache = layers[i % len(layers)]
+        fev[i][0].record(stream)
+        dw.fused_step()
+        fev[i][1].record(stream)
+    torch.cuda.synchronize()
     app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    ms_per_step = wall * 1e3 / args.steps
+    fus_ms = np.array([e[0].elapsed_time(e[1]) for e in fev])
 
     db = decode_bytes(wl)
     ab = append_bytes(wl)
@@ -289,9 +326,18 @@ def main():
     step_s = ms_per_step / 1e3
     value = db["kv"] / step_s / 1e9
     dec_avg_s = float(dec_ms.mean()) / 1e3
-    achieved = db["total"] / dec_avg_s / 1e9
-
-    traffic = traffic_from_profile(cfg.name)
+    if fused:
+        # the fused launch moves the decode bytes and the append bytes; its
+        # duration is the timed region's event span per step
+        kernel = "kv_append_decode_attn (decode_split_kernel<fused> + decode_combine_kernel)"
+        alg_bytes = db["total"] + ab
+        achieved = alg_bytes / (step_gpu_ms / 1e3) / 1e9
+        traffic = traffic_from_profile("kv_append_decode_attn", cfg.name)
+    else:
+        kernel = "kv_decode_attn (decode_split_kernel + decode_combine_kernel)"
+        alg_bytes = db["total"]
+        achieved = alg_bytes / dec_avg_s / 1e9
+        traffic = traffic_from_profile("kv_decode_attn", cfg.name)
 
     rec = {
         "metric": METRIC,
@@ -313,8 +359,13 @@ def main():
             "lengths": f"{cfg.lengths}{tuple(cfg.length_args)}", "total_tokens": int(wl.lengths.sum()),
             "rotating_cache_copies": args.layers,
         },
+        "path": args.path,
         "tokens_heads_per_s": round(tok_heads / step_s, 1),
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "step_gpu_us": round(step_gpu_ms * 1e3, 2),
+        "fused_us": round(float(fus_ms.mean()) * 1e3, 2),
+        "fused_us_p10_p90": [round(float(np.percentile(fus_ms, 10)) * 1e3, 2),
+                             round(float(np.percentile(fus_ms, 90)) * 1e3, 2)],
         "decode_us": round(float(dec_ms.mean()) * 1e3, 2),
         "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                               round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
@@ -326,7 +377,8 @@ def main():
         "device_copy_GBps_context": copy_gbps,
         "roofline": {
             "bound": "hbm",
-            "kernel": "kv_decode_attn (decode_split_kernel + decode_combine_kernel)",
+            "kernel": kernel,
+            "algorithmic_bytes_per_launch": alg_bytes,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
