@@ -111,6 +111,33 @@ def attend_regions(q_bits, cache: SeqCache):
     return merge([s4, s8])
 
 
+def prefill_attend(q_rows_bits, cache: SeqCache):
+    """Causal attention of the last T positions of a sequence over its quantized cache.
+
+    KV4-RL, "Future Directions": rollouts are re-prefilled after each policy
+    update; "Methodology in Plain English": attention reads the quantized
+    cache with the rotated query.  Reading: query row t of q_rows_bits [T, Hq, d]
+    sits at position p = L - T + t and attends positions [0, p], each key and
+    value taken as the cache holds it at length L (the INT8 copy for the
+    positions of the INT8 region at length L, the INT4 codes elsewhere).  The
+    last row is decode attention at length L.
+
+    Returns (out [T, Hq, d], lse [T, Hq]).
+    """
+    q_rows_bits = np.asarray(q_rows_bits, dtype=np.uint16)
+    T = q_rows_bits.shape[0]
+    if not 1 <= T <= cache.L:
+        raise ValueError(f"T = {T} rows do not fit a context of {cache.L}")
+    K, V = dequantized_kv(cache)
+    Hq, d = q_rows_bits.shape[1], q_rows_bits.shape[2]
+    out = np.zeros((T, Hq, d))
+    lse = np.zeros((T, Hq))
+    for t in range(T):
+        p = cache.L - T + t
+        out[t], lse[t] = softmax_attention(rotated_query(q_rows_bits[t], cache.h), K[:p + 1], V[:p + 1])
+    return out, lse
+
+
 def decode_reference(q_bits, k_bits, v_bits, h: int, s: int, w: int):
     """Quantize a sequence from raw bf16 K/V and attend with one query row."""
     return attend(q_bits, quantize_sequence(k_bits, v_bits, h, s, w))

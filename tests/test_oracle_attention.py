@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.attention import (attend, attend_regions, merge, region_stats,
+from oracle.attention import (attend, attend_regions, merge, prefill_attend, region_stats,
                               rotated_query, softmax_attention, unquantized_attention)
 from oracle.cache import dequantized_kv, quantize_sequence
 from oracle.hadamard import rotate_f64
@@ -141,3 +141,67 @@ def test_quantized_attention_error_vs_unquantized_is_reported(tiny):
     # the rotated-basis scores equal the unrotated ones: rotation alone changes nothing
     qr = rotated_query(q, c.had_block)
     assert qr.shape == (8, 128)
+
+
+# ---- causal multi-row attention over the quantized cache (prefill) ----------
+
+def _small_cache(L, H=2, h=16, s=2, w=5, seed=3):
+    rng = np.random.default_rng(seed)
+    k = torch.from_numpy(rng.standard_normal((L, H, 128)) * 2).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((L, H, 128))).to(torch.bfloat16)
+    return quantize_sequence(bf16_bits(k), bf16_bits(v), h, s, w)
+
+
+def _rows(T, Hq, seed=4):
+    rng = np.random.default_rng(seed)
+    return bf16_bits(torch.from_numpy(rng.standard_normal((T, Hq, 128))).to(torch.bfloat16))
+
+
+def test_prefill_last_row_is_decode_attention():
+    cache = _small_cache(37)
+    q = _rows(6, 4)
+    out, lse = prefill_attend(q, cache)
+    d_out, d_lse = attend(q[-1], cache)
+    assert np.array_equal(out[-1], d_out) and np.array_equal(lse[-1], d_lse)
+
+
+def test_prefill_rows_match_brute_force():
+    """Pure-Python causal softmax per row over the dequantized cache."""
+    cache = _small_cache(11, H=1, h=4, s=1, w=3)
+    q = _rows(4, 2)
+    out, _ = prefill_attend(q, cache)
+    K, V = dequantized_kv(cache)
+    for t in range(4):
+        p = cache.L - 4 + t
+        qr = rotated_query(q[t], cache.h)
+        ref = _brute(qr.tolist(), K[:p + 1].tolist(), V[:p + 1].tolist())
+        assert np.allclose(out[t], ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_matches_torch_causal_sdpa_fp64():
+    """Library routine: fp64 scaled_dot_product_attention with the causal mask of
+    rows at positions L - T .. L - 1 over keys 0 .. L - 1."""
+    L, T, Hq, Hkv = 70, 20, 8, 2
+    cache = _small_cache(L, H=Hkv, h=128, s=4, w=16)
+    q = _rows(T, Hq)
+    out, _ = prefill_attend(q, cache)
+    K, V = dequantized_kv(cache)
+    qr = np.stack([rotated_query(q[t], cache.h) for t in range(T)])      # [T, Hq, d]
+    g = Hq // Hkv
+    tq = torch.from_numpy(qr).permute(1, 0, 2)                              # [Hq, T, d]
+    tk = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(g, 0)       # [Hq, L, d]
+    tv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(g, 0)
+    mask = torch.arange(L)[None, :] <= (L - T + torch.arange(T))[:, None]   # [T, L]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_prefill_of_a_whole_sequence_starts_with_the_first_value():
+    """T = L: row 0 sees only position 0, so its output is the dequantized v_0."""
+    cache = _small_cache(9, H=2, h=8, s=1, w=2)
+    q = _rows(9, 4)
+    out, lse = prefill_attend(q, cache)
+    _, V = dequantized_kv(cache)
+    assert np.array_equal(out[0], np.repeat(V[0], 2, axis=0))
+    with pytest.raises(ValueError):
+        prefill_attend(_rows(10, 4), cache)
