@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import KvqCache, KvqError
 
-__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_append_decode_attn", "KvqError"]
+__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_append_decode_attn", "kv_prefill_attn",
+           "KvqError"]
 
 
 def _ptr(t):
@@ -135,4 +136,32 @@ def kv_append_decode_attn(cache: QuantKVCache, k, v, q, slot, block_table, ctx_l
                                          _ptr(block_table), block_table.shape[1], _ptr(ctx_len), B, _ptr(out),
                                          _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "kv_append_decode_attn")
+    return out, lse
+
+
+def kv_prefill_attn(cache: QuantKVCache, q, q_start, slot, block_table, ctx_len, max_rows: int, out=None, lse=None,
+                    stream=None):
+    """Causal attention of chunks of query rows over the quantized cache.
+
+    q [N, H_q, 128] bf16; rows of sequence b are q_start[b] .. q_start[b + 1] - 1
+    (q_start int32 [B + 1] on the device) at positions ctx_len[b] - T_b .. ctx_len[b] - 1.
+    max_rows bounds every T_b.  Returns (out fp32 [N, H_q, 128], lse [N, H_q]).
+    """
+    _dev_bf16(q, "q")
+    N, Hq, d = q.shape
+    _dev_i32(q_start, "q_start")
+    _dev_i32(slot, "slot")
+    _dev_i32(block_table, "block_table")
+    _dev_i32(ctx_len, "ctx_len")
+    B = slot.numel()
+    if ctx_len.numel() != B or q_start.numel() != B + 1:
+        raise ValueError("slot and ctx_len need one entry per sequence, q_start B + 1")
+    if out is None:
+        out = torch.empty((N, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    st = cache.lib.kv_prefill_attn(ctypes.byref(cache.desc), _ptr(q), Hq, _ptr(q_start), int(max_rows), _ptr(slot),
+                                   _ptr(block_table), block_table.shape[1], _ptr(ctx_len), B, _ptr(out), _ptr(lse),
+                                   _stream(stream))
+    _lib.check(st, "kv_prefill_attn")
     return out, lse

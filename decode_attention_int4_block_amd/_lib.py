@@ -39,6 +39,8 @@ SIGNATURES = {
                                c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "kv_append_decode_attn": (c_i32, [ctypes.POINTER(KvqCache), c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
                                       c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "kv_prefill_attn": (c_i32, [ctypes.POINTER(KvqCache), c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp,
+                                c_i32, c_vp, c_vp, c_vp]),
     "kvq_status_string": (ctypes.c_char_p, [c_i32]),
     "kvq_last_error": (ctypes.c_char_p, []),
 }

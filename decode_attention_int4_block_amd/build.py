@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["api.hip", "append.hip", "decode.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

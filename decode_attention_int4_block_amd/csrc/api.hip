@@ -253,6 +253,54 @@ kvq_status kv_append_decode_attn(const kvq_cache *c, const uint16_t *k, const ui
                          workspace_bytes, stream);
 }
 
+kvq_status kv_prefill_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads, const int32_t *q_start,
+                           int32_t max_rows, const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
+                           const int32_t *ctx_len, int32_t B, float *out, float *lse, void *stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (B < 0 || max_rows < 0) return fail(KVQ_ERR_SHAPE, "B = %d, max_rows = %d: negative", B, max_rows);
+    if (num_q_heads < 1 || num_q_heads % c->num_kv_heads)
+        return fail(KVQ_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, c->num_kv_heads);
+    const int g = num_q_heads / c->num_kv_heads;
+    if (g > 16) return fail(KVQ_ERR_UNSUPPORTED, "query group %d > 16", g);
+    if (B == 0 || max_rows == 0) return ok();
+    if (B > 65535 || c->num_kv_heads > 65535) return fail(KVQ_ERR_SHAPE, "B or num_kv_heads above 65535");
+    if (!q || !q_start || !slot || !block_table || !ctx_len || !out)
+        return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
+    if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
+    if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
+    if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+    kvq::PrefillArgs a;
+    a.q = q;
+    a.Hq = num_q_heads;
+    a.g = g;
+    a.R = 16 / g;
+    a.q_start = q_start;
+    a.slot = slot;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.ctx_len = ctx_len;
+    a.B = B;
+    a.int4_pool = static_cast<const uint8_t *>(c->int4_pool);
+    a.int8_pool = static_cast<const uint8_t *>(c->int8_pool);
+    a.H = c->num_kv_heads;
+    a.P = c->page_size;
+    a.logP = __builtin_ctz((unsigned)c->page_size);
+    a.h = c->had_block;
+    a.s = c->sink;
+    a.w = c->recent;
+    a.nr8 = nr8_of(c);
+    a.inv_sqrt_h = inv_sqrt(c->had_block);
+    a.out = out;
+    a.lse = lse;
+    const int64_t tiles = ((int64_t)max_rows + a.R - 1) / a.R;
+    if (tiles > 0x7FFFFFFF) return fail(KVQ_ERR_SHAPE, "max_rows too large");
+    hipError_t e = kvq::launch_prefill(a, (int)tiles, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char *kvq_status_string(kvq_status s) {
     switch (s) {
         case KVQ_OK: return "ok";

@@ -191,7 +191,26 @@ struct DecodeArgs {
     float *lse;
 };
 
+// Causal multi-row attention over the quantized cache (prefill).
+struct PrefillArgs {
+    const uint16_t *q;          // [N][Hq][128] bf16 query rows
+    int32_t Hq, g, R;           // query heads, group size, rows per tile (R g <= 16)
+    const int32_t *q_start;     // [B + 1] first query row of each sequence
+    const int32_t *slot;
+    const int32_t *block_table;
+    int32_t bt_stride;
+    const int32_t *ctx_len;
+    int32_t B;
+    const uint8_t *int4_pool;
+    const uint8_t *int8_pool;
+    int32_t H, P, logP, h, s, w, nr8;
+    float inv_sqrt_h;
+    float *out;                 // [N][Hq][128]
+    float *lse;                 // [N][Hq] or nullptr
+};
+
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream);
 hipError_t decode_max_workers(int g, bool fused, int *out);
 

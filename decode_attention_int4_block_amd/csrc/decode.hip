@@ -37,24 +37,9 @@
 #include "common.h"
 #include "lanes.h"
 #include "quant.h"
+#include "tiles.h"
 
 namespace kvq {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegInf = -__builtin_inff();
-
-constexpr int kStages = 3;
-constexpr int kStageBytes = 4352;       // 4 x 1 KB codes + 256 B params
-constexpr int kDmaPerStep = 5;
-
-// Stage layout of the params (INT4: tokens 0..31 of the step; INT8: entries 0..15).
-constexpr int kStKP = 4096;             // key (scale, zero) of token t at kStKP + 4 t
-constexpr int kStVP = 4224;             // value (scale, zero) of token t at kStVP + 4 t
 
 // Per group class GP (query heads per hi/lo half of the MFMA columns).
 template <int GP>
@@ -71,63 +56,6 @@ struct GC {
     static constexpr float kTau = kPacked ? 8.0f : 0.0f;
     static constexpr int kHiScale = kPacked ? 256 : 1;
 };
-
-__device__ inline floatx4 mfma16(half8 a, half8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline half8 pack8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
-    u32x4 u = {a0, a1, a2, a3};
-    return __builtin_bit_cast(half8, u);
-}
-
-// f16 pair of (a, b), round to nearest (keeps f16 subnormals: the lo parts
-// of small values live there).
-__device__ inline uint32_t f16x2(float a, float b) {
-    const half2v h = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half2v, w)[0]; }
-__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half2v, w)[1]; }
-
-// hi = f16(a / S, b / S), lo = f16(a - S hi, b - S hi): S hi + lo carries ~21
-// bits of a and b, and lo keeps absolute steps of 2^-24 for small values.
-// lo must be taken against the very f16 values packed into hi: the compiler
-// would otherwise re-derive them from a and b (e.g. by fusing the product that
-// formed a into a single-rounding f16 conversion), and where the two roundings
-// differ, hi + lo misses a by one f16 step of hi.  The empty asm makes the
-// packed word opaque.
-template <int S>
-__device__ inline void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    constexpr float inv = 1.0f / S;
-    hi = f16x2(a * inv, b * inv);
-    uint32_t h = hi;
-    __asm__("" : "+v"(h));
-    lo = f16x2(fmaf(h_lo(h), -(float)S, a), fmaf(h_hi(h), -(float)S, b));
-}
-
-__device__ inline float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
-
-template <typename T>
-__device__ inline T ldg(const void *p) { return *reinterpret_cast<const T *>(p); }
-
-typedef __attribute__((address_space(3))) void *lds_ptr;
-
-// Values every lane holds the same copy of, made visibly wave-uniform so that
-// the loads they index become scalar loads.
-__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ inline int64_t uni64(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Read-only launch inputs (lengths, slots, block table) read through the
-// constant address space so that wave-uniform reads are scalar loads.
-__device__ inline int ldc(const int32_t *p, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
-}
 
 // ---------------------------------------------------------------------------
 // Max / sum over the lanes that hold the same query head in the dense layout
@@ -165,34 +93,6 @@ __device__ inline uint32_t gather_slot(uint32_t hi, uint32_t lo) {
     }
 }
 
-// 16 bytes per lane from global memory (uniform base + per-lane offset) into
-// LDS at dst + 16 * lane.
-__device__ inline void dma16(const uint8_t *base, uint32_t off, uint8_t *dst_lds) {
-    __builtin_amdgcn_global_load_lds(base + off, (lds_ptr)dst_lds, 16, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-#define KVQ_VMCNT(n) (((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-#define KVQ_LGKM0 ((0xF) | (0x3 << 14) | (0x7 << 4))
-// The waitcnt intrinsic does not order memory accesses at the IR level; the
-// empty asm with a memory clobber keeps LDS reads of a stage below its wait.
-#define KVQ_FENCE() __asm__ volatile("" ::: "memory")
-
-__device__ inline void wait_vm_steps(int steps_after) {
-    // outstanding DMA instructions allowed = kDmaPerStep * steps_after
-    static_assert(kStages <= 4 && kDmaPerStep == 5, "wait table covers up to 4 stages x 5 loads");
-    if (steps_after <= 0) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(0));
-    else if (steps_after == 1 || kStages == 2) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(5));
-    else if (steps_after == 2 || kStages == 3) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(10));
-    else __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(15));
-    KVQ_FENCE();
-}
-
-__device__ inline void wait_lgkm0() {
-    __builtin_amdgcn_s_waitcnt(KVQ_LGKM0);
-    KVQ_FENCE();
-}
 
 // ---------------------------------------------------------------------------
 // Dense layout.  Lane (G, c) of a step holds kNP pairs of scores of head
@@ -537,10 +437,6 @@ __device__ inline void spread(const float s[8], float d[GC<GP>::kNE]) {
     }
 }
 
-// score (log2 units / K1) of one token from its raw code dot product d
-__device__ inline float tscore(float d, uint32_t kp, float Rh) {
-    return fmaf(d, h_lo(kp), h_hi(kp) * Rh);
-}
 
 // Online-softmax update on the dense scores t (-inf where invalid, with the
 // value params of invalid tokens zeroed); returns the value MFMA A operand(s):
@@ -635,7 +531,6 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
     }
 }
 
-__device__ inline uint32_t lds32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
 template <int GP>
 __device__ inline StepRegs<GP> read_stage(const uint8_t *st, const LaneCtx<GP> &L) {

@@ -11,7 +11,8 @@
  *                      attends the INT4 region and the INT8 region as disjoint
  *                      sets and merges them by log-sum-exp.
  *
- * kv_append_decode_attn does both for one new token per row in a single pass.
+ * kv_append_decode_attn does both for one new token per row in a single pass;
+ * kv_prefill_attn attends a chunk of causal query rows per sequence.
  *
  * The method: KV4-RL ("Unlocking Faster Asynchronous Rollouts for RLVR with
  * INT4 KV Cache Quantization"), sections "Key Contributions" item 4 and
@@ -217,6 +218,40 @@ kvq_status kv_append_decode_attn(const kvq_cache *cache,
                                  const int32_t *ctx_len, int32_t B,
                                  float *out, float *lse,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kv_prefill_attn -- causal attention of a chunk of query rows per sequence
+ * over the quantized cache: chunked prefill, or the re-prefill of in-flight
+ * rollouts after a policy update (KV4-RL, "Future Directions"), reading the
+ * packed codes with the rotated query as decode attention does (KV4-RL,
+ * "Methodology in Plain English").
+ *
+ *   q            bf16 [N][num_q_heads][128] (device), unrotated; rows of
+ *                sequence b are q_start[b] .. q_start[b + 1] - 1.
+ *   q_start      int32 [B + 1] (device), non-decreasing, q_start[0] = 0,
+ *                q_start[B] = N.  T_b = q_start[b + 1] - q_start[b] must satisfy
+ *                T_b <= max_rows and T_b <= ctx_len[b].
+ *   max_rows     host int: an upper bound on every T_b (sizes the launch).
+ *   slot, block_table, bt_stride, ctx_len, B: as for kv_decode_attn.  ctx_len
+ *                counts the chunk, whose keys/values must already be in the
+ *                cache (kv_quant_append with len_after = ctx_len).
+ *   out          fp32 [N][num_q_heads][128] (device): row t of sequence b sits
+ *                at position p = ctx_len[b] - T_b + t and gets
+ *                softmax(q.k / sqrt(128)) v over positions [0, p], each key and
+ *                value as the cache holds it at length ctx_len[b] (the INT8
+ *                copy for the sinks and the last `recent` positions, INT4
+ *                elsewhere).  Its last row equals kv_decode_attn's output.
+ *   lse          fp32 [N][num_q_heads] (device) or NULL.
+ *
+ * No workspace.  Returns KVQ_OK without launching when B == 0 or max_rows == 0.
+ * B and num_kv_heads must not exceed 65535.
+ */
+kvq_status kv_prefill_attn(const kvq_cache *cache,
+                           const uint16_t *q, int32_t num_q_heads,
+                           const int32_t *q_start, int32_t max_rows,
+                           const int32_t *slot, const int32_t *block_table, int32_t bt_stride,
+                           const int32_t *ctx_len, int32_t B,
+                           float *out, float *lse, void *stream);
 
 /* Static description of a status code. */
 const char *kvq_status_string(kvq_status status);

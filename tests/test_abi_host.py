@@ -103,6 +103,21 @@ def test_fused_argument_checks(lib):
     assert f(None, p, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 1
 
 
+def test_prefill_argument_checks(lib):
+    d = _desc(int4_pool=0x1000, int8_pool=0x2000)
+    p = ctypes.c_void_p(0x3000)
+    f = lib.kv_prefill_attn
+    assert f(ctypes.byref(d), p, 32, p, 0, p, p, 4, p, 2, p, None, None) == 0      # max_rows 0: nothing to do
+    assert f(ctypes.byref(d), p, 32, p, 8, p, p, 4, p, 0, p, None, None) == 0      # B 0
+    assert f(ctypes.byref(d), p, 32, p, -1, p, p, 4, p, 2, p, None, None) == 2
+    assert f(ctypes.byref(d), p, 256, p, 8, p, p, 4, p, 2, p, None, None) == 3
+    assert f(ctypes.byref(d), p, 12, p, 8, p, p, 4, p, 2, p, None, None) == 2
+    assert f(ctypes.byref(d), p, 32, None, 8, p, p, 4, p, 2, p, None, None) == 1
+    assert f(ctypes.byref(d), p, 32, p, 8, p, p, 0, p, 2, p, None, None) == 2
+    assert f(ctypes.byref(d), p, 32, p, 8, p, p, 4, p, 70000, p, None, None) == 2
+    assert f(None, p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 1
+
+
 def test_status_strings(lib):
     for s in range(6):
         assert lib.kvq_status_string(s)
