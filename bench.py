@@ -105,7 +105,8 @@ def cpu_baseline(wl, dw, budget_s=12.0):
                        f"(oracle quantization of the row + fp64 attention), {t_total:.1f} s, 1 thread")
 
 
-KERNEL_SOURCES = ("decode.hip", "common.h", "quant.h", "lanes.h")
+KERNEL_SOURCES = ("decode.hip", "common.h", "quant.h", "lanes.h", "tiles.h")
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 
 
 def decode_source_hash():
@@ -225,6 +226,67 @@ def measure_variants(torch, cfg, steps, warmup):
     return res
 
 
+PREFILL_WORKLOAD = "prefill_qwen3_8b_8x1024"
+
+
+def measure_prefill(torch, steps, warmup):
+    """kv_prefill_attn on the re-prefill workload: the last `chunk` positions of each
+    sequence attended again as causal query rows over the quantized cache."""
+    from decode_attention_int4_block_amd import kv_prefill_attn
+    from decode_attention_int4_block_amd.harness import DeviceWorkload
+    from workloads import build_workload, chunk_queries, get_config
+
+    cfg = get_config(PREFILL_WORKLOAD)
+    wl = build_workload(cfg)
+    dw = DeviceWorkload(wl, device="cuda", gen_device="cuda")
+    dw.prefill(include_step_token=True)
+    L = wl.lengths.astype(np.int64)
+    T = np.minimum(cfg.extra["chunk"], L)
+    q = chunk_queries(wl, T, device="cuda")
+    q_start = torch.from_numpy(np.concatenate([[0], np.cumsum(T)]).astype(np.int32)).cuda()
+    out = torch.empty((int(T.sum()), cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((int(T.sum()), cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        kv_prefill_attn(dw.cache, q, q_start, dw.slots, dw.block_table, dw.ctx_len, int(T.max()), out=out, lse=lse)
+
+    for _ in range(warmup):
+        launch()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    # algorithmic work: 2 * 128 flop for q.k and 2 * 128 for p.v per (row, query head, attended key)
+    attended = sum(int((L[b] - T[b] + np.arange(1, T[b] + 1)).sum()) for b in range(cfg.batch))
+    flops = attended * cfg.num_q_heads * 4 * cfg.head_dim
+    # unique cache bytes the chunks' causal prefixes cover (every position up to L)
+    n4, n8 = region_sizes(L, cfg.sink, cfg.recent)
+    kv_unique = int((cfg.num_kv_heads * (BYTES_INT4 * n4 + BYTES_INT8 * n8)).sum())
+    mean_us = float(us.mean())
+    achieved = flops / (mean_us * 1e-6) / 1e12
+    rec = {
+        "workload": cfg.name, "sequences": cfg.batch, "chunk_rows": [int(x) for x in T],
+        "lengths": [int(x) for x in L], "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+        "had_block": cfg.had_block, "sink": cfg.sink, "recent": cfg.recent, "page_size": wl.page_size,
+        "launches": steps, "us_mean": round(mean_us, 2),
+        "us_p10_p90": [round(float(np.percentile(us, 10)), 2), round(float(np.percentile(us, 90)), 2)],
+        "algorithmic_flops": flops, "attended_row_key_pairs_per_q_head": attended,
+        "kv_bytes_unique": kv_unique,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel (kv_prefill_attn)",
+                     "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "note": "fp16 MFMA peak; each product runs as f16 hi + lo, so the MFMAs issue twice the algorithmic flops"},
+    }
+    print(f"[bench] prefill {cfg.name}: {mean_us:.1f} us, {achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    del dw, q, out, lse
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +299,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
                     help="also time the protection-budget / rotation variants (s, w, h) on the same lengths")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the kv_prefill_attn measurement on the re-prefill workload")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="before warm-up, run one untimed 256 MiB device-to-device copy whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the decode kernel's")
@@ -388,6 +452,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, dw)
+    if not args.no_prefill:
+        rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2)
     if args.variants:
         del layers
         dw.cache = None

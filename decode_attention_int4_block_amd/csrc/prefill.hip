@@ -43,25 +43,39 @@ __device__ inline int ring_position(int e, int L, int s, int w) {
     return lo + ((e - s) - (lo - s) % w + w) % w;
 }
 
+// Block-table entries of the two 16-position subblocks of INT4 step r (the
+// second is -1 past the INT4 region); loaded one step ahead of their use.
+struct StepPages {
+    int A, B;
+};
+
+__device__ inline StepPages step_pages(const PrefillArgs &a, const RowPlan &rp, int n4, int slot, int r) {
+    StepPages p = {0, -1};
+    if (r < n4) {
+        const int pos0 = (rp.k0 + r) * 32;
+        const int32_t *bt = a.block_table + (int64_t)slot * a.bt_stride;
+        p.A = ldc(bt, pos0 >> a.logP);
+        if (pos0 + 16 < rp.hi4) p.B = ldc(bt, (pos0 + 16) >> a.logP);
+    }
+    return p;
+}
+
 // 5 direct-to-LDS loads of step r of the tile into stage st (the decode kernel's
 // step copy: key codes gathered by lane, value codes verbatim, params of both
 // halves at kStKP / kStVP + 4 t).
 __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &rp, int n4, int slot, int hk, int r,
-                                          uint8_t *st, uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8,
-                                          int lane) {
+                                          StepPages pg, uint8_t *st, uint32_t offK, uint32_t offV, uint32_t offP4,
+                                          uint32_t offP8, int lane) {
     if (r < n4) {
         const int pos0 = (rp.k0 + r) * 32;
-        const int32_t *bt = a.block_table + (int64_t)slot * a.bt_stride;
         const int subs = a.P >> 4;
-        const int pageA = ldc(bt, pos0 >> a.logP);
         const uint8_t *baseA = a.int4_pool +
-            ((size_t)((int64_t)pageA * a.H + hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSub4Bytes;
+            ((size_t)((int64_t)pg.A * a.H + hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSub4Bytes;
         // subblock B past the INT4 region is never used; re-read A (valid memory)
         const uint8_t *baseB = baseA;
-        if (pos0 + 16 < rp.hi4) {
-            const int pageB = ldc(bt, (pos0 + 16) >> a.logP);
+        if (pg.B >= 0) {
             baseB = a.int4_pool +
-                ((size_t)((int64_t)pageB * a.H + hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSub4Bytes;
+                ((size_t)((int64_t)pg.B * a.H + hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSub4Bytes;
         }
         dma16(baseA + kSub4K, offK, st + 0);
         dma16(baseB + kSub4K, offK, st + 1024);
@@ -80,7 +94,8 @@ __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &r
 
 }  // namespace
 
-__global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x;
     const int b = blockIdx.z, hk = blockIdx.y;
@@ -188,10 +203,12 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int s = 0; s < kStages; ++s) {
         if (s < nsteps) {
-            issue_prefill_step(a, rp, n4, slot, hk, s, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
+            issue_prefill_step(a, rp, n4, slot, hk, s, step_pages(a, rp, n4, slot, s), smem + s * kStageBytes, offK,
+                               offV, offP4, offP8, lane);
             ++issued;
         }
     }
+    StepPages next = step_pages(a, rp, n4, slot, kStages);    // pages of the producer's next step
 
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
     floatx4 Oh[8], Ol[8];                       // O[col 4G + i][16 t + n], hi (x 256) and lo parts
@@ -212,8 +229,9 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
         const u32x4 vpB = *reinterpret_cast<const u32x4 *>(st + kStVP + 64 + 16 * G);
         wait_lgkm0();
         if (i + kStages < nsteps) {
-            issue_prefill_step(a, rp, n4, slot, hk, i + kStages, st, offK, offV, offP4, offP8, lane);
+            issue_prefill_step(a, rp, n4, slot, hk, i + kStages, next, st, offK, offV, offP4, offP8, lane);
             ++issued;
+            next = step_pages(a, rp, n4, slot, i + kStages + 1);
         }
         const bool int8 = i >= n4;
 
@@ -240,10 +258,15 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
                 for (int j = 0; j < 4; ++j) sA[j] = fmaf(sB[j], 16.0f, sA[j]);   // high-nibble plane
             }
             const int base = int8 ? 16 * (i - n4) : (rp.k0 + i) * 32;
+            // an INT4 step inside the region and at or before the tile's first
+            // row is valid for every column: no per-position tests
+            const bool full = !int8 && base >= rp.lo4 && base + 32 <= min(rp.hi4, pos0 + 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 bool okA, okB;
-                if (int8) {
+                if (full) {
+                    okA = okB = true;
+                } else if (int8) {
                     const int e = base + 4 * G + j;
                     okA = e < rp.n8e && ring_position(e, L, a.s, a.w) <= cpos;
                     okB = false;

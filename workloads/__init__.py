@@ -13,5 +13,6 @@ from .gen import (  # noqa: F401
     build_workload,
     seq_kv,
     seq_query,
+    chunk_queries,
     bf16_bits,
 )

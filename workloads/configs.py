@@ -1,4 +1,4 @@
-"""The five decode workloads, each named by what it is and its sizes.
+"""The five decode workloads and one prefill workload, each named by what it is and its sizes.
 
 Lengths ``L_b`` always count the token appended in the timed decode step.
 Shapes follow the Qwen3-4B / Qwen3-8B / Qwen2.5-3B attention layouts the
@@ -67,6 +67,14 @@ CONFIGS: dict[str, WorkloadConfig] = {
         name="refill_512", batch=512, num_q_heads=32, num_kv_heads=8, head_dim=128,
         lengths="refill", length_args=(1, 32768, 0.2, 63), page_size=16,
         had_block=64, sink=4, recent=128, seed=1004),
+    # Re-prefill of in-flight rollouts after a policy update (KV4-RL, "Future
+    # Directions"): Qwen3-8B heads, 8 sequences of uniform length in [4K, 12K];
+    # the last extra["chunk"] positions of each are attended again as one chunk
+    # of causal query rows over the quantized cache.
+    "prefill_qwen3_8b_8x1024": WorkloadConfig(
+        name="prefill_qwen3_8b_8x1024", batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        lengths="uniform", length_args=(4096, 12288), page_size=16,
+        had_block=128, sink=4, recent=128, seed=1005, extra={"chunk": 1024}),
 }
 
 # Order used when a config is referred to by position.

@@ -48,6 +48,9 @@ def draw_lengths(cfg: WorkloadConfig, rng: np.random.Generator) -> np.ndarray:
         u = 1.0 - rng.random(B)               # (0, 1]
         L = np.floor(xm * u ** (-1.0 / alpha)).astype(np.int64)
         L = np.clip(L, xm, hi)
+    elif cfg.lengths == "uniform":
+        lo, hi = a
+        L = rng.integers(lo, hi + 1, size=B).astype(np.int64)
     elif cfg.lengths == "refill":
         lo, hi, fresh_frac, fresh_max = a
         L = rng.integers(lo, hi + 1, size=B).astype(np.int64)
@@ -163,6 +166,15 @@ def seq_query(wl: Workload, device="cpu") -> torch.Tensor:
     g = _generator(device, cfg.seed * 1_000_003 + 17)
     q = torch.randn((cfg.batch, cfg.num_q_heads, cfg.head_dim), generator=g,
                     device=device, dtype=torch.float32)
+    return q.to(torch.bfloat16)
+
+
+def chunk_queries(wl: Workload, rows, device="cpu") -> torch.Tensor:
+    """Query rows of a prefill chunk per sequence, [sum(rows), H_q, head_dim] bf16, N(0,1)."""
+    cfg = wl.cfg
+    g = _generator(device, cfg.seed * 1_000_003 + 29)
+    n = int(np.sum(rows))
+    q = torch.randn((n, cfg.num_q_heads, cfg.head_dim), generator=g, device=device, dtype=torch.float32)
     return q.to(torch.bfloat16)
 
 
