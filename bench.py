@@ -229,7 +229,41 @@ def measure_variants(torch, cfg, steps, warmup):
 PREFILL_WORKLOAD = "prefill_qwen3_8b_8x1024"
 
 
-def measure_prefill(torch, steps, warmup):
+def prefill_cpu_baseline(wl, q, T, budget_s=6.0):
+    """The oracle's causal multi-row attention on a sample: the last rows of the first
+    sequence's chunk, one at a time until ~budget_s, single-threaded BLAS."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import rotated_query, softmax_attention
+    from oracle.cache import dequantized_kv, quantize_sequence
+    from workloads import bf16_bits, seq_kv
+
+    c = wl.cfg
+    L0, T0 = int(wl.lengths[0]), int(T[0])
+    qb = bf16_bits(q[:T0])
+    with threadpool_limits(limits=1):
+        k, v = seq_kv(wl, 0, device="cpu")
+        t_q = time.perf_counter()
+        cache = quantize_sequence(bf16_bits(k), bf16_bits(v), c.had_block, c.sink, c.recent)
+        K, V = dequantized_kv(cache)
+        t_quant = time.perf_counter() - t_q
+        done, flops, t_att = 0, 0, 0.0
+        for t in range(T0 - 1, -1, -1):
+            p = L0 - T0 + t
+            t0 = time.perf_counter()
+            softmax_attention(rotated_query(qb[t], c.had_block), K[:p + 1], V[:p + 1])
+            t_att += time.perf_counter() - t0
+            done += 1
+            flops += (p + 1) * c.num_q_heads * 4 * c.head_dim
+            if t_att >= budget_s:
+                break
+    return dict(value=round(flops / t_att / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"the last {done} of {T0} chunk rows of sequence 0 (L = {L0}), fp64 attention over "
+                       f"the oracle's dequantized cache, {t_att:.1f} s, 1 thread (quantizing the sequence "
+                       f"took another {t_quant:.1f} s)")
+
+
+def measure_prefill(torch, steps, warmup, cpu=False):
     """kv_prefill_attn on the re-prefill workload: the last `chunk` positions of each
     sequence attended again as causal query rows over the quantized cache."""
     from decode_attention_int4_block_amd import kv_prefill_attn
@@ -281,6 +315,8 @@ def measure_prefill(torch, steps, warmup):
                      "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
                      "note": "fp16 MFMA peak; each product runs as f16 hi + lo, so the MFMAs issue twice the algorithmic flops"},
     }
+    if cpu:
+        rec["cpu_baseline"] = prefill_cpu_baseline(wl, q.cpu(), T)
     print(f"[bench] prefill {cfg.name}: {mean_us:.1f} us, {achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
     del dw, q, out, lse
     torch.cuda.empty_cache()
@@ -453,7 +489,8 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, dw)
     if not args.no_prefill:
-        rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2)
+        rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2,
+                                         cpu=not args.no_cpu_baseline)
     if args.variants:
         del layers
         dw.cache = None
