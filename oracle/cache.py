@@ -15,7 +15,7 @@ import numpy as np
 
 from .hadamard import fwht_f32
 from .numerics import bf16_to_f32
-from .quant import quantize, dequantize, INT4_QMAX, INT8_QMAX
+from .quant import quantize, dequantize, qmax_of, INT8_QMAX
 from .regions import int8_region, ring_entry
 
 
@@ -51,15 +51,21 @@ def rotated_keys_f32(k_bits, h: int) -> np.ndarray:
     return fwht_f32(bf16_to_f32(k_bits), h)
 
 
-def quantize_sequence(k_bits, v_bits, h: int, s: int, w: int) -> SeqCache:
-    """Quantize a whole sequence's keys/values [L, H, d] (bf16 patterns)."""
+def quantize_sequence(k_bits, v_bits, h: int, s: int, w: int, main_bits: int = 4) -> SeqCache:
+    """Quantize a whole sequence's keys/values [L, H, d] (bf16 patterns).
+
+    main_bits is the width of the main cache's codes: 4, or 2 for the sub-4-bit
+    cache under the same INT8 sink / recent protection (KV4-RL, "Future
+    Directions"); the fields k4 / v4 then hold the 2-bit codes.
+    """
     k_bits = np.asarray(k_bits, dtype=np.uint16)
     v_bits = np.asarray(v_bits, dtype=np.uint16)
     L = k_bits.shape[0]
     yk = rotated_keys_f32(k_bits, h)
     yv = bf16_to_f32(v_bits)
-    k4, k4s, k4z = quantize(yk, INT4_QMAX)
-    v4, v4s, v4z = quantize(yv, INT4_QMAX)
+    qm = qmax_of(main_bits)
+    k4, k4s, k4z = quantize(yk, qm)
+    v4, v4s, v4z = quantize(yv, qm)
     pos8 = np.array(int8_region(L, s, w), dtype=np.int64)
     k8, k8s, k8z = quantize(yk[pos8], INT8_QMAX)
     v8, v8s, v8z = quantize(yv[pos8], INT8_QMAX)

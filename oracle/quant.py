@@ -29,6 +29,16 @@ from .numerics import f32_to_f16_bits, f16_bits_to_f32, f16_bits_to_f64
 
 INT4_QMAX = 15
 INT8_QMAX = 255
+# Sub-4-bit main caches (KV4-RL, "Future Directions": 3- or 2-bit caches under the
+# same sink / recent protection): the same affine scheme with 2^bits levels.
+INT2_QMAX = 3
+
+
+def qmax_of(bits: int) -> int:
+    """Largest code of a `bits`-bit affine code."""
+    if bits not in (2, 4, 8):
+        raise ValueError(f"unsupported code width {bits}")
+    return (1 << bits) - 1
 
 
 def quantize(y, qmax: int):
@@ -112,6 +122,20 @@ def unpack_int4(packed) -> np.ndarray:
     out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
     out[..., 0::2] = p & 0x0F
     out[..., 1::2] = p >> 4
+    return out
+
+
+def pack_int2(codes) -> np.ndarray:
+    """Four codes per byte, element 4j + f in bits 2f .. 2f + 1 (canonical byte form)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)).astype(np.uint8)
+
+
+def unpack_int2(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (4 * p.shape[-1],), dtype=np.uint8)
+    for f in range(4):
+        out[..., f::4] = (p >> (2 * f)) & 0x3
     return out
 
 

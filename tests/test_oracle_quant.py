@@ -8,8 +8,8 @@ import pytest
 
 from oracle.hadamard import fwht_f32
 from oracle.numerics import f16_bits_to_f64
-from oracle.quant import (INT4_QMAX, INT8_QMAX, bytes_per_token_head, dequantize,
-                          pack_int4, quantize, tie_near, unpack_int4)
+from oracle.quant import (INT2_QMAX, INT4_QMAX, INT8_QMAX, bytes_per_token_head, dequantize,
+                          pack_int2, pack_int4, qmax_of, quantize, tie_near, unpack_int2, unpack_int4)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -35,7 +35,7 @@ def _brute_nearest(y, scale_h, zero_h, qmax):
     return code
 
 
-@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
 def test_codes_are_nearest_levels(qmax):
     y = fwht_f32(_vectors(3000, 1), 128)
     c, sb, zb = quantize(y, qmax)
@@ -47,7 +47,7 @@ def test_codes_are_nearest_levels(qmax):
     assert not np.any(mism & ~ties), int((mism & ~ties).sum())
 
 
-@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
 def test_scale_and_zero_are_fp16_of_range_and_min(qmax):
     y = _vectors(2000, 2)
     c, sb, zb = quantize(y, qmax)
@@ -60,7 +60,7 @@ def test_scale_and_zero_are_fp16_of_range_and_min(qmax):
     assert np.all(np.abs(z - mn) <= 2.0 ** -11 * np.abs(mn) * 1.0001 + 2.0 ** -25)
 
 
-@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
 def test_round_trip_bound(qmax):
     y = fwht_f32(_vectors(3000, 3), 64)
     c, sb, zb = quantize(y, qmax)
@@ -77,7 +77,7 @@ def test_round_trip_bound(qmax):
     assert np.all(err <= s * 0.5 + slack + 1e-6 * np.abs(y).max(axis=1))
 
 
-@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
 def test_grid_vectors_round_trip_exactly(qmax):
     rng = np.random.default_rng(4)
     n = 200
@@ -95,7 +95,7 @@ def test_grid_vectors_round_trip_exactly(qmax):
     assert np.array_equal(dequantize(c, sb, zb), y.astype(np.float64))
 
 
-@pytest.mark.parametrize("qmax", [INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
 def test_zero_range_guard(qmax):
     y = np.stack([np.full(128, 0.3, np.float32), np.zeros(128, np.float32),
                   np.full(128, -7.25, np.float32)])
@@ -141,3 +141,37 @@ def test_storage_accounting_matches_pages():
     assert per_elem_bits == g["bits_per_element"] == g["code_bits"] + g["param_bits_per_group"] / d
     assert bytes_per_token_head(128, 4) == 136
     assert bytes_per_token_head(128, 8) == 264
+
+
+def test_pack_int2_round_trip_and_bit_order():
+    rng = np.random.default_rng(7)
+    c = rng.integers(0, 4, (40, 128)).astype(np.uint8)
+    p = pack_int2(c)
+    assert p.shape == (40, 32)
+    assert np.array_equal(p[:, 0], c[:, 0] | (c[:, 1] << 2) | (c[:, 2] << 4) | (c[:, 3] << 6))
+    assert np.array_equal(unpack_int2(p), c)
+    # a worked byte: codes 3, 0, 2, 1 -> 0b01_10_00_11
+    assert pack_int2(np.array([3, 0, 2, 1], np.uint8))[0] == 0x63
+
+
+def test_code_widths():
+    assert [qmax_of(b) for b in (2, 4, 8)] == [3, 15, 255]
+    with pytest.raises(ValueError):
+        qmax_of(3)
+    # K+V bytes per (token, head) at 2 bits: 2 * (32 + 4) = 72, i.e. 2.25 bits per element
+    assert bytes_per_token_head(128, 2) == 72
+    assert bytes_per_token_head(128, 2) * 8 / 256 == 2.25
+
+
+def test_int2_cache_keeps_the_int8_protection():
+    """A 2-bit main cache: main codes in [0, 3], the INT8 region's copies unchanged."""
+    import torch
+    from oracle.cache import quantize_sequence
+    from workloads import bf16_bits
+    rng = np.random.default_rng(8)
+    k = bf16_bits(torch.from_numpy(rng.standard_normal((50, 2, 128)) * 3).to(torch.bfloat16))
+    v = bf16_bits(torch.from_numpy(rng.standard_normal((50, 2, 128))).to(torch.bfloat16))
+    c4 = quantize_sequence(k, v, 64, 4, 16)
+    c2 = quantize_sequence(k, v, 64, 4, 16, main_bits=2)
+    assert c2.k4.max() <= 3 and c2.v4.max() <= 3 and c4.k4.max() > 3
+    assert np.array_equal(c2.pos8, c4.pos8) and np.array_equal(c2.k8, c4.k8) and np.array_equal(c2.v8, c4.v8)
