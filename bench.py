@@ -189,7 +189,7 @@ def measure_variants(torch, cfg, steps, warmup):
         if db["total"] < (2 << 30):
             for _ in range(3):
                 c2 = QuantKVCache(vcfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
-                                  vcfg.had_block, vcfg.sink, vcfg.recent)
+                                  vcfg.had_block, vcfg.sink, vcfg.recent, code_bits=vcfg.code_bits)
                 c2.int4_pool.copy_(dw.cache.int4_pool)
                 c2.int8_pool.copy_(dw.cache.int8_pool)
                 copies.append(c2)
@@ -364,7 +364,7 @@ def main():
     from decode_attention_int4_block_amd import QuantKVCache
     for _ in range(args.layers - 1):
         c2 = QuantKVCache(cfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
-                          cfg.had_block, cfg.sink, cfg.recent)
+                          cfg.had_block, cfg.sink, cfg.recent, code_bits=cfg.code_bits)
         c2.int4_pool.copy_(dw.cache.int4_pool)
         c2.int8_pool.copy_(dw.cache.int8_pool)
         layers.append(c2)

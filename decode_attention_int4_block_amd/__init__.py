@@ -45,10 +45,11 @@ class QuantKVCache:
     """Device memory of one INT4 paged cache plus its INT8 side cache."""
 
     def __init__(self, num_kv_heads: int, page_size: int, num_pages: int, num_slots: int,
-                 had_block: int, sink: int, recent: int, device="cuda", head_dim: int = 128):
+                 had_block: int, sink: int, recent: int, device="cuda", head_dim: int = 128, code_bits: int = 4):
         self.lib = _lib.load()
         self.desc = KvqCache(num_kv_heads, head_dim, page_size, num_pages, num_slots,
-                             had_block, sink, recent, None, None)
+                             had_block, sink, recent, None, None, code_bits)
+        self.code_bits = code_bits
         n4 = self.lib.kvq_int4_pool_bytes(ctypes.byref(self.desc))
         n8 = self.lib.kvq_int8_pool_bytes(ctypes.byref(self.desc))
         if n4 == 0 and num_pages > 0:

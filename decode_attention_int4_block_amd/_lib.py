@@ -25,6 +25,7 @@ class KvqCache(ctypes.Structure):
         ("recent", c_i32),
         ("int4_pool", c_vp),
         ("int8_pool", c_vp),
+        ("code_bits", c_i32),
     ]
 
 

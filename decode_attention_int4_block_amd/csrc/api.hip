@@ -37,8 +37,9 @@ constexpr int kMinUnitsPerWorker = 8;
 // {first half, even w}, {first, odd}, {second, even}, {second, odd}.
 constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
 constexpr int kMaxDevices = 64;
-// per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused append)
-std::atomic<int> g_max_workers[kMaxDevices][6];
+// per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused
+// append, attention over the 2-bit cache)
+std::atomic<int> g_max_workers[kMaxDevices][9];
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -54,8 +55,12 @@ kvq_status check_cache(const kvq_cache *c) {
         return fail(KVQ_ERR_SHAPE, "had_block %d is not a power of two in [1, 128]", c->had_block);
     if (c->sink < 0 || c->recent < 0) return fail(KVQ_ERR_SHAPE, "negative sink/recent");
     if ((int64_t)c->sink + c->recent > (1 << 20)) return fail(KVQ_ERR_SHAPE, "sink + recent too large");
+    if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 4)
+        return fail(KVQ_ERR_UNSUPPORTED, "code_bits %d: the main cache holds 4- or 2-bit codes", c->code_bits);
     return KVQ_OK;
 }
+
+int bits_of(const kvq_cache *c) { return c->code_bits == 2 ? 2 : 4; }
 
 int nr8_of(const kvq_cache *c) { return kvq::ceil_div(c->sink + c->recent, kvq::kSub); }
 
@@ -63,14 +68,14 @@ float inv_sqrt(int h) { return (float)(1.0 / sqrt((double)h)); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-kvq_status max_workers(int g, bool fused, int *out) {
+kvq_status max_workers(int g, bool fused, int bits, int *out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
-    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (fused ? 3 : 0);
+    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (bits == 2 ? 6 : (fused ? 3 : 0));
     int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
-        hipError_t e = kvq::decode_max_workers(g, fused, &v);
+        hipError_t e = kvq::decode_max_workers(g, fused, bits, &v);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         g_max_workers[dev][cls].store(v, std::memory_order_relaxed);
     }
@@ -105,7 +110,7 @@ extern "C" {
 
 size_t kvq_int4_pool_bytes(const kvq_cache *c) {
     if (check_cache(c) != KVQ_OK) return 0;
-    return (size_t)c->num_pages * c->num_kv_heads * (c->page_size / kvq::kSub) * kvq::kSub4Bytes;
+    return (size_t)c->num_pages * c->num_kv_heads * (c->page_size / kvq::kSub) * kvq::main_sub_bytes(bits_of(c));
 }
 
 size_t kvq_int8_pool_bytes(const kvq_cache *c) {
@@ -145,6 +150,7 @@ kvq_status kv_quant_append(const kvq_cache *c, const uint16_t *k, const uint16_t
     a.s = c->sink;
     a.w = c->recent;
     a.nr8 = nr8_of(c);
+    a.bits = bits_of(c);
     a.inv_sqrt_h = inv_sqrt(c->had_block);
     hipError_t e = kvq::launch_quant_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "quant-append launch failed: %s", hipGetErrorString(e));
@@ -157,7 +163,10 @@ size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num
     if (g > 16) return 0;
     // large enough for both kernels (attention only and fused append)
     int workers = 0, workers_fused = 0;
-    if (max_workers(g, false, &workers) != KVQ_OK || max_workers(g, true, &workers_fused) != KVQ_OK) return 0;
+    const int bits = bits_of(c);
+    if (max_workers(g, false, bits, &workers) != KVQ_OK) return 0;
+    if (bits == 2) return ws_layout(c, B, g, workers).total;
+    if (max_workers(g, true, bits, &workers_fused) != KVQ_OK) return 0;
     const size_t a = ws_layout(c, B, g, workers).total, b = ws_layout(c, B, g, workers_fused).total;
     return a > b ? a : b;
 }
@@ -187,9 +196,11 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+    if (fused && bits_of(c) != 4)
+        return fail(KVQ_ERR_UNSUPPORTED, "the fused append serves the 4-bit cache only (code_bits %d)", c->code_bits);
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
     int workers = 0;
-    st = max_workers(g, fused, &workers);
+    st = max_workers(g, fused, bits_of(c), &workers);
     if (st != KVQ_OK) return st;
     const WsLayout l = ws_layout(c, B, g, workers);
     if (workspace_bytes < l.total)
@@ -215,6 +226,7 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.s = c->sink;
     a.w = c->recent;
     a.nr8 = nr8_of(c);
+    a.bits = bits_of(c);
     a.inv_sqrt_h = inv_sqrt(c->had_block);
     a.max_workers = workers;
     a.min_units = kMinUnitsPerWorker;
@@ -271,6 +283,8 @@ kvq_status kv_prefill_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+    if (bits_of(c) != 4)
+        return fail(KVQ_ERR_UNSUPPORTED, "prefill attention reads the 4-bit cache only (code_bits %d)", c->code_bits);
     kvq::PrefillArgs a;
     a.q = q;
     a.Hq = num_q_heads;

@@ -13,6 +13,9 @@
 
 namespace kvq {
 
+// BITS: width of the main cache's codes, 4 or 2 (the sub-4-bit cache of KV4-RL,
+// "Future Directions", with the same INT8 sink / recent copies).
+template <int BITS>
 __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -25,13 +28,13 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
     const int page = a.block_table[(int64_t)slot * a.bt_stride + p / a.P];
     const int row = p % a.P;
     uint8_t *base4 = a.int4_pool +
-        ((size_t)((int64_t)page * a.H + hk) * (a.P / kSub) + (row >> 4)) * kSub4Bytes;
+        ((size_t)((int64_t)page * a.H + hk) * (a.P / kSub) + (row >> 4)) * (BITS == 2 ? kSub2Bytes : kSub4Bytes);
 
     const uint16_t *krow = a.k + item * kHeadDim;
     const uint16_t *vrow = a.v + item * kHeadDim;
     const int vd0 = 32 * (lane >> 4) + (lane & 15);
     const TokenCodes tc = quantize_token(reinterpret_cast<const uint32_t *>(krow)[lane], vrow[vd0], vrow[vd0 + 16],
-                                         a.h, a.inv_sqrt_h, lane);
+                                         a.h, a.inv_sqrt_h, lane, BITS == 2 ? 3.0f : 15.0f);
 
     // INT8 side cache: sinks and the final recent window
     const int L_after = a.len_after[slot];
@@ -39,13 +42,21 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
     const int e = p < a.s ? p : (a.w > 0 ? a.s + (p - a.s) % a.w : 0);
     uint8_t *base8 = write8 ? a.int8_pool + ((size_t)((int64_t)slot * a.H + hk) * a.nr8 + (e >> 4)) * kSub8Bytes
                             : nullptr;
-    store_token(tc, base4, row & 15, base8, e & 15, write8, lane);
+    if constexpr (BITS == 2) {
+        store_token_int2(tc, base4, row & 15, lane);
+        if (write8) store_token_int8(tc, base8, e & 15, lane);
+    } else {
+        store_token(tc, base4, row & 15, base8, e & 15, write8, lane);
+    }
 }
 
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream) {
     const int64_t items = (int64_t)a.T * a.H;
     const int64_t blocks = (items + 3) / 4;
-    hipLaunchKernelGGL(quant_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (a.bits == 2)
+        hipLaunchKernelGGL(quant_append_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(quant_append_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

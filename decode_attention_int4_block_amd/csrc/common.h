@@ -26,6 +26,16 @@ constexpr int kSub8VHi = 3072;
 constexpr int kSub8KP = 4096;
 constexpr int kSub8VP = 4160;
 
+// 2-bit subblock (main cache at code_bits = 2): 16 tokens x (32 B key codes +
+// 32 B value codes + 4 + 4 B params); layouts in quant.h (store_token_int2).
+constexpr int kSub2Bytes = 1152;
+constexpr int kSub2K = 0;
+constexpr int kSub2V = 512;
+constexpr int kSub2KP = 1024;
+constexpr int kSub2VP = 1088;
+
+__host__ __device__ inline int main_sub_bytes(int bits) { return bits == 2 ? kSub2Bytes : kSub4Bytes; }
+
 // Workspace of the decode attention: header, per-row cost prefix, partial pieces.
 constexpr int kPieceStride = 132;           // floats per (piece, query head): m, l, 0, 0, acc[128]
 constexpr size_t kWsHeaderBytes = 256;
@@ -161,6 +171,7 @@ struct AppendArgs {
     uint8_t *int4_pool;
     uint8_t *int8_pool;
     int32_t H, P, h, s, w, nr8;
+    int32_t bits;       // main cache code width: 4 or 2
     float inv_sqrt_h;   // fp32 value nearest to 1/sqrt(h)
 };
 
@@ -177,6 +188,7 @@ struct DecodeArgs {
     const uint16_t *k_new;  // [B][H][128] bf16 key / value each row appends at
     const uint16_t *v_new;  //   position ctx_len - 1 (fused append), or nullptr
     int32_t H, P, logP, h, s, w, nr8;
+    int32_t bits;                       // main cache code width: 4 or 2
     float inv_sqrt_h;
     int32_t max_workers, min_units;
     int32_t part_wt[4];                 // worker weights (Partition)
@@ -212,6 +224,6 @@ struct PrefillArgs {
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream);
-hipError_t decode_max_workers(int g, bool fused, int *out);
+hipError_t decode_max_workers(int g, bool fused, int bits, int *out);
 
 }  // namespace kvq

@@ -502,17 +502,36 @@ __device__ inline void softmax_dense(SegCtx<GP> &c, const LaneCtx<GP> &L, const 
 // Producer: issue the 5 direct-to-LDS loads of the step at cursor c into stage
 // st.  Both kinds of step leave key params at stage offset 4096 + 4 t and value
 // params at 4224 + 4 t for token (entry) t.
+//
+// A 2-bit main-cache step copies its two subblocks' 512-byte code areas verbatim
+// (32 lanes x 16 B; they are stored in lane order) to stage offsets 0 / 512
+// (keys) and 1024 / 1536 (values), and its params like an INT4 step.
+template <int BITS>
 __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lookup &k, uint8_t *st,
                                   uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8, int lane) {
     if (c.r < c.rp.n4) {
+        constexpr int kSubBytes = BITS == 2 ? kSub2Bytes : kSub4Bytes;
         const int pos0 = (c.rp.k0 + c.r) * 32;
         const int subs = a.P >> 4;
         const uint8_t *baseA = a.int4_pool +
-            ((size_t)((int64_t)k.pageA * a.H + c.hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSub4Bytes;
+            ((size_t)((int64_t)k.pageA * a.H + c.hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSubBytes;
         // subblock B past the INT4 region is never used; re-read A (valid memory)
         const uint8_t *baseB = (pos0 + 16 < c.rp.hi4)
-            ? a.int4_pool + ((size_t)((int64_t)k.pageB * a.H + c.hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSub4Bytes
+            ? a.int4_pool + ((size_t)((int64_t)k.pageB * a.H + c.hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSubBytes
             : baseA;
+        if constexpr (BITS == 2) {
+            const uint32_t off = 16 * (uint32_t)lane;
+            if (lane < 32) {
+                dma16(baseA + kSub2K, off, st + 0);
+                dma16(baseB + kSub2K, off, st + 512);
+                dma16(baseA + kSub2V, off, st + 1024);
+                dma16(baseB + kSub2V, off, st + 1536);
+            }
+            // params: as for INT4, from the 2-bit subblock's param areas
+            const uint32_t offP2 = offP4 - kSub4KP + kSub2KP;
+            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP2, st + 4096);
+            return;
+        }
         dma16(baseA + kSub4K, offK, st + 0);
         dma16(baseB + kSub4K, offK, st + 1024);
         dma16(baseA + kSub4V, offV, st + 2048);
@@ -532,14 +551,28 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
 }
 
 
-template <int GP>
-__device__ inline StepRegs<GP> read_stage(const uint8_t *st, const LaneCtx<GP> &L) {
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// main2: a 2-bit main-cache step (8 bytes of codes per lane and quarter).
+template <int GP, int BITS>
+__device__ inline StepRegs<GP> read_stage(const uint8_t *st, const LaneCtx<GP> &L, bool main2) {
     StepRegs<GP> r;
     const int lane = L.lane;
-    r.kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
-    r.kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
-    r.vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
-    r.vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
+    if (BITS == 2 && main2) {
+        const u32x2 ka = *reinterpret_cast<const u32x2 *>(st + lane * 8);
+        const u32x2 kb = *reinterpret_cast<const u32x2 *>(st + 512 + lane * 8);
+        const u32x2 va = *reinterpret_cast<const u32x2 *>(st + 1024 + lane * 8);
+        const u32x2 vb = *reinterpret_cast<const u32x2 *>(st + 1536 + lane * 8);
+        r.kA = u32x4{ka[0], ka[1], 0u, 0u};
+        r.kB = u32x4{kb[0], kb[1], 0u, 0u};
+        r.vA = u32x4{va[0], va[1], 0u, 0u};
+        r.vB = u32x4{vb[0], vb[1], 0u, 0u};
+    } else {
+        r.kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
+        r.kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
+        r.vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
+        r.vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
+    }
     const uint8_t *kp = st + L.offKP;
     const uint8_t *vp = st + L.offKP + (kStVP - kStKP);
     if constexpr (GP == 4) {
@@ -597,13 +630,43 @@ struct KAcc {
     floatx4 dA[GC<GP>::kQ], dB[GC<GP>::kQ];
 };
 
-template <int GP>
-__device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r) {
+// 2-bit codes of one dword half-pair as the four f16 subnormal pairs the INT4
+// nibble masks give: field f of bytes 0 and 2 (dims f and 4 + f of a chunk)
+// scaled 1 for even f and 16 for odd f, so that the same query operand (and the
+// same value tile scaling) serves both widths.
+__device__ inline uint32_t int2_field(uint32_t x, int f) {
+    switch (f) {
+        case 0: return x & 0x00030003u;
+        case 1: return (x << 2) & 0x00300030u;
+        case 2: return (x >> 4) & 0x00030003u;
+        default: return (x >> 2) & 0x00300030u;
+    }
+}
+__device__ inline half8 int2_chunk(uint32_t x) {
+    return pack8(int2_field(x, 0), int2_field(x, 1), int2_field(x, 2), int2_field(x, 3));
+}
+
+template <int GP, int BITS>
+__device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r, bool main2) {
     constexpr int kQ = GC<GP>::kQ;
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
     KAcc<GP> k;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) k.dA[q] = k.dB[q] = zero4;
+    if (BITS == 2 && main2) {
+        // chunk i: dword i / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half8 ak = int2_chunk(r.kA[i >> 1] >> (8 * (i & 1)));
+            const half8 bk = int2_chunk(r.kB[i >> 1] >> (8 * (i & 1)));
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
+                k.dB[q] = mfma16(bk, c.q4[q][i], k.dB[q]);
+            }
+        }
+        return k;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t x = r.kA[i], x8 = x >> 8;
@@ -656,7 +719,7 @@ __device__ inline KOut<GP> kpart_tail(const SegCtx<GP> &c, const LaneCtx<GP> &L,
     return k;
 }
 
-template <int GP>
+template <int GP, int BITS>
 __device__ inline void vpart(SegCtx<GP> &c, const LaneCtx<GP> &L, const KOut<GP> &k) {
     constexpr int kQ = GC<GP>::kQ;
     half8 pop[kQ];
@@ -672,6 +735,20 @@ __device__ inline void vpart(SegCtx<GP> &c, const LaneCtx<GP> &L, const KOut<GP>
 #pragma unroll
             for (int j = 0; j < 4; ++j) pop[q][4 + j] = pop[q][4 + j] * wb + pop[q][j] * wa;
         }
+    }
+    if (BITS == 2 && !k.int8) {
+        // 2-bit values: dword cc, field f = dims 16 (4 cc + f) + n, tile 4 cc + f
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const half8 vt = pack8(int2_field(x, f), int2_field(x8, f), int2_field(y, f), int2_field(y8, f));
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) c.O[4 * cc + f] = mfma16(pop[q], vt, c.O[4 * cc + f]);
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -909,7 +986,7 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int GP, bool APPEND>
+template <int GP, bool APPEND, int BITS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a) {
     using SL = SmemLayout<GP, APPEND>;
@@ -1067,7 +1144,7 @@ void decode_split_kernel(DecodeArgs a) {
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + s * kKvBytes, lane);
             }
-            issue_step(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
+            issue_step<BITS>(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
             cursor_next(a, R, P);
             ++issued;
             advance_half(P);
@@ -1111,7 +1188,7 @@ void decode_split_kernel(DecodeArgs a) {
         if constexpr (APPEND) {
             if (C.r == C.rp.rn) append_new_token(a, R, C, kvs, st, lane);
         }
-        const StepRegs<GP> r = read_stage<GP>(st, L);
+        const StepRegs<GP> r = read_stage<GP, BITS>(st, L, int4);
         QRing<GP> qr;
         if (!open) qr = read_query<GP>(qs, lane);
         Lookup look = {0, 0, 0};
@@ -1122,7 +1199,7 @@ void decode_split_kernel(DecodeArgs a) {
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvs, lane);
             }
-            issue_step(a, P, uniform(look), st, offK, offV, offP4, offP8, lane);
+            issue_step<BITS>(a, P, uniform(look), st, offK, offV, offP4, offP8, lane);
             cursor_next(a, R, P);
             ++issued;
             advance_half(P);
@@ -1130,7 +1207,7 @@ void decode_split_kernel(DecodeArgs a) {
         if (!open) {
             // this step starts a segment: finish the previous one first
             if (pend) {
-                vpart<GP>(c, L, kp);
+                vpart<GP, BITS>(c, L, kp);
                 end_segment(E);
                 pend = false;
             }
@@ -1144,8 +1221,8 @@ void decode_split_kernel(DecodeArgs a) {
         const int sbase = int4 ? (C.rp.k0 + C.r) * 32 : e0;
         const int slo = int4 ? C.rp.lo4 : 0;
         const int shi = int4 ? C.rp.hi4 : min(C.rp.n8e, e0 + 16);
-        const KAcc<GP> ka = kpart_mfma<GP>(c, r);
-        if (pend) vpart<GP>(c, L, kp);          // previous step, same segment
+        const KAcc<GP> ka = kpart_mfma<GP, BITS>(c, r, int4);
+        if (pend) vpart<GP, BITS>(c, L, kp);    // previous step, same segment
         kp = kpart_tail<GP>(c, L, r, ka, !int4, sbase, slo, shi);
         pend = true;
         E = C;
@@ -1153,7 +1230,7 @@ void decode_split_kernel(DecodeArgs a) {
         cursor_next(a, R, C);
     }
     if (pend) {
-        vpart<GP>(c, L, kp);
+        vpart<GP, BITS>(c, L, kp);
         end_segment(E);
     }
     if (lane == 0) {
@@ -1368,20 +1445,29 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     }
 }
 
-template <int GP, bool APPEND>
-static const void *split_fn() { return reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND>); }
+template <int GP, bool APPEND, int BITS>
+static const void *split_fn() { return reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS>); }
 
 static int group_class(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
     const bool fused = a.k_new != nullptr;
-    switch (group_class(a.g) + (fused ? 1 : 0)) {
-        case 4: hipLaunchKernelGGL((decode_split_kernel<4, false>), dim3(grid), dim3(64), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((decode_split_kernel<4, true>), dim3(grid), dim3(64), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((decode_split_kernel<8, false>), dim3(grid), dim3(64), 0, stream, a); break;
-        case 9: hipLaunchKernelGGL((decode_split_kernel<8, true>), dim3(grid), dim3(64), 0, stream, a); break;
-        case 16: hipLaunchKernelGGL((decode_split_kernel<16, false>), dim3(grid), dim3(64), 0, stream, a); break;
-        default: hipLaunchKernelGGL((decode_split_kernel<16, true>), dim3(grid), dim3(64), 0, stream, a); break;
+    if (a.bits == 2) {
+        // the fused append is built for the 4-bit cache only (the host rejects it here)
+        switch (group_class(a.g)) {
+            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+        }
+    } else {
+        switch (group_class(a.g) + (fused ? 1 : 0)) {
+            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1390,7 +1476,7 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t decode_max_workers(int g, bool fused, int *out) {
+hipError_t decode_max_workers(int g, bool fused, int bits, int *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -1399,8 +1485,13 @@ hipError_t decode_max_workers(int g, bool fused, int *out) {
     if (e != hipSuccess) return e;
     int per_cu = 0;
     const int cls = group_class(g);
-    const void *fn = fused ? (cls == 4 ? split_fn<4, true>() : (cls == 8 ? split_fn<8, true>() : split_fn<16, true>()))
-                           : (cls == 4 ? split_fn<4, false>() : (cls == 8 ? split_fn<8, false>() : split_fn<16, false>()));
+    const void *fn;
+    if (bits == 2)
+        fn = cls == 4 ? split_fn<4, false, 2>() : (cls == 8 ? split_fn<8, false, 2>() : split_fn<16, false, 2>());
+    else if (fused)
+        fn = cls == 4 ? split_fn<4, true, 4>() : (cls == 8 ? split_fn<8, true, 4>() : split_fn<16, true, 4>());
+    else
+        fn = cls == 4 ? split_fn<4, false, 4>() : (cls == 8 ? split_fn<8, false, 4>() : split_fn<16, false, 4>());
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
     if (e != hipSuccess) return e;
     // The split kernel relies on every worker being resident at once (a worker

@@ -53,16 +53,18 @@ __device__ inline uint32_t qparam_word(const QParams &p) {
 
 // Codes and params of one (token, KV head) in both caches.
 struct TokenCodes {
-    uint8_t k4, v4;             // this lane's INT4 bytes (key dims 2l, 2l+1; value dims n+32c, n+16+32c)
+    uint8_t k4, v4;             // this lane's main-cache codes as a nibble pair (key dims 2l, 2l+1;
+                                // value dims n+32c, n+16+32c): the INT4 byte, or two 2-bit codes
     uint8_t k8lo, k8hi;         // INT8 key codes split into nibble planes
     uint8_t v8lo, v8hi;
     uint32_t kp4, vp4, kp8, vp8; // (scale, zero) fp16 pairs, wave-uniform
 };
 
 // kw: this lane's bf16 pair of key dims 2l, 2l+1; vlo, vhi: its value dims
-// n + 32c and n + 16 + 32c (bf16 bits).
+// n + 32c and n + 16 + 32c (bf16 bits).  qmain: levels - 1 of the main cache
+// (15, or 3 for the 2-bit cache).
 __device__ inline TokenCodes quantize_token(uint32_t kw, uint32_t vlo, uint32_t vhi, int h, float inv_sqrt_h,
-                                            int lane) {
+                                            int lane, float qmain = 15.0f) {
 #pragma clang fp contract(off)
     // ---- keys: fp32 block Hadamard, strides 1, 2, ..., h/2 ascending --------
     float x0 = bf16_to_f32(kw & 0xFFFFu);
@@ -91,10 +93,10 @@ __device__ inline TokenCodes quantize_token(uint32_t kw, uint32_t vlo, uint32_t 
     const float vmx = wave_max(fmaxf(v0, v1));
     TokenCodes t;
     {
-        const QParams kp = qparams(kmn, kmx, 15.0f);
-        const QParams vp = qparams(vmn, vmx, 15.0f);
-        t.k4 = (uint8_t)(qcode(x0, kp, 15.0f) | (qcode(x1, kp, 15.0f) << 4));
-        t.v4 = (uint8_t)(qcode(v0, vp, 15.0f) | (qcode(v1, vp, 15.0f) << 4));
+        const QParams kp = qparams(kmn, kmx, qmain);
+        const QParams vp = qparams(vmn, vmx, qmain);
+        t.k4 = (uint8_t)(qcode(x0, kp, qmain) | (qcode(x1, kp, qmain) << 4));
+        t.v4 = (uint8_t)(qcode(v0, vp, qmain) | (qcode(v1, vp, qmain) << 4));
         t.kp4 = qparam_word(kp);
         t.vp4 = qparam_word(vp);
     }
@@ -119,6 +121,54 @@ __device__ inline int sub_k_byte(int tok, int lane) { return tok * 64 + lane; }
 __device__ inline int sub_v_byte(int tok, int lane) {
     const int G = tok >> 2, r = tok & 3, vn = lane & 15, vc = lane >> 4;
     return 4 * ((G * 16 + vn) * 4 + vc) + r;
+}
+
+// 2-bit main cache.  Key codes of token t: 8 bytes at (G 16 + t) 8 for dims
+// 32 G .. 32 G + 31; within dword w (dims 32 G + 16 w + j, j < 16) byte
+// {0, 2, 1, 3}[j / 4] holds dim j in bits 2 (j % 4).  Value codes: dword
+// (G 16 + n) 2 + cc of the value area, byte r = token 4 G + r, bits 2 f =
+// dim n + 16 f + 64 cc.  A byte holds four codes, two from each of two lanes:
+// the key byte of lanes l and l ^ 1, the value byte of lanes l and l ^ 16.
+__device__ inline int sub2_k_byte(int tok, int lane) {
+    const int q = ((2 * lane) & 15) >> 2;        // dims 2l, 2l+1 sit at 4 q + (0, 1) or (2, 3) of their dword
+    return ((lane >> 4) * 16 + tok) * 8 + (((lane & 15) >> 3) << 2) + (((q & 1) << 1) | (q >> 1));
+}
+__device__ inline int sub2_v_byte(int tok, int lane) {
+    const int G = tok >> 2, r = tok & 3, n = lane & 15, c = lane >> 4;
+    return ((G * 16 + n) * 2 + (c >> 1)) * 4 + r;
+}
+// The byte this lane's pair of codes completes (valid in the lanes that store it).
+__device__ inline uint32_t int2_key_byte(uint8_t nib2, int lane) {
+    const uint32_t mine = ((nib2 & 3u) | (((uint32_t)nib2 >> 4) << 2)) << (4 * (lane & 1));
+    return mine | (uint32_t)__shfl_xor((int)mine, 1, 64);
+}
+__device__ inline uint32_t int2_value_byte(uint8_t nib2, int lane) {
+    const uint32_t mine = ((nib2 & 3u) | (((uint32_t)nib2 >> 4) << 2)) << (4 * ((lane >> 4) & 1));
+    return mine | (uint32_t)__shfl_xor((int)mine, 16, 64);
+}
+
+// Stores of one token into a 2-bit subblock.  Call with the whole wave.
+__device__ inline void store_token_int2(const TokenCodes &t, uint8_t *base2, int tok, int lane) {
+    const uint32_t kb = int2_key_byte(t.k4, lane);
+    const uint32_t vb = int2_value_byte(t.v4, lane);
+    if ((lane & 1) == 0) base2[kSub2K + sub2_k_byte(tok, lane)] = (uint8_t)kb;
+    if (((lane >> 4) & 1) == 0) base2[kSub2V + sub2_v_byte(tok, lane)] = (uint8_t)vb;
+    if (lane == 0) {
+        *reinterpret_cast<uint32_t *>(base2 + kSub2KP + 4 * tok) = t.kp4;
+        *reinterpret_cast<uint32_t *>(base2 + kSub2VP + 4 * tok) = t.vp4;
+    }
+}
+
+// INT8 ring copy of one token (when write8).
+__device__ inline void store_token_int8(const TokenCodes &t, uint8_t *base8, int ee, int lane) {
+    base8[kSub8KLo + sub_k_byte(ee, lane)] = t.k8lo;
+    base8[kSub8KHi + sub_k_byte(ee, lane)] = t.k8hi;
+    base8[kSub8VLo + sub_v_byte(ee, lane)] = t.v8lo;
+    base8[kSub8VHi + sub_v_byte(ee, lane)] = t.v8hi;
+    if (lane == 0) {
+        *reinterpret_cast<uint32_t *>(base8 + kSub8KP + 4 * ee) = t.kp8;
+        *reinterpret_cast<uint32_t *>(base8 + kSub8VP + 4 * ee) = t.vp8;
+    }
 }
 
 // Stores of one token into an INT4 subblock and (when write8) an INT8 ring subblock.

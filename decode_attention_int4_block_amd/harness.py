@@ -29,7 +29,7 @@ class DeviceWorkload:
         B = cfg.batch
         self.B = B
         self.cache = QuantKVCache(cfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
-                                  cfg.had_block, cfg.sink, cfg.recent, device=self.device)
+                                  cfg.had_block, cfg.sink, cfg.recent, device=self.device, code_bits=cfg.code_bits)
         self.block_table = torch.from_numpy(wl.block_table).to(self.device)
         self.slots = torch.from_numpy(wl.slots.astype(np.int32)).to(self.device)
         self.lengths = wl.lengths.astype(np.int64)
@@ -117,10 +117,12 @@ class DeviceWorkload:
 
     # --- inspection helpers (host copies of what the GPU wrote) ----------------
     def int4_subblocks(self, idx: np.ndarray) -> np.ndarray:
-        from .layout import SUB4_BYTES
-        pool = self.cache.int4_pool[: (self.cache.int4_pool.numel() // SUB4_BYTES) * SUB4_BYTES]
+        """Main-cache subblocks (INT4, or 2-bit when the cache holds 2-bit codes)."""
+        from .layout import SUB2_BYTES, SUB4_BYTES
+        nb = SUB2_BYTES if self.cache.code_bits == 2 else SUB4_BYTES
+        pool = self.cache.int4_pool[: (self.cache.int4_pool.numel() // nb) * nb]
         t = torch.from_numpy(np.asarray(idx, np.int64)).to(self.device)
-        return pool.view(-1, SUB4_BYTES).index_select(0, t).cpu().numpy()
+        return pool.view(-1, nb).index_select(0, t).cpu().numpy()
 
     def int8_subblocks(self, idx: np.ndarray) -> np.ndarray:
         from .layout import SUB8_BYTES

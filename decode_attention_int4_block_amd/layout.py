@@ -10,6 +10,7 @@ import numpy as np
 
 SUB = 16
 SUB4_BYTES = 2176
+SUB2_BYTES = 1152
 SUB8_BYTES = 4224
 
 
@@ -77,4 +78,27 @@ def decode_sub8(blocks: np.ndarray, ent) -> dict:
     vc = _nibbles_v(blocks, rows, 2048, e) | (_nibbles_v(blocks, rows, 3072, e) << 4)
     kp = blocks[rows, 4096 + 4 * e[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
     vp = blocks[rows, 4160 + 4 * e[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])
+
+
+def decode_sub2(blocks: np.ndarray, tok) -> dict:
+    """Codes and fp16 params of token `tok` (0..15) of each 2-bit subblock [N, 1152]."""
+    blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, SUB2_BYTES)
+    t = np.asarray(tok, dtype=np.int64).reshape(-1)
+    N = blocks.shape[0]
+    rows = np.arange(N)[:, None]
+    kc = np.empty((N, 128), np.uint8)
+    for d in range(128):
+        G, rem = d // 32, d % 32
+        w, i = rem // 16, rem % 16
+        byte = (G * 16 + t) * 8 + 4 * w + (0, 2, 1, 3)[i // 4]
+        kc[:, d] = (blocks[rows[:, 0], byte] >> (2 * (i % 4))) & 3
+    G, r = t // 4, t % 4
+    vc = np.empty((N, 128), np.uint8)
+    for d in range(128):
+        n, f, cc = d % 16, (d // 16) % 4, d // 64
+        byte = 512 + ((G * 16 + n) * 2 + cc) * 4 + r
+        vc[:, d] = (blocks[rows[:, 0], byte] >> (2 * f)) & 3
+    kp = blocks[rows, 1024 + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    vp = blocks[rows, 1088 + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
     return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])

@@ -92,6 +92,23 @@
  *     [4096, 4160) key   (scale, zero) fp16 pairs, 4 bytes per entry;
  *     [4160, 4224) value (scale, zero) fp16 pairs, 4 bytes per entry.
  *
+ * 2-bit main cache (code_bits = 2; KV4-RL, "Future Directions": caches below
+ * 4 bits under the same sink / recent protection).  Same quantization with
+ * qmax = 3; same pages, subblocks of 16 tokens and INT8 side cache.  Subblock j
+ * of (page, kv_head) starts at byte ((page * num_kv_heads + kv_head) * (P/16) + j) * 1152:
+ *     [   0,  512) key codes: the 8 bytes at (G * 16 + t) * 8 hold token t's
+ *                  rotated dims 32 G .. 32 G + 31 (G = 0..3); within dword w
+ *                  (dims 32 G + 16 w + i, i = 0..15) byte {0, 2, 1, 3}[i / 4]
+ *                  holds dim i in bits 2 (i % 4) .. 2 (i % 4) + 1;
+ *     [ 512, 1024) value codes: dword (G * 16 + n) * 2 + cc (G = t / 4),
+ *                  byte r = token 4 G + r, bits 2 f .. 2 f + 1 = value dim
+ *                  n + 16 f + 64 cc (n = 0..15, cc = 0..1, f = 0..3);
+ *     [1024, 1088) key   (scale, zero) fp16 pairs, 4 bytes per token;
+ *     [1088, 1152) value (scale, zero) fp16 pairs, 4 bytes per token.
+ *   1152 bytes / (16 tokens * 256 elements) = 2.25 bits per element.
+ *   kv_quant_append and kv_decode_attn serve both widths; kv_append_decode_attn
+ *   and kv_prefill_attn return KVQ_ERR_UNSUPPORTED for code_bits = 2.
+ *
  * Block table: int32 [num_slots][bt_stride], row = slot; entry i is the page
  * holding positions [i P, (i + 1) P) of that slot's sequence.  Only entries
  * i < ceil(L / P) are read.
@@ -127,6 +144,9 @@ typedef struct {
     void *int4_pool;         /* device, kvq_int4_pool_bytes(cache) bytes          */
     void *int8_pool;         /* device, kvq_int8_pool_bytes(cache) bytes; may be
                                 NULL only when sink + recent == 0                 */
+    int32_t code_bits;       /* width of the main (paged) cache's codes: 4, or 2
+                                for the 2-bit cache (0 means 4).  The INT8 side
+                                cache is the same for both.                       */
 } kvq_cache;
 
 /* Bytes of the INT4 pool / INT8 side cache for this descriptor (0 on bad input). */

@@ -16,10 +16,10 @@ from workloads import WorkloadConfig, bf16_bits, build_workload
 ATOL = 2e-3
 
 
-def small_config(lengths, *, Hq=8, Hkv=2, P=16, h=64, s=4, w=32, seed=77, name="small"):
+def small_config(lengths, *, Hq=8, Hkv=2, P=16, h=64, s=4, w=32, seed=77, name="small", bits=4):
     return WorkloadConfig(name=name, batch=len(lengths), num_q_heads=Hq, num_kv_heads=Hkv,
                           head_dim=128, lengths="explicit", length_args=tuple(int(x) for x in lengths),
-                          page_size=P, had_block=h, sink=s, recent=w, seed=seed)
+                          page_size=P, had_block=h, sink=s, recent=w, seed=seed, code_bits=bits)
 
 
 def check_workload_invariants(wl):
@@ -63,14 +63,16 @@ def compare_cache(dw, b, positions=None):
     """Compare the GPU cache of row b with the oracle's quantization of the same
     bf16 inputs.  Returns dict of mismatch / tie counts; raises on a mismatch
     that is not near a rounding tie."""
-    from decode_attention_int4_block_amd.layout import (decode_sub4, decode_sub8, sub4_index,
+    from decode_attention_int4_block_amd.layout import (decode_sub2, decode_sub4, decode_sub8, sub4_index,
                                                         sub8_index)
     wl = dw.wl
     cfg = wl.cfg
     L = int(wl.lengths[b])
     k, v = dw.host_kv[b]
     kb, vb = bf16_bits(k), bf16_bits(v)
-    oc = quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent)
+    oc = quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent, main_bits=cfg.code_bits)
+    qmain = (1 << cfg.code_bits) - 1
+    decode_main = decode_sub2 if cfg.code_bits == 2 else decode_sub4
     H = cfg.num_kv_heads
     P = wl.page_size
     slot = int(wl.slots[b])
@@ -81,10 +83,10 @@ def compare_cache(dw, b, positions=None):
     for hk in range(H):
         pages = wl.block_table[slot, pos // P]
         idx = sub4_index(pages, hk, pos % P, H, P)
-        got = decode_sub4(dw.int4_subblocks(idx), (pos % P) % 16)
+        got = decode_main(dw.int4_subblocks(idx), (pos % P) % 16)
         for kind, y, codes, sc, ze in (("k", yk, oc.k4, oc.k4_scale, oc.k4_zero),
                                        ("v", yv, oc.v4, oc.v4_scale, oc.v4_zero)):
-            ties = tie_near(y[pos, hk], 15)
+            ties = tie_near(y[pos, hk], qmain)
             mism = got[kind] != codes[pos, hk]
             stats["int4_ties"] += int((mism & ties).sum())
             stats["int4_mismatch"] += int((mism & ~ties).sum())
@@ -123,7 +125,8 @@ def compare_attention(dw, rows, report_unquantized=False):
             continue
         k, v = dw.host_kv[b]
         kb, vb = bf16_bits(k), bf16_bits(v)
-        ref, ref_lse = attend(qb[b], quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent))
+        ref, ref_lse = attend(qb[b], quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent,
+                                                       main_bits=cfg.code_bits))
         assert np.isfinite(out[b]).all() and np.isfinite(lse[b]).all(), f"non-finite output in row {b}"
         worst = max(worst, float(np.abs(out[b] - ref).max()))
         worst_lse = max(worst_lse, float(np.abs(lse[b] - ref_lse).max()))
