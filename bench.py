@@ -34,6 +34,7 @@ METRIC = "decode-attn effective KV GB/s + tokens·heads/s; % of MI355X HBM peak"
 HBM_PEAK_GBPS = 8000.0
 BYTES_INT4 = 136     # K+V codes + fp16 scale/zero of one (token, KV head), INT4
 BYTES_INT8 = 264     # same, INT8
+BYTES_INT2 = 72      # same, 2-bit main cache
 
 
 def region_sizes(L, s, w):
@@ -47,7 +48,8 @@ def decode_bytes(wl):
     """Algorithmic bytes one decode-attention launch must move."""
     c = wl.cfg
     n4, n8 = region_sizes(wl.lengths, c.sink, c.recent)
-    kv = int((c.num_kv_heads * (BYTES_INT4 * n4 + BYTES_INT8 * n8)).sum())
+    main = BYTES_INT2 if c.code_bits == 2 else BYTES_INT4
+    kv = int((c.num_kv_heads * (main * n4 + BYTES_INT8 * n8)).sum())
     P = wl.page_size
     lo4, hi4 = c.sink, wl.lengths - c.recent
     pages = np.where(hi4 > lo4, (hi4 + P - 1) // P - lo4 // P, 0)
@@ -167,10 +169,11 @@ def budget_variants(cfg, max_len):
         ("budget 144/0 (all sink)", dict(sink=144, recent=0)),
         ("budget 0/144 (all recent)", dict(sink=0, recent=144)),
         ("KV8 everywhere (s+w >= L)", dict(sink=cfg.sink, recent=max(max_len - cfg.sink, cfg.recent))),
+        ("K2V2: 2-bit main cache (s=%d, w=%d)" % (cfg.sink, cfg.recent), dict(code_bits=2)),
     ]
 
 
-def measure_variants(torch, cfg, steps, warmup):
+def measure_variants(torch, cfg, steps, warmup, only=None):
     """Decode and append time of each budget variant, caches rotated like the main
     measurement (one copy when a copy alone is far beyond the 256 MB Infinity Cache)."""
     from decode_attention_int4_block_amd import QuantKVCache
@@ -180,6 +183,8 @@ def measure_variants(torch, cfg, steps, warmup):
     base = build_workload(cfg)
     res = []
     for tag, kw in budget_variants(cfg, int(base.lengths.max())):
+        if only is not None and not tag.startswith(only):
+            continue
         vcfg = cfg.scaled(**kw)
         wl = build_workload(vcfg)
         dw = DeviceWorkload(wl, device="cuda", gen_device="cuda")
@@ -205,8 +210,10 @@ def measure_variants(torch, cfg, steps, warmup):
             dw.decode_step()
             if ev:
                 ev[2].record()
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        for i in range(steps):
+        # the fused append serves the 4-bit cache only
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)] \
+            if vcfg.code_bits == 4 else []
+        for i in range(len(fev)):
             dw.cache = copies[i % len(copies)]
             fev[i][0].record()
             dw.fused_step()
@@ -214,11 +221,13 @@ def measure_variants(torch, cfg, steps, warmup):
         torch.cuda.synchronize()
         dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
         app = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-        fus = np.array([e[0].elapsed_time(e[1]) for e in fev]) * 1e3
+        fus = np.array([e[0].elapsed_time(e[1]) for e in fev]) * 1e3 if fev else None
         us = float(np.median(dec))
         res.append(dict(variant=tag, sink=vcfg.sink, recent=vcfg.recent, had_block=vcfg.had_block,
+                        code_bits=vcfg.code_bits,
                         decode_algorithmic_bytes=db["total"], decode_us=round(us, 2),
-                        append_us=round(float(np.median(app)), 2), fused_us=round(float(np.median(fus)), 2),
+                        append_us=round(float(np.median(app)), 2),
+                        fused_us=round(float(np.median(fus)), 2) if fus is not None else None,
                         GBps=round(db["total"] / us / 1e3, 1), hbm_frac=round(db["total"] / us / 1e3 / HBM_PEAK_GBPS, 4)))
         print(f"[bench] variant {tag}: decode {us:.1f} us, {db['total'] / 1e6:.1f} MB", file=sys.stderr, flush=True)
         del dw, copies
@@ -335,6 +344,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
                     help="also time the protection-budget / rotation variants (s, w, h) on the same lengths")
+    ap.add_argument("--no-sub4bit", action="store_true",
+                    help="skip the decode measurement with the 2-bit main cache (K2V2)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the kv_prefill_attn measurement on the re-prefill workload")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -488,6 +499,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, dw)
+    if not args.no_sub4bit:
+        # the 2-bit main cache (same lengths, seeds and INT8 protection): decode time and bytes
+        k2 = measure_variants(torch, cfg, steps=max(5, min(args.steps, 20)), warmup=3,
+                              only="K2V2")
+        rec["k2v2"] = k2[0] if k2 else None
     if not args.no_prefill:
         rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2,
                                          cpu=not args.no_cpu_baseline)
