@@ -36,6 +36,11 @@ constexpr int kMinUnitsPerWorker = 8;
 // XCDs, of which the odd-numbered ones (odd w) stream ~6% slower.  Weights:
 // {first half, even w}, {first, odd}, {second, even}, {second, odd}.
 constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
+// A segment's start (query build) and end (reduction, piece or output stores)
+// take about as long as two steps of one wave (regression of the per-wave
+// durations on units and segments, Qwen3-8B batch), so the split counts each
+// segment as this many units more than it streams.
+constexpr int32_t kSegWeight = 2;
 constexpr int kMaxDevices = 64;
 // per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused
 // append, attention over the 2-bit cache)
@@ -231,6 +236,7 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.max_workers = workers;
     a.min_units = kMinUnitsPerWorker;
     for (int i = 0; i < 4; ++i) a.part_wt[i] = kPartWeights[i];
+    a.seg_wt = kSegWeight;
     a.ws_header = reinterpret_cast<int32_t *>(ws);
     a.ws_first = reinterpret_cast<int32_t *>(ws + l.first_off);
     a.ws_wseg = reinterpret_cast<int32_t *>(ws + l.wseg_off);

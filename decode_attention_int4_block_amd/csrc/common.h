@@ -192,6 +192,7 @@ struct DecodeArgs {
     float inv_sqrt_h;
     int32_t max_workers, min_units;
     int32_t part_wt[4];                 // worker weights (Partition)
+    int32_t seg_wt;                     // weight-only units counted before each segment
     int32_t *ws_header;     // [0] workers of this launch
     int32_t *ws_first;      // [B*H] worker that attended the segment's first unit
     int32_t *ws_last;       // [B*H] worker that attended the segment's last unit

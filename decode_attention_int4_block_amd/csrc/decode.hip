@@ -189,10 +189,19 @@ __device__ inline int row_slot(const DecodeArgs &a, const RowRegs &R, int b) {
     return ldc(a.slot, b);
 }
 
+// Units of the work split: a segment of `cost` steps counts as a.seg_wt
+// weight-only units followed by its steps (unit index u is global over these).
+// Weight units carry the segment's fixed cost into the split; no wave issues
+// them.
+__device__ inline int seg_units(const DecodeArgs &a, const RowPlan &rp) {
+    return rp.cost > 0 ? rp.cost + a.seg_wt : 0;
+}
+
 __device__ inline void cursor_next(const DecodeArgs &a, const RowRegs &R, Cursor &c) {
     ++c.u;
     if (++c.r < c.rp.cost) return;
     c.r = 0;
+    c.u += a.seg_wt;        // over the next segment's weight units
     if (++c.hk < a.H) return;
     c.hk = 0;
     for (++c.b; c.b < a.B; ++c.b) {
@@ -228,7 +237,7 @@ __device__ inline void fetch_pages(const DecodeArgs &a, const RowRegs &R, int64_
     int64_t pre = bc.pre;
     while (b < a.B) {
         const int L = row_len(a, R, b);
-        const int64_t rowu = (int64_t)row_plan(L, a.s, a.w).cost * a.H;
+        const int64_t rowu = (int64_t)seg_units(a, row_plan(L, a.s, a.w)) * a.H;
         if (pre + rowu > hb && rowu > 0) {
             const int sl = row_slot(a, R, b);
             if (u >= pre && u < pre + rowu) {
@@ -249,9 +258,12 @@ __device__ inline void fetch_pages(const DecodeArgs &a, const RowRegs &R, int64_
     if (mine && u < u_end) {
         const RowPlan rp = row_plan(myL, a.s, a.w);
         const uint32_t off = (uint32_t)(u - mypre);
-        const uint32_t hk = off / (uint32_t)rp.cost;
-        const int r = (int)(off - hk * (uint32_t)rp.cost);
-        if (r < rp.n4) {
+        const uint32_t vc = (uint32_t)seg_units(a, rp);
+        const uint32_t hk = off / vc;
+        const int r = (int)(off - hk * vc) - a.seg_wt;
+        if (r < 0) {
+            // a weight unit: no step, never read
+        } else if (r < rp.n4) {
             const int pos0 = (rp.k0 + r) * 32;
             // lanes kPgHalf.. take subblock B (the producer ignores it past the INT4 region)
             const int pos = (lane >= kPgHalf && pos0 + 16 < rp.hi4) ? pos0 + 16 : pos0;
@@ -1001,7 +1013,8 @@ void decode_split_kernel(DecodeArgs a) {
     int64_t cost[4], excl[4];
     int64_t res_total = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cost[k] = lane + 64 * k < a.B ? (int64_t)row_plan(R.L[k], a.s, a.w).cost * a.H : 0;
+    for (int k = 0; k < 4; ++k)
+        cost[k] = lane + 64 * k < a.B ? (int64_t)seg_units(a, row_plan(R.L[k], a.s, a.w)) * a.H : 0;
     // 32-bit DPP scans when 256 row costs cannot reach 2^31 (every realistic
     // batch), 64-bit shuffle scans otherwise
     const bool small = !__any(cost[0] >= (1 << 22) || cost[1] >= (1 << 22) || cost[2] >= (1 << 22) ||
@@ -1024,7 +1037,8 @@ void decode_split_kernel(DecodeArgs a) {
     int64_t total = res_total;
     if (a.B > kResRows) {
         int64_t rest = 0;
-        for (int b = kResRows + lane; b < a.B; b += 64) rest += (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H;
+        for (int b = kResRows + lane; b < a.B; b += 64)
+            rest += (int64_t)seg_units(a, row_plan(a.ctx_len[b], a.s, a.w)) * a.H;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) rest += __shfl_xor(rest, o, 64);
         total += uni64(rest);
@@ -1059,7 +1073,7 @@ void decode_split_kernel(DecodeArgs a) {
         int64_t base = res_total;
         for (int cb = kResRows; cb < a.B; cb += 64) {
             const int b = cb + lane;
-            const int64_t c = b < a.B ? (int64_t)row_plan(a.ctx_len[b], a.s, a.w).cost * a.H : 0;
+            const int64_t c = b < a.B ? (int64_t)seg_units(a, row_plan(a.ctx_len[b], a.s, a.w)) * a.H : 0;
             const int64_t incl = wave_scan(c, lane);
             const int64_t ex = base + incl - c;
             const uint64_t mk = __ballot(b < a.B && c > 0 && ex <= u_begin && u_begin < ex + c);
@@ -1078,9 +1092,21 @@ void decode_split_kernel(DecodeArgs a) {
     Cursor start;
     start.b = b0;
     start.rp = row_plan(row_len(a, R, b0), a.s, a.w);
-    start.hk = (int)((u_begin - pre0) / start.rp.cost);
-    start.r = (int)(u_begin - pre0 - (int64_t)start.hk * start.rp.cost);
-    start.u = u_begin;
+    {
+        const int vc = seg_units(a, start.rp);
+        start.hk = (int)((u_begin - pre0) / vc);
+        const int v = (int)(u_begin - pre0 - (int64_t)start.hk * vc);
+        // a range that opens on weight units starts at the segment's first step
+        start.r = v < a.seg_wt ? 0 : v - a.seg_wt;
+        start.u = u_begin + (v < a.seg_wt ? a.seg_wt - v : 0);
+    }
+    if (start.u >= u_end) {                     // weight units only: no steps, no pieces
+        if (lane == 0) {
+            a.ws_wseg[2 * wid] = -1;
+            a.ws_wseg[2 * wid + 1] = -1;
+        }
+        return;
+    }
 
     const LaneCtx<GP> L = lane_ctx<GP>(lane);
     SegCtx<GP> c;
@@ -1140,7 +1166,7 @@ void decode_split_kernel(DecodeArgs a) {
     for (int s = 0; s < kStages; ++s) {
         if (P.u < u_end) {
             const Lookup look = uniform(read_pages(P));
-            if (P.r == 0 || P.u == u_begin) issue_query<GP>(a, P.b, P.hk, L, qring + s * QRing<GP>::kBytes);
+            if (P.r == 0 || P.u == start.u) issue_query<GP>(a, P.b, P.hk, L, qring + s * QRing<GP>::kBytes);
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + s * kKvBytes, lane);
             }
@@ -1195,7 +1221,7 @@ void decode_split_kernel(DecodeArgs a) {
         if (P.u < u_end) look = read_pages(P);
         wait_lgkm0();
         if (P.u < u_end) {
-            if (P.r == 0 || P.u == u_begin) issue_query<GP>(a, P.b, P.hk, L, qs);
+            if (P.r == 0 || P.u == start.u) issue_query<GP>(a, P.b, P.hk, L, qs);
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvs, lane);
             }
