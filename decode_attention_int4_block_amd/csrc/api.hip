@@ -62,6 +62,13 @@ kvq_status check_cache(const kvq_cache *c) {
     if ((int64_t)c->sink + c->recent > (1 << 20)) return fail(KVQ_ERR_SHAPE, "sink + recent too large");
     if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 4)
         return fail(KVQ_ERR_UNSUPPORTED, "code_bits %d: the main cache holds 4- or 2-bit codes", c->code_bits);
+    // the kernels index subblocks with 32-bit integers
+    const uint64_t subs4 = (uint64_t)c->num_pages * (uint64_t)c->num_kv_heads * (uint64_t)(c->page_size / kvq::kSub);
+    const uint64_t subs8 = (uint64_t)c->num_slots * (uint64_t)c->num_kv_heads *
+                           (uint64_t)kvq::ceil_div(c->sink + c->recent, kvq::kSub);
+    if (subs4 >= ((uint64_t)1 << 32) || subs8 >= ((uint64_t)1 << 32))
+        return fail(KVQ_ERR_SHAPE, "a pool of 2^32 or more subblocks (%llu main, %llu ring)",
+                    (unsigned long long)subs4, (unsigned long long)subs8);
     return KVQ_OK;
 }
 

@@ -166,12 +166,20 @@ struct RowRegs {
 };
 
 __device__ inline RowRegs load_rows(const DecodeArgs &a, int lane) {
+    // all eight loads issued back to back (rows past B read row 0, B >= 1)
+    int Lr[4], Sr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = lane + 64 * k < a.B ? lane + 64 * k : 0;
+        Lr[k] = a.ctx_len[b];
+        Sr[k] = a.slot[b];
+    }
     RowRegs R;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int b = lane + 64 * k;
-        R.L[k] = b < a.B ? a.ctx_len[b] : 0;
-        R.S[k] = b < a.B ? a.slot[b] : 0;
+        const bool in = lane + 64 * k < a.B;
+        R.L[k] = in ? Lr[k] : 0;
+        R.S[k] = in ? Sr[k] : 0;
     }
     return R;
 }
@@ -522,15 +530,19 @@ template <int BITS>
 __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lookup &k, uint8_t *st,
                                   uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8, int lane) {
     if (c.r < c.rp.n4) {
-        constexpr int kSubBytes = BITS == 2 ? kSub2Bytes : kSub4Bytes;
+        constexpr uint32_t kSubBytes = BITS == 2 ? kSub2Bytes : kSub4Bytes;
         const int pos0 = (c.rp.k0 + c.r) * 32;
-        const int subs = a.P >> 4;
-        const uint8_t *baseA = a.int4_pool +
-            ((size_t)((int64_t)k.pageA * a.H + c.hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSubBytes;
-        // subblock B past the INT4 region is never used; re-read A (valid memory)
-        const uint8_t *baseB = (pos0 + 16 < c.rp.hi4)
-            ? a.int4_pool + ((size_t)((int64_t)k.pageB * a.H + c.hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSubBytes
-            : baseA;
+        // subblock indices fit 32 bits (the descriptor check bounds the pools);
+        // a page holds 1 << (logP - 4) subblocks of a KV head
+        const uint32_t sh = (uint32_t)a.logP - 4;
+        const uint32_t idxA = (((uint32_t)k.pageA * (uint32_t)a.H + (uint32_t)c.hk) << sh) +
+                              ((uint32_t)(pos0 & (a.P - 1)) >> 4);
+        const uint8_t *baseA = a.int4_pool + (uint64_t)idxA * kSubBytes;
+        // subblock B past the INT4 region is never used; re-read A (valid memory).
+        // Pages of 32 or more positions hold both 16-position halves of a step.
+        const uint8_t *baseB = pos0 + 16 >= c.rp.hi4 ? baseA
+            : sh > 0 ? baseA + kSubBytes
+            : a.int4_pool + (uint64_t)((uint32_t)k.pageB * (uint32_t)a.H + (uint32_t)c.hk) * kSubBytes;
         if constexpr (BITS == 2) {
             const uint32_t off = 16 * (uint32_t)lane;
             if (lane < 32) {
@@ -552,8 +564,9 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
     } else {
         // the low-nibble planes take the place of subblock A, the high-nibble
         // planes that of subblock B
-        const int sub = c.r - c.rp.n4;
-        const uint8_t *base = a.int8_pool + ((size_t)((int64_t)k.slot * a.H + c.hk) * a.nr8 + sub) * kSub8Bytes;
+        const uint32_t sub = (uint32_t)(c.r - c.rp.n4);
+        const uint32_t idx = ((uint32_t)k.slot * (uint32_t)a.H + (uint32_t)c.hk) * (uint32_t)a.nr8 + sub;
+        const uint8_t *base = a.int8_pool + (uint64_t)idx * kSub8Bytes;
         dma16(base + kSub8KLo, offK, st + 0);
         dma16(base + kSub8KHi, offK, st + 1024);
         dma16(base + kSub8VLo, offV, st + 2048);
@@ -1010,6 +1023,14 @@ void decode_split_kernel(DecodeArgs a) {
     // rows of the register table take one load round trip and four
     // independent lane scans; rows beyond it are summed from memory.
     const RowRegs R = load_rows(a, lane);
+    // The kernel arguments of the prologue, in one scalar round trip under the
+    // row table's loads (left to itself the compiler loads them where first
+    // used, each load waited on the prologue's critical path).
+    __asm__ volatile("" ::"s"(a.ws_header), "s"(a.ws_wseg), "s"(a.block_table), "s"(a.bt_stride), "s"(a.H),
+                     "s"(a.P), "s"(a.logP), "s"(a.s), "s"(a.w), "s"(a.nr8), "s"(a.max_workers), "s"(a.min_units),
+                     "s"(a.part_wt[0]), "s"(a.part_wt[1]), "s"(a.part_wt[2]), "s"(a.part_wt[3]), "s"(a.seg_wt),
+                     "s"(a.int4_pool), "s"(a.int8_pool), "s"(a.q), "s"(a.Hq), "s"(a.g), "s"(a.ws_piece),
+                     "s"(a.out), "s"(a.lse));
     int64_t cost[4], excl[4];
     int64_t res_total = 0;
 #pragma unroll
@@ -1132,7 +1153,10 @@ void decode_split_kernel(DecodeArgs a) {
     int hcur = 0;                             // its half index
     fetch_pages(a, R, hb, u_end, bc, lane, pg);
     if (hb + kPgHalf < u_end) fetch_pages(a, R, hb + kPgHalf, u_end, bc, lane, pg + 2 * kPgHalf);
-    __builtin_amdgcn_s_waitcnt(0);            // both halves landed (nothing else is in flight yet)
+    // Both halves landed (nothing else is in flight yet).  A gather whose lanes
+    // all hold INT8, weight or past-the-range units issues no load at all, so
+    // a partial count here could leave the first half in flight.
+    __builtin_amdgcn_s_waitcnt(0);
     KVQ_FENCE();
     // pages of the producer's next step (LDS reads; waited with the stage reads)
     auto read_pages = [&](const Cursor &c) {

@@ -136,8 +136,11 @@ typedef struct {
     int32_t num_kv_heads;    /* >= 1                                              */
     int32_t head_dim;        /* must be 128                                       */
     int32_t page_size;       /* tokens per page: a power of two >= 16             */
-    int32_t num_pages;       /* pages in int4_pool                                */
-    int32_t num_slots;       /* sequence slots (rows of the block table / INT8)   */
+    int32_t num_pages;       /* pages in int4_pool; num_pages * num_kv_heads *
+                                page_size / 16 < 2^32 (subblocks of the pool)     */
+    int32_t num_slots;       /* sequence slots (rows of the block table / INT8);
+                                num_slots * num_kv_heads * ceil((sink + recent)
+                                / 16) < 2^32                                      */
     int32_t had_block;       /* Hadamard block size h: power of two in [1, 128]   */
     int32_t sink;            /* s >= 0                                            */
     int32_t recent;          /* w >= 0                                            */
