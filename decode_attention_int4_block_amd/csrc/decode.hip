@@ -1302,9 +1302,10 @@ void decode_split_kernel(DecodeArgs a) {
 // completes the count folds the chunk partials.  Pieces and chunks are folded in
 // worker order, so the result is the same whoever finishes last.
 //
-// Lane l handles query heads 8 k + l / 16 and 8 k + 4 + l / 16 and dims
-// 8 (l % 16) .. + 8 of a piece laid out as [head][m, l, 0, 0, acc[128]].
-constexpr int kCombBatch = 4;
+// Lane l handles query heads l / 16 (g <= 4), or 8 k + l / 16 and 8 k + 4 +
+// l / 16, and dims 8 (l % 16) .. + 8 of a piece laid out as
+// [head][m, l, 0, 0, acc[128]].
+constexpr int kCombBatch = 8;
 
 struct MergeAcc {
     float M, Ls, acc[8];
@@ -1317,41 +1318,40 @@ __device__ inline void merge_init(MergeAcc &r) {
     for (int e = 0; e < 8; ++e) r.acc[e] = 0.0f;
 }
 
-// Folds pieces ptr(0), ..., ptr(cnt - 1) (wave-uniform bases) for heads
-// jj[0] and, when two2, jj[1] (two head groups share each batch of loads).
-template <typename PtrFn>
-__device__ inline void fold_pieces(MergeAcc (&r)[2], PtrFn ptr, int cnt, const int (&jj)[2], bool two2, int part) {
-    for (int k0 = 0; k0 < cnt; k0 += kCombBatch) {
-        float m[2][kCombBatch], l[2][kCombBatch];
-        u32x4 v0[2][kCombBatch], v1[2][kCombBatch];
+// Folds pieces ptr(0), ..., ptr(cnt - 1) (wave-uniform bases) for the NH
+// heads jj[h] of this lane, kCombBatch / NH pieces per round trip.
+template <int NH, typename PtrFn>
+__device__ inline void fold_pieces(MergeAcc (&r)[NH], PtrFn ptr, int cnt, const int (&jj)[NH], int part) {
+    constexpr int NB = kCombBatch / NH;
+    for (int k0 = 0; k0 < cnt; k0 += NB) {
+        float m[NH][NB], l[NH][NB];
+        u32x4 v0[NH][NB], v1[NH][NB];
+        // branch-free: a batch past the last piece re-reads it and drops it,
+        // so all of a batch's loads issue before the first wait
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int t = 0; t < NB; ++t) {
+            const float *pt = ptr(min(k0 + t, cnt - 1));
 #pragma unroll
-            for (int t = 0; t < kCombBatch; ++t) {
-                if (k0 + t < cnt && (h == 0 || two2)) {
-                    const float *pp = ptr(k0 + t) + jj[h] * kPieceStride;
-                    m[h][t] = pp[0];
-                    l[h][t] = pp[1];
-                    v0[h][t] = ldg<u32x4>(pp + 4 + 8 * part);
-                    v1[h][t] = ldg<u32x4>(pp + 8 + 8 * part);
-                } else {
-                    m[h][t] = kNegInf;
-                    l[h][t] = 0.0f;
-                    v0[h][t] = u32x4{0u, 0u, 0u, 0u};
-                    v1[h][t] = u32x4{0u, 0u, 0u, 0u};
-                }
+            for (int h = 0; h < NH; ++h) {
+                const float *pp = pt + jj[h] * kPieceStride;
+                const float2 ml = *reinterpret_cast<const float2 *>(pp);
+                m[h][t] = k0 + t < cnt ? ml.x : kNegInf;
+                l[h][t] = ml.y;
+                v0[h][t] = ldg<u32x4>(pp + 4 + 8 * part);
+                v1[h][t] = ldg<u32x4>(pp + 8 + 8 * part);
             }
+        }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NH; ++h) {
             float Mn = r[h].M;
 #pragma unroll
-            for (int t = 0; t < kCombBatch; ++t) Mn = fmaxf(Mn, m[h][t]);
+            for (int t = 0; t < NB; ++t) Mn = fmaxf(Mn, m[h][t]);
             const float fr = r[h].M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(r[h].M - Mn);
             r[h].Ls *= fr;
 #pragma unroll
             for (int e = 0; e < 8; ++e) r[h].acc[e] *= fr;
 #pragma unroll
-            for (int t = 0; t < kCombBatch; ++t) {
+            for (int t = 0; t < NB; ++t) {
                 const float f = m[h][t] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m[h][t] - Mn);
                 r[h].Ls = fmaf(l[h][t], f, r[h].Ls);
 #pragma unroll
@@ -1362,6 +1362,32 @@ __device__ inline void fold_pieces(MergeAcc (&r)[2], PtrFn ptr, int cnt, const i
             }
             r[h].M = Mn;
         }
+    }
+}
+
+// Folds the pieces for every head of the group and hands each head's result
+// to out(r, j): one pass of single heads for g <= 4, else passes over pairs of
+// head quartets (lane l takes heads hg + l / 16 and hg + 4 + l / 16).
+template <typename PtrFn, typename OutFn>
+__device__ inline void fold_heads(int g, int lane, int part, int cnt, PtrFn ptr, OutFn out) {
+    if (g <= 4) {
+        const int j = lane >> 4;
+        MergeAcc r[1];
+        merge_init(r[0]);
+        const int jj[1] = {j < g ? j : 0};
+        fold_pieces<1>(r, ptr, cnt, jj, part);
+        if (j < g) out(r[0], j);
+        return;
+    }
+    for (int hg = 0; hg < g; hg += 8) {
+        const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
+        const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
+        MergeAcc r[2];
+        merge_init(r[0]);
+        merge_init(r[1]);
+        fold_pieces<2>(r, ptr, cnt, jj, part);
+        if (j[0] < g) out(r[0], j[0]);
+        if (j[1] < g) out(r[1], j[1]);
     }
 }
 
@@ -1426,17 +1452,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
         const int n = (int)(wl - wf + 1);
         if (n == 1 || n > T) return;            // finished by its only worker / folded by the helpers
         const float *basep = a.ws_piece + (wf + seg) * piece_elems;
-        for (int hg = 0; hg < g; hg += 8) {
-            const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
-            const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
-            MergeAcc r[2];
-            merge_init(r[0]);
-            merge_init(r[1]);
-            fold_pieces(r, [&](int k) { return basep + k * piece_elems; }, n, jj, hg + 4 < g, part);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                if (j[h] < g) merge_write(a, r[h], b, hk, j[h], part);
-        }
+        fold_heads(g, lane, part, n, [&](int k) { return basep + k * piece_elems; },
+                   [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); });
         return;
     }
     // helper: the pieces of workers [w0, w0 + T)
@@ -1462,17 +1479,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
         const int64_t wb = (w0 + T - 1 < wl ? w0 + T - 1 : wl);
         const float *basep = a.ws_piece + (wa + s) * piece_elems;
         float *chunk = a.ws_l2 + (jc + s) * piece_elems;
-        for (int hg = 0; hg < g; hg += 8) {
-            const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
-            const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
-            MergeAcc r[2];
-            merge_init(r[0]);
-            merge_init(r[1]);
-            fold_pieces(r, [&](int k) { return basep + k * piece_elems; }, (int)(wb - wa + 1), jj, hg + 4 < g, part);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                if (j[h] < g) merge_store(r[h], chunk, j[h], part);
-        }
+        fold_heads(g, lane, part, (int)(wb - wa + 1), [&](int k) { return basep + k * piece_elems; },
+                   [&](const MergeAcc &r, int j) { merge_store(r, chunk, j, part); });
         int before = 0;
         if (lane == 0)
             before = __hip_atomic_fetch_add(a.ws_count + s, (int)(wb - wa + 1), __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -1481,17 +1489,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
         // the last helper of the segment folds its chunk partials
         const int64_t jf = wf / T, jl = wl / T;
         const float *c0 = a.ws_l2 + (jf + s) * piece_elems;
-        for (int hg = 0; hg < g; hg += 8) {
-            const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
-            const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
-            MergeAcc r[2];
-            merge_init(r[0]);
-            merge_init(r[1]);
-            fold_pieces(r, [&](int k) { return c0 + k * piece_elems; }, (int)(jl - jf + 1), jj, hg + 4 < g, part);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                if (j[h] < g) merge_write(a, r[h], b, hk, j[h], part);
-        }
+        fold_heads(g, lane, part, (int)(jl - jf + 1), [&](int k) { return c0 + k * piece_elems; },
+                   [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); });
     }
 }
 
