@@ -88,26 +88,34 @@ __host__ __device__ inline RowPlan row_plan(int L, int s, int w) {
     return r;
 }
 
-// Start unit of worker w when `total` units are split over `workers` workers.
-__host__ __device__ inline int64_t worker_begin(int64_t w, int64_t total, int64_t workers) {
-    return (w * total) / workers;
-}
-
-// The worker whose unit range contains unit u.
-__host__ __device__ inline int64_t worker_of(int64_t u, int64_t total, int64_t workers) {
-    return ((u + 1) * workers - 1) / total;
+// q = n / d for the split's non-negative operands (d > 0).  A wave-uniform
+// 64-bit division costs about a hundred scalar instructions on the prologue's
+// critical path; operands that fit 32 bits take the 32-bit divide, and
+// numerators below 2^53 a double-precision quotient corrected to the exact one
+// (the rounded quotient is within 1 of it).
+__host__ __device__ inline int64_t div_nonneg(int64_t n, int64_t d) {
+    if ((uint64_t)(n | d) < ((uint64_t)1 << 32)) return (int64_t)((uint32_t)n / (uint32_t)d);
+    if (n < ((int64_t)1 << 53) && d < ((int64_t)1 << 32)) {
+        int64_t q = (int64_t)((double)n / (double)d);
+        if (q * d > n)
+            --q;
+        else if ((q + 1) * d <= n)
+            ++q;
+        return q;
+    }
+    return n / d;
 }
 
 __host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_workers, int64_t min_units) {
-    int64_t w = (total + min_units - 1) / min_units;
+    int64_t w = div_nonneg(total + min_units - 1, min_units);
     if (w < 1) w = 1;
     return w < max_workers ? w : max_workers;
 }
 
 // Weighted split of the units over W workers: worker w takes a share in
 // proportion to wt[2 r + (w & 1)], where r = (w >= W / 2), so that waves of
-// different measured speed (dispatch order, XCD) finish together.  With fewer units than W full
-// workers need, an even split over the workers needed.
+// different measured speed (dispatch order, XCD) finish together.  With fewer
+// units than W full workers need, an even split over the workers needed.
 struct Partition {
     int64_t total, W, half;
     int64_t wt[4];
@@ -142,11 +150,11 @@ __host__ __device__ inline Partition make_partition(int64_t total, int64_t max_w
 
 // First unit of worker w (w <= W).
 __host__ __device__ inline int64_t part_begin(const Partition &p, int64_t w) {
-    return p.total * part_cum(p, w) / p.csum;
+    return div_nonneg(p.total * part_cum(p, w), p.csum);
 }
 
 // The worker whose unit range contains unit u (u < total); workers with empty
-// ranges are never returned.
+// ranges are never returned.  (The inverse of part_begin, for checking it.)
 __host__ __device__ inline int64_t part_of(const Partition &p, int64_t u) {
     // invert the cumulative weight, then correct the rounding
     const int64_t c = u * p.csum / p.total;

@@ -1115,7 +1115,7 @@ void decode_split_kernel(DecodeArgs a) {
     start.rp = row_plan(row_len(a, R, b0), a.s, a.w);
     {
         const int vc = seg_units(a, start.rp);
-        start.hk = (int)((u_begin - pre0) / vc);
+        start.hk = (int)div_nonneg(u_begin - pre0, vc);
         const int v = (int)(u_begin - pre0 - (int64_t)start.hk * vc);
         // a range that opens on weight units starts at the segment's first step
         start.r = v < a.seg_wt ? 0 : v - a.seg_wt;

@@ -1,10 +1,12 @@
 """Host check of the work split shared by the decode kernels (csrc/common.h).
 
-The split kernel gives worker w the units [part_begin(w), part_begin(w + 1))
-and the combine kernel finds the workers of a segment with part_of(u); the two
-must agree exactly, the ranges must tile [0, total), and no unit may map to a
-worker without units.  The header is compiled for the host with hipcc and the
-properties are checked on many sizes (no GPU needed).
+The split kernel gives worker w the units [part_begin(w), part_begin(w + 1)).
+The ranges must tile [0, total), and part_of(u), their inverse, must agree
+with them exactly and never return a worker without units.  part_begin
+divides with div_nonneg, whose 32-bit, corrected double-precision and 64-bit
+routes are each reached by the sizes below, and div_nonneg is also checked
+directly against the 64-bit quotient.  The header is compiled for the host
+with hipcc (no GPU needed).
 """
 
 import os
@@ -24,8 +26,20 @@ using namespace kvq;
 int main() {
     const int32_t weights[3][4] = {{128, 128, 100, 100}, {131, 123, 103, 97}, {1, 1, 1, 1}};
     long checks = 0;
+    // exact division on every route: 32-bit, double-precision with correction, 64-bit
+    for (long long n : {0LL, 1LL, 4294967295LL, 4294967296LL, 12345678901234LL, 9007199254740991LL,
+                        9007199254740992LL, 9007199254740993LL, 4611686018427387903LL})
+    for (long long d : {1LL, 2LL, 3LL, 7LL, 2047LL, 285887LL, 4294967295LL, 4294967296LL, 4294967311LL}) {
+        if (div_nonneg(n, d) != n / d) { printf("div_nonneg(%lld, %lld) = %lld, want %lld\n", n, d, (long long)div_nonneg(n, d), n / d); return 1; }
+        for (long long k : {1LL, 2LL, 1000003LL}) {
+            const long long m = n / k;
+            if (div_nonneg(m, d) != m / d) { printf("div_nonneg(%lld, %lld)\n", m, d); return 1; }
+            if (m >= 1 && div_nonneg(m - 1, d) != (m - 1) / d) { printf("div_nonneg(%lld, %lld)\n", m - 1, d); return 1; }
+        }
+    }
     for (const auto &wt : weights)
-    for (long long total : {1LL, 7LL, 8LL, 100LL, 16383LL, 16384LL, 16385LL, 96700LL, 1234567LL, 99999989LL})
+    for (long long total : {1LL, 7LL, 8LL, 100LL, 16383LL, 16384LL, 16385LL, 96700LL, 1234567LL, 99999989LL,
+                            1099511627776LL})
     for (long long maxw : {1LL, 2LL, 3LL, 5LL, 2047LL, 2048LL, 2816LL}) {
         const Partition p = make_partition(total, maxw, wt, 8);
         if (p.W < 1 || p.W > maxw) { printf("bad W\n"); return 1; }
