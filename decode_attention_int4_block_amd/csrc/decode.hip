@@ -1228,32 +1228,25 @@ void decode_split_kernel(DecodeArgs a) {
     bool pend = false;          // a step of the current segment awaits its value part
     KOut<GP> kp;                // that step's scores and value codes
     Cursor E = C;               // its cursor
+    // Each iteration reads the next step's stage (and query, and the pages of
+    // the producer's step after next) from LDS first, then issues the
+    // producer's step into the slot the current step freed, and only then
+    // waits for the reads: their latency runs under the producer's work.
+    // (A query copy issued with a later step only makes the stage waits
+    // stricter.)
+    Lookup look = {0, 0, 0};    // pages of the producer's step P
+    if (P.u < u_end) look = read_pages(P);
+    wait_vm_steps(issued - 1);
+    if constexpr (APPEND) {
+        if (C.r == C.rp.rn) append_new_token(a, R, C, kvring, smem, lane);
+    }
+    StepRegs<GP> r = read_stage<GP, BITS>(smem, L, C.r < C.rp.n4);
+    QRing<GP> qr = read_query<GP>(qring, lane);     // the first step opens a segment
+    wait_lgkm0();
+    look = uniform(look);
     for (int i = 0; C.u < u_end; ++i) {
-        // (a query copy issued with a later step only makes this wait stricter)
-        wait_vm_steps(issued - i - 1);
-        uint8_t *st = smem + (i % kStages) * kStageBytes;
-        uint8_t *qs = qring + (i % kStages) * QRing<GP>::kBytes;
-        uint8_t *kvs = kvring + (i % kStages) * kKvBytes;
+        const int scur = i % kStages, snxt = (i + 1) % kStages;
         const bool int4 = C.r < C.rp.n4;
-        if constexpr (APPEND) {
-            if (C.r == C.rp.rn) append_new_token(a, R, C, kvs, st, lane);
-        }
-        const StepRegs<GP> r = read_stage<GP, BITS>(st, L, int4);
-        QRing<GP> qr;
-        if (!open) qr = read_query<GP>(qs, lane);
-        Lookup look = {0, 0, 0};
-        if (P.u < u_end) look = read_pages(P);
-        wait_lgkm0();
-        if (P.u < u_end) {
-            if (P.r == 0 || P.u == start.u) issue_query<GP>(a, P.b, P.hk, L, qs);
-            if constexpr (APPEND) {
-                if (P.r == P.rp.rn) issue_new_token(a, R, P, kvs, lane);
-            }
-            issue_step<BITS>(a, P, uniform(look), st, offK, offV, offP4, offP8, lane);
-            cursor_next(a, R, P);
-            ++issued;
-            advance_half(P);
-        }
         if (!open) {
             // this step starts a segment: finish the previous one first
             if (pend) {
@@ -1278,6 +1271,31 @@ void decode_split_kernel(DecodeArgs a) {
         E = C;
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
         cursor_next(a, R, C);
+        // the next step's stage (its DMA is i + 1's, issued three steps ago)
+        if (C.u < u_end) {
+            wait_vm_steps(issued - i - 2);
+            if constexpr (APPEND) {
+                if (C.r == C.rp.rn)
+                    append_new_token(a, R, C, kvring + snxt * kKvBytes, smem + snxt * kStageBytes, lane);
+            }
+            r = read_stage<GP, BITS>(smem + snxt * kStageBytes, L, C.r < C.rp.n4);
+            if (!open) qr = read_query<GP>(qring + snxt * QRing<GP>::kBytes, lane);
+        }
+        // producer: step P into the slot this iteration's step was read from
+        if (P.u < u_end) {
+            uint8_t *qs = qring + scur * QRing<GP>::kBytes;
+            if (P.r == 0 || P.u == start.u) issue_query<GP>(a, P.b, P.hk, L, qs);
+            if constexpr (APPEND) {
+                if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + scur * kKvBytes, lane);
+            }
+            issue_step<BITS>(a, P, look, smem + scur * kStageBytes, offK, offV, offP4, offP8, lane);
+            cursor_next(a, R, P);
+            ++issued;
+            advance_half(P);
+            if (P.u < u_end) look = read_pages(P);
+        }
+        wait_lgkm0();
+        look = uniform(look);
     }
     if (pend) {
         vpart<GP, BITS>(c, L, kp);
