@@ -54,9 +54,9 @@ def rotated_keys_f32(k_bits, h: int) -> np.ndarray:
 def quantize_sequence(k_bits, v_bits, h: int, s: int, w: int, main_bits: int = 4) -> SeqCache:
     """Quantize a whole sequence's keys/values [L, H, d] (bf16 patterns).
 
-    main_bits is the width of the main cache's codes: 4, or 2 for the sub-4-bit
-    cache under the same INT8 sink / recent protection (KV4-RL, "Future
-    Directions"); the fields k4 / v4 then hold the 2-bit codes.
+    main_bits is the width of the main cache's codes: 4, or 3 or 2 for the
+    sub-4-bit caches under the same INT8 sink / recent protection (KV4-RL,
+    "Future Directions"); the fields k4 / v4 then hold the 3- or 2-bit codes.
     """
     k_bits = np.asarray(k_bits, dtype=np.uint16)
     v_bits = np.asarray(v_bits, dtype=np.uint16)

@@ -32,11 +32,12 @@ INT8_QMAX = 255
 # Sub-4-bit main caches (KV4-RL, "Future Directions": 3- or 2-bit caches under the
 # same sink / recent protection): the same affine scheme with 2^bits levels.
 INT2_QMAX = 3
+INT3_QMAX = 7
 
 
 def qmax_of(bits: int) -> int:
     """Largest code of a `bits`-bit affine code."""
-    if bits not in (2, 4, 8):
+    if bits not in (2, 3, 4, 8):
         raise ValueError(f"unsupported code width {bits}")
     return (1 << bits) - 1
 
@@ -136,6 +137,30 @@ def unpack_int2(packed) -> np.ndarray:
     out = np.empty(p.shape[:-1] + (4 * p.shape[-1],), dtype=np.uint8)
     for f in range(4):
         out[..., f::4] = (p >> (2 * f)) & 0x3
+    return out
+
+
+def pack_int3(codes) -> np.ndarray:
+    """Canonical byte form of 3-bit codes, as two bit planes: the low two bits of
+    every code packed like pack_int2, then the high bits eight to a byte
+    (element 8j + i in bit i of byte j).  A vector of n codes takes n / 4 + n / 8
+    bytes."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lo = pack_int2(c & 0x3)
+    hi = np.zeros(c.shape[:-1] + (c.shape[-1] // 8,), dtype=np.uint8)
+    for i in range(8):
+        hi |= ((c[..., i::8] >> 2) & 0x1) << i
+    return np.concatenate([lo, hi], axis=-1).astype(np.uint8)
+
+
+def unpack_int3(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    n = p.shape[-1] * 8 // 3
+    lo = unpack_int2(p[..., : n // 4])
+    hi = p[..., n // 4:]
+    out = lo.copy()
+    for i in range(8):
+        out[..., i::8] |= ((hi >> i) & 0x1) << 2
     return out
 
 

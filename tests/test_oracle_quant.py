@@ -8,8 +8,9 @@ import pytest
 
 from oracle.hadamard import fwht_f32
 from oracle.numerics import f16_bits_to_f64
-from oracle.quant import (INT2_QMAX, INT4_QMAX, INT8_QMAX, bytes_per_token_head, dequantize,
-                          pack_int2, pack_int4, qmax_of, quantize, tie_near, unpack_int2, unpack_int4)
+from oracle.quant import (INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX, bytes_per_token_head, dequantize,
+                          pack_int2, pack_int3, pack_int4, qmax_of, quantize, tie_near, unpack_int2, unpack_int3,
+                          unpack_int4)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -35,7 +36,7 @@ def _brute_nearest(y, scale_h, zero_h, qmax):
     return code
 
 
-@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
 def test_codes_are_nearest_levels(qmax):
     y = fwht_f32(_vectors(3000, 1), 128)
     c, sb, zb = quantize(y, qmax)
@@ -47,7 +48,7 @@ def test_codes_are_nearest_levels(qmax):
     assert not np.any(mism & ~ties), int((mism & ~ties).sum())
 
 
-@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
 def test_scale_and_zero_are_fp16_of_range_and_min(qmax):
     y = _vectors(2000, 2)
     c, sb, zb = quantize(y, qmax)
@@ -60,7 +61,7 @@ def test_scale_and_zero_are_fp16_of_range_and_min(qmax):
     assert np.all(np.abs(z - mn) <= 2.0 ** -11 * np.abs(mn) * 1.0001 + 2.0 ** -25)
 
 
-@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
 def test_round_trip_bound(qmax):
     y = fwht_f32(_vectors(3000, 3), 64)
     c, sb, zb = quantize(y, qmax)
@@ -77,7 +78,7 @@ def test_round_trip_bound(qmax):
     assert np.all(err <= s * 0.5 + slack + 1e-6 * np.abs(y).max(axis=1))
 
 
-@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
 def test_grid_vectors_round_trip_exactly(qmax):
     rng = np.random.default_rng(4)
     n = 200
@@ -95,7 +96,7 @@ def test_grid_vectors_round_trip_exactly(qmax):
     assert np.array_equal(dequantize(c, sb, zb), y.astype(np.float64))
 
 
-@pytest.mark.parametrize("qmax", [INT2_QMAX, INT4_QMAX, INT8_QMAX])
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
 def test_zero_range_guard(qmax):
     y = np.stack([np.full(128, 0.3, np.float32), np.zeros(128, np.float32),
                   np.full(128, -7.25, np.float32)])
@@ -155,12 +156,49 @@ def test_pack_int2_round_trip_and_bit_order():
 
 
 def test_code_widths():
-    assert [qmax_of(b) for b in (2, 4, 8)] == [3, 15, 255]
-    with pytest.raises(ValueError):
-        qmax_of(3)
-    # K+V bytes per (token, head) at 2 bits: 2 * (32 + 4) = 72, i.e. 2.25 bits per element
+    assert [qmax_of(b) for b in (2, 3, 4, 8)] == [3, 7, 15, 255]
+    for bad in (1, 5, 6):
+        with pytest.raises(ValueError):
+            qmax_of(bad)
+    # K+V bytes per (token, head) at 2 bits: 2 * (32 + 4) = 72, i.e. 2.25 bits per element;
+    # at 3 bits: 2 * (48 + 4) = 104, 3.25 bits per element
     assert bytes_per_token_head(128, 2) == 72
     assert bytes_per_token_head(128, 2) * 8 / 256 == 2.25
+    assert bytes_per_token_head(128, 3) == 104
+    assert bytes_per_token_head(128, 3) * 8 / 256 == 3.25
+    assert pack_int3(np.zeros((1, 128), np.uint8)).shape == (1, 48)
+
+
+def test_pack_int3_round_trip_and_bit_order():
+    rng = np.random.default_rng(17)
+    c = rng.integers(0, 8, (40, 128)).astype(np.uint8)
+    p = pack_int3(c)
+    assert p.shape == (40, 48)
+    assert np.array_equal(unpack_int3(p), c)
+    # the low plane is the 2-bit packing of the low bits, the high plane bit i of
+    # byte j is element 8 j + i's bit 2
+    assert np.array_equal(p[:, :32], pack_int2(c & 3))
+    assert np.array_equal((p[:, 32] >> 3) & 1, (c[:, 3] >> 2) & 1)
+    # a worked vector: codes 7, 0, 5, 2, 4, 1, 6, 3 -> low plane bytes 0b10_01_00_11,
+    # 0b11_10_01_00; high plane byte 0b0101_0101
+    w = np.zeros(128, np.uint8)
+    w[:8] = [7, 0, 5, 2, 4, 1, 6, 3]
+    pw = pack_int3(w)
+    assert pw[0] == 0x93 and pw[1] == 0xE4 and pw[32] == 0x55 and not pw[2:32].any() and not pw[33:].any()
+
+
+def test_int3_cache_keeps_the_int8_protection():
+    """A 3-bit main cache: main codes in [0, 7], the INT8 region's copies unchanged."""
+    import torch
+    from oracle.cache import quantize_sequence
+    from workloads import bf16_bits
+    rng = np.random.default_rng(18)
+    k = bf16_bits(torch.from_numpy(rng.standard_normal((50, 2, 128)) * 3).to(torch.bfloat16))
+    v = bf16_bits(torch.from_numpy(rng.standard_normal((50, 2, 128))).to(torch.bfloat16))
+    c4 = quantize_sequence(k, v, 64, 4, 16)
+    c3 = quantize_sequence(k, v, 64, 4, 16, main_bits=3)
+    assert c3.k4.max() <= 7 and c3.v4.max() <= 7 and c4.k4.max() > 7
+    assert np.array_equal(c3.pos8, c4.pos8) and np.array_equal(c3.k8, c4.k8) and np.array_equal(c3.v8, c4.v8)
 
 
 def test_int2_cache_keeps_the_int8_protection():
