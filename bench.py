@@ -35,6 +35,7 @@ HBM_PEAK_GBPS = 8000.0
 BYTES_INT4 = 136     # K+V codes + fp16 scale/zero of one (token, KV head), INT4
 BYTES_INT8 = 264     # same, INT8
 BYTES_INT2 = 72      # same, 2-bit main cache
+BYTES_INT3 = 104     # same, 3-bit main cache
 
 
 def region_sizes(L, s, w):
@@ -48,7 +49,7 @@ def decode_bytes(wl):
     """Algorithmic bytes one decode-attention launch must move."""
     c = wl.cfg
     n4, n8 = region_sizes(wl.lengths, c.sink, c.recent)
-    main = BYTES_INT2 if c.code_bits == 2 else BYTES_INT4
+    main = {2: BYTES_INT2, 3: BYTES_INT3}.get(c.code_bits, BYTES_INT4)
     kv = int((c.num_kv_heads * (main * n4 + BYTES_INT8 * n8)).sum())
     P = wl.page_size
     lo4, hi4 = c.sink, wl.lengths - c.recent
@@ -169,6 +170,7 @@ def budget_variants(cfg, max_len):
         ("budget 144/0 (all sink)", dict(sink=144, recent=0)),
         ("budget 0/144 (all recent)", dict(sink=0, recent=144)),
         ("KV8 everywhere (s+w >= L)", dict(sink=cfg.sink, recent=max(max_len - cfg.sink, cfg.recent))),
+        ("K3V3: 3-bit main cache (s=%d, w=%d)" % (cfg.sink, cfg.recent), dict(code_bits=3)),
         ("K2V2: 2-bit main cache (s=%d, w=%d)" % (cfg.sink, cfg.recent), dict(code_bits=2)),
     ]
 
@@ -345,7 +347,7 @@ def main():
     ap.add_argument("--variants", action="store_true",
                     help="also time the protection-budget / rotation variants (s, w, h) on the same lengths")
     ap.add_argument("--no-sub4bit", action="store_true",
-                    help="skip the decode measurement with the 2-bit main cache (K2V2)")
+                    help="skip the decode measurements with the 3- and 2-bit main caches (K3V3, K2V2)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the kv_prefill_attn measurement on the re-prefill workload")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -500,10 +502,10 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, dw)
     if not args.no_sub4bit:
-        # the 2-bit main cache (same lengths, seeds and INT8 protection): decode time and bytes
-        k2 = measure_variants(torch, cfg, steps=max(5, min(args.steps, 20)), warmup=3,
-                              only="K2V2")
-        rec["k2v2"] = k2[0] if k2 else None
+        # the 3- and 2-bit main caches (same lengths, seeds and INT8 protection): decode time and bytes
+        for tag in ("K3V3", "K2V2"):
+            kx = measure_variants(torch, cfg, steps=max(5, min(args.steps, 20)), warmup=3, only=tag)
+            rec[tag.lower()] = kx[0] if kx else None
     if not args.no_prefill:
         rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2,
                                          cpu=not args.no_cpu_baseline)

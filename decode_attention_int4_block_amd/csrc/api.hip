@@ -44,7 +44,7 @@ constexpr int32_t kSegWeight = 2;
 constexpr int kMaxDevices = 64;
 // per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused
 // append, attention over the 2-bit cache)
-std::atomic<int> g_max_workers[kMaxDevices][9];
+std::atomic<int> g_max_workers[kMaxDevices][12];
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -60,8 +60,8 @@ kvq_status check_cache(const kvq_cache *c) {
         return fail(KVQ_ERR_SHAPE, "had_block %d is not a power of two in [1, 128]", c->had_block);
     if (c->sink < 0 || c->recent < 0) return fail(KVQ_ERR_SHAPE, "negative sink/recent");
     if ((int64_t)c->sink + c->recent > (1 << 20)) return fail(KVQ_ERR_SHAPE, "sink + recent too large");
-    if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 4)
-        return fail(KVQ_ERR_UNSUPPORTED, "code_bits %d: the main cache holds 4- or 2-bit codes", c->code_bits);
+    if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 3 && c->code_bits != 4)
+        return fail(KVQ_ERR_UNSUPPORTED, "code_bits %d: the main cache holds 4-, 3- or 2-bit codes", c->code_bits);
     // the kernels index subblocks with 32-bit integers
     const uint64_t subs4 = (uint64_t)c->num_pages * (uint64_t)c->num_kv_heads * (uint64_t)(c->page_size / kvq::kSub);
     const uint64_t subs8 = (uint64_t)c->num_slots * (uint64_t)c->num_kv_heads *
@@ -72,7 +72,7 @@ kvq_status check_cache(const kvq_cache *c) {
     return KVQ_OK;
 }
 
-int bits_of(const kvq_cache *c) { return c->code_bits == 2 ? 2 : 4; }
+int bits_of(const kvq_cache *c) { return c->code_bits == 2 || c->code_bits == 3 ? c->code_bits : 4; }
 
 int nr8_of(const kvq_cache *c) { return kvq::ceil_div(c->sink + c->recent, kvq::kSub); }
 
@@ -84,7 +84,7 @@ kvq_status max_workers(int g, bool fused, int bits, int *out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
-    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (bits == 2 ? 6 : (fused ? 3 : 0));
+    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (bits == 2 ? 6 : (bits == 3 ? 9 : (fused ? 3 : 0)));
     int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
         hipError_t e = kvq::decode_max_workers(g, fused, bits, &v);
@@ -177,7 +177,7 @@ size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num
     int workers = 0, workers_fused = 0;
     const int bits = bits_of(c);
     if (max_workers(g, false, bits, &workers) != KVQ_OK) return 0;
-    if (bits == 2) return ws_layout(c, B, g, workers).total;
+    if (bits != 4) return ws_layout(c, B, g, workers).total;     // no fused kernel below 4 bits
     if (max_workers(g, true, bits, &workers_fused) != KVQ_OK) return 0;
     const size_t a = ws_layout(c, B, g, workers).total, b = ws_layout(c, B, g, workers_fused).total;
     return a > b ? a : b;

@@ -13,8 +13,8 @@
 
 namespace kvq {
 
-// BITS: width of the main cache's codes, 4 or 2 (the sub-4-bit cache of KV4-RL,
-// "Future Directions", with the same INT8 sink / recent copies).
+// BITS: width of the main cache's codes, 4, 3 or 2 (the sub-4-bit caches of
+// KV4-RL, "Future Directions", with the same INT8 sink / recent copies).
 template <int BITS>
 __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
     const int lane = threadIdx.x & 63;
@@ -28,13 +28,13 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
     const int page = a.block_table[(int64_t)slot * a.bt_stride + p / a.P];
     const int row = p % a.P;
     uint8_t *base4 = a.int4_pool +
-        ((size_t)((int64_t)page * a.H + hk) * (a.P / kSub) + (row >> 4)) * (BITS == 2 ? kSub2Bytes : kSub4Bytes);
+        ((size_t)((int64_t)page * a.H + hk) * (a.P / kSub) + (row >> 4)) * main_sub_bytes(BITS);
 
     const uint16_t *krow = a.k + item * kHeadDim;
     const uint16_t *vrow = a.v + item * kHeadDim;
     const int vd0 = 32 * (lane >> 4) + (lane & 15);
     const TokenCodes tc = quantize_token(reinterpret_cast<const uint32_t *>(krow)[lane], vrow[vd0], vrow[vd0 + 16],
-                                         a.h, a.inv_sqrt_h, lane, BITS == 2 ? 3.0f : 15.0f);
+                                         a.h, a.inv_sqrt_h, lane, (float)((1 << BITS) - 1));
 
     // INT8 side cache: sinks and the final recent window
     const int L_after = a.len_after[slot];
@@ -44,6 +44,9 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendArgs a) {
                             : nullptr;
     if constexpr (BITS == 2) {
         store_token_int2(tc, base4, row & 15, lane);
+        if (write8) store_token_int8(tc, base8, e & 15, lane);
+    } else if constexpr (BITS == 3) {
+        store_token_int3(tc, base4, row & 15, lane);
         if (write8) store_token_int8(tc, base8, e & 15, lane);
     } else {
         store_token(tc, base4, row & 15, base8, e & 15, write8, lane);
@@ -55,6 +58,8 @@ hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream) {
     const int64_t blocks = (items + 3) / 4;
     if (a.bits == 2)
         hipLaunchKernelGGL(quant_append_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (a.bits == 3)
+        hipLaunchKernelGGL(quant_append_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(quant_append_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -34,7 +34,20 @@ constexpr int kSub2V = 512;
 constexpr int kSub2KP = 1024;
 constexpr int kSub2VP = 1088;
 
-__host__ __device__ inline int main_sub_bytes(int bits) { return bits == 2 ? kSub2Bytes : kSub4Bytes; }
+// 3-bit subblock (code_bits = 3): the low two bits of every code in the 2-bit
+// layouts (512 B keys, 512 B values), the high bits as a key plane and a value
+// plane of 256 B each, then the params; layouts in quant.h (store_token_int3).
+constexpr int kSub3Bytes = 1664;
+constexpr int kSub3K = 0;
+constexpr int kSub3V = 512;
+constexpr int kSub3KH = 1024;
+constexpr int kSub3VH = 1280;
+constexpr int kSub3KP = 1536;
+constexpr int kSub3VP = 1600;
+
+__host__ __device__ constexpr int main_sub_bytes(int bits) {
+    return bits == 2 ? kSub2Bytes : (bits == 3 ? kSub3Bytes : kSub4Bytes);
+}
 
 // Workspace of the decode attention: header, per-row cost prefix, partial pieces.
 constexpr int kPieceStride = 132;           // floats per (piece, query head): m, l, 0, 0, acc[128]

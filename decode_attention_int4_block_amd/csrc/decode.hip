@@ -530,7 +530,7 @@ template <int BITS>
 __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lookup &k, uint8_t *st,
                                   uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8, int lane) {
     if (c.r < c.rp.n4) {
-        constexpr uint32_t kSubBytes = BITS == 2 ? kSub2Bytes : kSub4Bytes;
+        constexpr uint32_t kSubBytes = (uint32_t)main_sub_bytes(BITS);
         const int pos0 = (c.rp.k0 + c.r) * 32;
         // subblock indices fit 32 bits (the descriptor check bounds the pools);
         // a page holds 1 << (logP - 4) subblocks of a KV head
@@ -556,6 +556,24 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
             if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP2, st + 4096);
             return;
         }
+        if constexpr (BITS == 3) {
+            // low planes as the 2-bit step (lanes 0-31 subblock A, 32-63 B, one
+            // load each for keys and values), high planes of A and B to stage
+            // offsets 2048 (keys) and 2560 (values), params as for INT4: five loads
+            const uint8_t *lo = lane < 32 ? baseA : baseB;
+            const uint32_t off = 16 * (uint32_t)(lane & 31);
+            dma16(lo + kSub3K, off, st + 0);
+            dma16(lo + kSub3V, off, st + 1024);
+            if (lane < 32) {
+                const uint8_t *hi = lane < 16 ? baseA : baseB;
+                const uint32_t offh = 16 * (uint32_t)(lane & 15);
+                dma16(hi + kSub3KH, offh, st + 2048);
+                dma16(hi + kSub3VH, offh, st + 2560);
+            }
+            const uint32_t offP3 = offP4 - kSub4KP + kSub3KP;
+            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP3, st + 4096);
+            return;
+        }
         dma16(baseA + kSub4K, offK, st + 0);
         dma16(baseB + kSub4K, offK, st + 1024);
         dma16(baseA + kSub4V, offV, st + 2048);
@@ -578,20 +596,25 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// main2: a 2-bit main-cache step (8 bytes of codes per lane and quarter).
+// main2: a 2- or 3-bit main-cache step (8 bytes of low-plane codes per lane and
+// quarter; at 3 bits the lane's high-plane dword goes to word 2).
 template <int GP, int BITS>
 __device__ inline StepRegs<GP> read_stage(const uint8_t *st, const LaneCtx<GP> &L, bool main2) {
     StepRegs<GP> r;
     const int lane = L.lane;
-    if (BITS == 2 && main2) {
+    if ((BITS == 2 || BITS == 3) && main2) {
         const u32x2 ka = *reinterpret_cast<const u32x2 *>(st + lane * 8);
         const u32x2 kb = *reinterpret_cast<const u32x2 *>(st + 512 + lane * 8);
         const u32x2 va = *reinterpret_cast<const u32x2 *>(st + 1024 + lane * 8);
         const u32x2 vb = *reinterpret_cast<const u32x2 *>(st + 1536 + lane * 8);
-        r.kA = u32x4{ka[0], ka[1], 0u, 0u};
-        r.kB = u32x4{kb[0], kb[1], 0u, 0u};
-        r.vA = u32x4{va[0], va[1], 0u, 0u};
-        r.vB = u32x4{vb[0], vb[1], 0u, 0u};
+        const uint32_t kha = BITS == 3 ? lds32(st + 2048 + 4 * lane) : 0u;
+        const uint32_t khb = BITS == 3 ? lds32(st + 2304 + 4 * lane) : 0u;
+        const uint32_t vha = BITS == 3 ? lds32(st + 2560 + 4 * lane) : 0u;
+        const uint32_t vhb = BITS == 3 ? lds32(st + 2816 + 4 * lane) : 0u;
+        r.kA = u32x4{ka[0], ka[1], kha, 0u};
+        r.kB = u32x4{kb[0], kb[1], khb, 0u};
+        r.vA = u32x4{va[0], va[1], vha, 0u};
+        r.vB = u32x4{vb[0], vb[1], vhb, 0u};
     } else {
         r.kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
         r.kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
@@ -670,6 +693,26 @@ __device__ inline uint32_t int2_field(uint32_t x, int f) {
 __device__ inline half8 int2_chunk(uint32_t x) {
     return pack8(int2_field(x, 0), int2_field(x, 1), int2_field(x, 2), int2_field(x, 3));
 }
+// 3-bit codes: a 2-bit field with its high bit ORed in at value 4 (bit 2 or 6
+// of each half, next to the field's two bits).  h holds the high bits of the
+// field's codes at bits 2 / 6 (+ 16) for the even / odd fields, or 8 above.
+__device__ inline uint32_t int3_field(uint32_t x, uint32_t h, int f) {
+    const uint32_t hs = f < 2 ? h : h >> 8;
+    return int2_field(x, f) | (hs & ((f & 1) ? 0x00400040u : 0x00040004u));
+}
+// key chunk i: the high-plane dword shifted to its bytes (key plane layout in quant.h)
+__device__ inline half8 int3_key_chunk(uint32_t x, uint32_t hh, int i) {
+    const uint32_t h = i == 0 ? hh : (i == 1 ? hh >> 1 : (i == 2 ? hh << 2 : hh << 1));
+    return pack8(int3_field(x, h, 0), int3_field(x, h, 1), int3_field(x, h, 2), int3_field(x, h, 3));
+}
+// value field f of low-plane dword cc, bytes (0, 2) (odd = false) or (1, 3): the
+// high byte's bit for (cc, f) moved to bit 2 / 6 (value plane layout in quant.h)
+__device__ inline uint32_t int3_value_field(uint32_t x, uint32_t hv, int cc, int f, bool odd) {
+    const int g = cc == 0 ? (0x7362 >> (4 * f)) & 15 : (0x5140 >> (4 * f)) & 15;
+    const int s = g + (odd ? 8 : 0) - ((f & 1) ? 6 : 2);
+    const uint32_t h = s >= 0 ? hv >> s : hv << (-s);
+    return int2_field(x, f) | (h & ((f & 1) ? 0x00400040u : 0x00040004u));
+}
 
 template <int GP, int BITS>
 __device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r, bool main2) {
@@ -678,12 +721,13 @@ __device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r
     KAcc<GP> k;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) k.dA[q] = k.dB[q] = zero4;
-    if (BITS == 2 && main2) {
+    if ((BITS == 2 || BITS == 3) && main2) {
         // chunk i: dword i / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const half8 ak = int2_chunk(r.kA[i >> 1] >> (8 * (i & 1)));
-            const half8 bk = int2_chunk(r.kB[i >> 1] >> (8 * (i & 1)));
+            const uint32_t xa = r.kA[i >> 1] >> (8 * (i & 1)), xb = r.kB[i >> 1] >> (8 * (i & 1));
+            const half8 ak = BITS == 3 ? int3_key_chunk(xa, r.kA[2], i) : int2_chunk(xa);
+            const half8 bk = BITS == 3 ? int3_key_chunk(xb, r.kB[2], i) : int2_chunk(xb);
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
                 k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
@@ -761,14 +805,18 @@ __device__ inline void vpart(SegCtx<GP> &c, const LaneCtx<GP> &L, const KOut<GP>
             for (int j = 0; j < 4; ++j) pop[q][4 + j] = pop[q][4 + j] * wb + pop[q][j] * wa;
         }
     }
-    if (BITS == 2 && !k.int8) {
+    if ((BITS == 2 || BITS == 3) && !k.int8) {
         // 2-bit values: dword cc, field f = dims 16 (4 cc + f) + n, tile 4 cc + f
+        // (3-bit: with the high bits of the lane's value-plane dword word 2)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                const half8 vt = pack8(int2_field(x, f), int2_field(x8, f), int2_field(y, f), int2_field(y8, f));
+                const half8 vt = BITS == 3
+                    ? pack8(int3_value_field(x, k.vA[2], cc, f, false), int3_value_field(x8, k.vA[2], cc, f, true),
+                            int3_value_field(y, k.vB[2], cc, f, false), int3_value_field(y8, k.vB[2], cc, f, true))
+                    : pack8(int2_field(x, f), int2_field(x8, f), int2_field(y, f), int2_field(y8, f));
 #pragma unroll
                 for (int q = 0; q < kQ; ++q) c.O[4 * cc + f] = mfma16(pop[q], vt, c.O[4 * cc + f]);
             }
@@ -1526,6 +1574,12 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
             case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
             default: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
         }
+    } else if (a.bits == 3) {
+        switch (group_class(a.g)) {
+            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+        }
     } else {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
             case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
@@ -1555,6 +1609,8 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out) {
     const void *fn;
     if (bits == 2)
         fn = cls == 4 ? split_fn<4, false, 2>() : (cls == 8 ? split_fn<8, false, 2>() : split_fn<16, false, 2>());
+    else if (bits == 3)
+        fn = cls == 4 ? split_fn<4, false, 3>() : (cls == 8 ? split_fn<8, false, 3>() : split_fn<16, false, 3>());
     else if (fused)
         fn = cls == 4 ? split_fn<4, true, 4>() : (cls == 8 ? split_fn<8, true, 4>() : split_fn<16, true, 4>());
     else

@@ -147,6 +147,59 @@ __device__ inline uint32_t int2_value_byte(uint8_t nib2, int lane) {
     return mine | (uint32_t)__shfl_xor((int)mine, 16, 64);
 }
 
+// 3-bit main cache: the low two bits of each code go to the 2-bit layouts
+// above; the high bits form two planes laid out for the decode kernel's
+// 2-bit unpacking, each byte (key: each dword) holding a single token so that
+// a token's stores touch no other token's bits.
+//
+// Key high plane: dword G 16 + t holds token t's dims 32 G .. 32 G + 31.  The
+// dim in 2-bit dword w, byte b, field f (dims 32 G + 16 w + j, b = {0, 2, 1,
+// 3}[j / 4], f = j % 4) sits at bit 16 (b / 2) + 4 f + (w ? 0 : 2) + (b % 2).
+__device__ inline int int3_key_hibit(int within) {
+    const int w = within >> 4, j = within & 15;
+    const int b = (0x3120 >> (4 * (j >> 2))) & 3;       // {0, 2, 1, 3}[j / 4]
+    return 16 * (b >> 1) + 4 * (j & 3) + (w ? 0 : 2) + (b & 1);
+}
+// Value high plane: dword G 16 + n, byte r = token 4 G + r; dim n + 16 f + 64 cc
+// sits at bit {2, 6, 3, 7}[f] (cc = 0) or {0, 4, 1, 5}[f] (cc = 1) of the byte.
+__device__ inline int int3_value_hibit(int cc, int f) {
+    return cc == 0 ? (0x7362 >> (4 * f)) & 15 : (0x5140 >> (4 * f)) & 15;
+}
+// This lane's high bits (codes of nibble pair k4 / v4) placed in the key dword of
+// its 32-dim group, and in the value byte of its value lane n.
+__device__ inline uint32_t int3_key_hibits(uint8_t k4, int lane) {
+    const int within = 2 * (lane & 15);
+    return (((uint32_t)k4 >> 2) & 1u) << int3_key_hibit(within) |
+           (((uint32_t)k4 >> 6) & 1u) << int3_key_hibit(within + 1);
+}
+__device__ inline uint32_t int3_value_hibits(uint8_t v4, int lane) {
+    const int c = lane >> 4, cc = c >> 1;
+    return (((uint32_t)v4 >> 2) & 1u) << int3_value_hibit(cc, (2 * c) & 3) |
+           (((uint32_t)v4 >> 6) & 1u) << int3_value_hibit(cc, (2 * c + 1) & 3);
+}
+
+// Stores of one token into a 3-bit subblock.  Call with the whole wave.
+__device__ inline void store_token_int3(const TokenCodes &t, uint8_t *base3, int tok, int lane) {
+    const uint32_t kb = int2_key_byte((uint8_t)(t.k4 & 0x33u), lane);
+    const uint32_t vb = int2_value_byte((uint8_t)(t.v4 & 0x33u), lane);
+    if ((lane & 1) == 0) base3[kSub3K + sub2_k_byte(tok, lane)] = (uint8_t)kb;
+    if (((lane >> 4) & 1) == 0) base3[kSub3V + sub2_v_byte(tok, lane)] = (uint8_t)vb;
+    uint32_t kh = int3_key_hibits(t.k4, lane);
+    kh |= (uint32_t)__shfl_xor((int)kh, 1, 64);
+    kh |= (uint32_t)__shfl_xor((int)kh, 2, 64);
+    kh |= (uint32_t)__shfl_xor((int)kh, 4, 64);
+    kh |= (uint32_t)__shfl_xor((int)kh, 8, 64);
+    uint32_t vh = int3_value_hibits(t.v4, lane);
+    vh |= (uint32_t)__shfl_xor((int)vh, 16, 64);
+    vh |= (uint32_t)__shfl_xor((int)vh, 32, 64);
+    if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(base3 + kSub3KH + 4 * ((lane >> 4) * 16 + tok)) = kh;
+    if (lane < 16) base3[kSub3VH + 4 * ((tok >> 2) * 16 + lane) + (tok & 3)] = (uint8_t)vh;
+    if (lane == 0) {
+        *reinterpret_cast<uint32_t *>(base3 + kSub3KP + 4 * tok) = t.kp4;
+        *reinterpret_cast<uint32_t *>(base3 + kSub3VP + 4 * tok) = t.vp4;
+    }
+}
+
 // Stores of one token into a 2-bit subblock.  Call with the whole wave.
 __device__ inline void store_token_int2(const TokenCodes &t, uint8_t *base2, int tok, int lane) {
     const uint32_t kb = int2_key_byte(t.k4, lane);

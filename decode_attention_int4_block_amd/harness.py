@@ -117,9 +117,9 @@ class DeviceWorkload:
 
     # --- inspection helpers (host copies of what the GPU wrote) ----------------
     def int4_subblocks(self, idx: np.ndarray) -> np.ndarray:
-        """Main-cache subblocks (INT4, or 2-bit when the cache holds 2-bit codes)."""
-        from .layout import SUB2_BYTES, SUB4_BYTES
-        nb = SUB2_BYTES if self.cache.code_bits == 2 else SUB4_BYTES
+        """Main-cache subblocks (INT4, or 3- / 2-bit when the cache holds such codes)."""
+        from .layout import SUB2_BYTES, SUB3_BYTES, SUB4_BYTES
+        nb = {2: SUB2_BYTES, 3: SUB3_BYTES}.get(self.cache.code_bits, SUB4_BYTES)
         pool = self.cache.int4_pool[: (self.cache.int4_pool.numel() // nb) * nb]
         t = torch.from_numpy(np.asarray(idx, np.int64)).to(self.device)
         return pool.view(-1, nb).index_select(0, t).cpu().numpy()

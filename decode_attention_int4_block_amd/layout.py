@@ -11,6 +11,7 @@ import numpy as np
 SUB = 16
 SUB4_BYTES = 2176
 SUB2_BYTES = 1152
+SUB3_BYTES = 1664
 SUB8_BYTES = 4224
 
 
@@ -81,24 +82,61 @@ def decode_sub8(blocks: np.ndarray, ent) -> dict:
     return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])
 
 
+def _int2_codes(blocks, t, kbase, vbase):
+    """Key and value codes [N, 128] of token t in the 2-bit layouts at kbase / vbase."""
+    rows = np.arange(blocks.shape[0])
+    kc = np.empty((blocks.shape[0], 128), np.uint8)
+    for d in range(128):
+        G, rem = d // 32, d % 32
+        w, i = rem // 16, rem % 16
+        byte = kbase + (G * 16 + t) * 8 + 4 * w + (0, 2, 1, 3)[i // 4]
+        kc[:, d] = (blocks[rows, byte] >> (2 * (i % 4))) & 3
+    G, r = t // 4, t % 4
+    vc = np.empty((blocks.shape[0], 128), np.uint8)
+    for d in range(128):
+        n, f, cc = d % 16, (d // 16) % 4, d // 64
+        byte = vbase + ((G * 16 + n) * 2 + cc) * 4 + r
+        vc[:, d] = (blocks[rows, byte] >> (2 * f)) & 3
+    return kc, vc
+
+
+def _params(blocks, t, kp_off, vp_off):
+    rows = np.arange(blocks.shape[0])[:, None]
+    kp = blocks[rows, kp_off + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    vp = blocks[rows, vp_off + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
+    return dict(k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])
+
+
 def decode_sub2(blocks: np.ndarray, tok) -> dict:
     """Codes and fp16 params of token `tok` (0..15) of each 2-bit subblock [N, 1152]."""
     blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, SUB2_BYTES)
     t = np.asarray(tok, dtype=np.int64).reshape(-1)
-    N = blocks.shape[0]
-    rows = np.arange(N)[:, None]
-    kc = np.empty((N, 128), np.uint8)
+    kc, vc = _int2_codes(blocks, t, 0, 512)
+    return dict(k=kc, v=vc, **_params(blocks, t, 1024, 1088))
+
+
+def decode_sub3(blocks: np.ndarray, tok) -> dict:
+    """Codes and fp16 params of token `tok` (0..15) of each 3-bit subblock [N, 1664]:
+    low two bits in the 2-bit layouts at 0 / 512, high bits in the key plane at
+    1024 (dword G 16 + t; dim in 2-bit dword w, byte b, field f at bit
+    16 (b / 2) + 4 f + (2 if w == 0 else 0) + b % 2) and the value plane at 1280
+    (dword G 16 + n, byte t % 4; dim n + 16 f + 64 cc at bit {2, 6, 3, 7}[f] or
+    {0, 4, 1, 5}[f] for cc = 0 / 1), params at 1536 / 1600."""
+    blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, SUB3_BYTES)
+    t = np.asarray(tok, dtype=np.int64).reshape(-1)
+    rows = np.arange(blocks.shape[0])
+    kc, vc = _int2_codes(blocks, t, 0, 512)
     for d in range(128):
         G, rem = d // 32, d % 32
         w, i = rem // 16, rem % 16
-        byte = (G * 16 + t) * 8 + 4 * w + (0, 2, 1, 3)[i // 4]
-        kc[:, d] = (blocks[rows[:, 0], byte] >> (2 * (i % 4))) & 3
+        b, f = (0, 2, 1, 3)[i // 4], i % 4
+        bit = 16 * (b // 2) + 4 * f + (2 if w == 0 else 0) + b % 2
+        off = 1024 + 4 * (G * 16 + t) + bit // 8
+        kc[:, d] |= ((blocks[rows, off] >> (bit % 8)) & 1) << 2
     G, r = t // 4, t % 4
-    vc = np.empty((N, 128), np.uint8)
     for d in range(128):
         n, f, cc = d % 16, (d // 16) % 4, d // 64
-        byte = 512 + ((G * 16 + n) * 2 + cc) * 4 + r
-        vc[:, d] = (blocks[rows[:, 0], byte] >> (2 * f)) & 3
-    kp = blocks[rows, 1024 + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
-    vp = blocks[rows, 1088 + 4 * t[:, None] + np.arange(4)[None, :]].copy().view(np.uint16)
-    return dict(k=kc, v=vc, k_scale=kp[:, 0], k_zero=kp[:, 1], v_scale=vp[:, 0], v_zero=vp[:, 1])
+        bit = ((2, 6, 3, 7) if cc == 0 else (0, 4, 1, 5))[f]
+        off = 1280 + 4 * (G * 16 + n) + r
+        vc[:, d] |= ((blocks[rows, off] >> bit) & 1) << 2
+    return dict(k=kc, v=vc, **_params(blocks, t, 1536, 1600))

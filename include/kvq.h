@@ -106,8 +106,25 @@
  *     [1024, 1088) key   (scale, zero) fp16 pairs, 4 bytes per token;
  *     [1088, 1152) value (scale, zero) fp16 pairs, 4 bytes per token.
  *   1152 bytes / (16 tokens * 256 elements) = 2.25 bits per element.
- *   kv_quant_append and kv_decode_attn serve both widths; kv_append_decode_attn
- *   and kv_prefill_attn return KVQ_ERR_UNSUPPORTED for code_bits = 2.
+ *
+ * 3-bit main cache (code_bits = 3; the same "Future Directions" item).  qmax = 7;
+ * subblock j starts at byte ((page * num_kv_heads + kv_head) * (P/16) + j) * 1664:
+ *     [   0,  512) the low two bits of every key code, in the 2-bit key layout;
+ *     [ 512, 1024) the low two bits of every value code, in the 2-bit value layout;
+ *     [1024, 1280) key high bits: dword G * 16 + t holds token t's dims
+ *                  32 G .. 32 G + 31; the dim in 2-bit dword w, byte b, bits
+ *                  2 f .. 2 f + 1 has its bit 2 at bit
+ *                  16 (b / 2) + 4 f + (w == 0 ? 2 : 0) + (b % 2);
+ *     [1280, 1536) value high bits: dword G * 16 + n, byte r = token 4 G + r;
+ *                  dim n + 16 f + 64 cc has its bit 2 at bit {2, 6, 3, 7}[f]
+ *                  (cc = 0) or {0, 4, 1, 5}[f] (cc = 1) of the byte;
+ *     [1536, 1600) key   (scale, zero) fp16 pairs, 4 bytes per token;
+ *     [1600, 1664) value (scale, zero) fp16 pairs, 4 bytes per token.
+ *   1664 bytes / (16 tokens * 256 elements) = 3.25 bits per element.
+ *
+ *   kv_quant_append and kv_decode_attn serve all three widths;
+ *   kv_append_decode_attn and kv_prefill_attn return KVQ_ERR_UNSUPPORTED for
+ *   code_bits = 2 or 3.
  *
  * Block table: int32 [num_slots][bt_stride], row = slot; entry i is the page
  * holding positions [i P, (i + 1) P) of that slot's sequence.  Only entries
@@ -147,9 +164,9 @@ typedef struct {
     void *int4_pool;         /* device, kvq_int4_pool_bytes(cache) bytes          */
     void *int8_pool;         /* device, kvq_int8_pool_bytes(cache) bytes; may be
                                 NULL only when sink + recent == 0                 */
-    int32_t code_bits;       /* width of the main (paged) cache's codes: 4, or 2
-                                for the 2-bit cache (0 means 4).  The INT8 side
-                                cache is the same for both.                       */
+    int32_t code_bits;       /* width of the main (paged) cache's codes: 4, or 3
+                                or 2 for the sub-4-bit caches (0 means 4).  The
+                                INT8 side cache is the same for all.              */
 } kvq_cache;
 
 /* Bytes of the INT4 pool / INT8 side cache for this descriptor (0 on bad input). */

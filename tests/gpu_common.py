@@ -63,8 +63,8 @@ def compare_cache(dw, b, positions=None):
     """Compare the GPU cache of row b with the oracle's quantization of the same
     bf16 inputs.  Returns dict of mismatch / tie counts; raises on a mismatch
     that is not near a rounding tie."""
-    from decode_attention_int4_block_amd.layout import (decode_sub2, decode_sub4, decode_sub8, sub4_index,
-                                                        sub8_index)
+    from decode_attention_int4_block_amd.layout import (decode_sub2, decode_sub3, decode_sub4, decode_sub8,
+                                                        sub4_index, sub8_index)
     wl = dw.wl
     cfg = wl.cfg
     L = int(wl.lengths[b])
@@ -72,7 +72,7 @@ def compare_cache(dw, b, positions=None):
     kb, vb = bf16_bits(k), bf16_bits(v)
     oc = quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent, main_bits=cfg.code_bits)
     qmain = (1 << cfg.code_bits) - 1
-    decode_main = decode_sub2 if cfg.code_bits == 2 else decode_sub4
+    decode_main = {2: decode_sub2, 3: decode_sub3}.get(cfg.code_bits, decode_sub4)
     H = cfg.num_kv_heads
     P = wl.page_size
     slot = int(wl.slots[b])

@@ -118,19 +118,25 @@ def test_prefill_argument_checks(lib):
     assert f(None, p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 1
 
 
-def test_two_bit_cache_sizes_and_limits(lib):
+def test_sub4bit_cache_sizes_and_limits(lib):
     d = _desc(code_bits=2)
     assert lib.kvq_int4_pool_bytes(ctypes.byref(d)) == 100 * 8 * 1 * 1152
     assert lib.kvq_int8_pool_bytes(ctypes.byref(d)) == 4 * 8 * 9 * 4224       # the INT8 side cache is unchanged
     # 1152 bytes hold 16 tokens x 256 K+V elements: 2.25 bits per element
     assert 1152 * 8 / (16 * 256) == 2.25
-    assert lib.kvq_int4_pool_bytes(ctypes.byref(_desc(code_bits=3))) == 0
+    # 3 bits: 1664 bytes (two low planes of 512, two high planes of 256, params)
+    # hold 16 tokens x 256 K+V elements: 3.25 bits per element
+    assert lib.kvq_int4_pool_bytes(ctypes.byref(_desc(code_bits=3))) == 100 * 8 * 1 * 1664
+    assert 1664 * 8 / (16 * 256) == 3.25
+    for bad in (1, 5, 8):
+        assert lib.kvq_int4_pool_bytes(ctypes.byref(_desc(code_bits=bad))) == 0
     assert lib.kvq_int4_pool_bytes(ctypes.byref(_desc(code_bits=0))) == 100 * 8 * 2176   # 0 means 4
     p = ctypes.c_void_p(0x3000)
-    d2 = _desc(int4_pool=0x1000, int8_pool=0x2000, code_bits=2)
-    # the fused append and the prefill attention serve the 4-bit cache only
-    assert lib.kv_append_decode_attn(ctypes.byref(d2), p, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
-    assert lib.kv_prefill_attn(ctypes.byref(d2), p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 3
+    for bits in (2, 3):
+        d2 = _desc(int4_pool=0x1000, int8_pool=0x2000, code_bits=bits)
+        # the fused append and the prefill attention serve the 4-bit cache only
+        assert lib.kv_append_decode_attn(ctypes.byref(d2), p, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
+        assert lib.kv_prefill_attn(ctypes.byref(d2), p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 3
 
 
 def test_status_strings(lib):

@@ -30,7 +30,7 @@ class WorkloadConfig:
     outlier_channels: int = 4
     outlier_scale: float = 20.0
     rope_base: float = 1.0e6
-    code_bits: int = 4      # width of the main cache's codes (4, or 2 for the sub-4-bit cache)
+    code_bits: int = 4      # width of the main cache's codes (4, or 3 or 2 for the sub-4-bit caches)
     extra: dict = field(default_factory=dict)
 
     @property
