@@ -43,7 +43,7 @@ constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
 constexpr int32_t kSegWeight = 2;
 constexpr int kMaxDevices = 64;
 // per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused
-// append, attention over the 2-bit cache)
+// append, attention over the 2-bit cache, attention over the 3-bit cache)
 std::atomic<int> g_max_workers[kMaxDevices][12];
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }

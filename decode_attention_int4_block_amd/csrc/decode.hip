@@ -525,7 +525,9 @@ __device__ inline void softmax_dense(SegCtx<GP> &c, const LaneCtx<GP> &L, const 
 //
 // A 2-bit main-cache step copies its two subblocks' 512-byte code areas verbatim
 // (32 lanes x 16 B; they are stored in lane order) to stage offsets 0 / 512
-// (keys) and 1024 / 1536 (values), and its params like an INT4 step.
+// (keys) and 1024 / 1536 (values), and its params like an INT4 step.  A 3-bit
+// step copies its low planes the same way and its two 256-byte high planes to
+// 2048 (keys) and 2560 (values).
 template <int BITS>
 __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lookup &k, uint8_t *st,
                                   uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8, int lane) {

@@ -54,7 +54,7 @@ __device__ inline uint32_t qparam_word(const QParams &p) {
 // Codes and params of one (token, KV head) in both caches.
 struct TokenCodes {
     uint8_t k4, v4;             // this lane's main-cache codes as a nibble pair (key dims 2l, 2l+1;
-                                // value dims n+32c, n+16+32c): the INT4 byte, or two 2-bit codes
+                                // value dims n+32c, n+16+32c): the INT4 byte, or two 3- / 2-bit codes
     uint8_t k8lo, k8hi;         // INT8 key codes split into nibble planes
     uint8_t v8lo, v8hi;
     uint32_t kp4, vp4, kp8, vp8; // (scale, zero) fp16 pairs, wave-uniform
@@ -62,7 +62,7 @@ struct TokenCodes {
 
 // kw: this lane's bf16 pair of key dims 2l, 2l+1; vlo, vhi: its value dims
 // n + 32c and n + 16 + 32c (bf16 bits).  qmain: levels - 1 of the main cache
-// (15, or 3 for the 2-bit cache).
+// (15, or 7 / 3 for the 3- / 2-bit caches).
 __device__ inline TokenCodes quantize_token(uint32_t kw, uint32_t vlo, uint32_t vhi, int h, float inv_sqrt_h,
                                             int lane, float qmain = 15.0f) {
 #pragma clang fp contract(off)
