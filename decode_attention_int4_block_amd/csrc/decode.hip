@@ -283,7 +283,7 @@ __device__ inline void fetch_pages(const DecodeArgs &a, const RowRegs &R, int64_
     // lanes [0, kPgHalf) fill pa, [kPgHalf, 2 kPgHalf) pb; the others write nothing
     if (lane < 2 * kPgHalf) {
         if (src != nullptr)
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)pg_half, 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)pg_half, 4, 0, kCachePolicyNonTemporal);
         else
             pg_half[lane] = val;
     }
@@ -319,7 +319,7 @@ __device__ inline void issue_query(const DecodeArgs &a, int b, int hk, const Lan
     const uint16_t *qp = a.q + ((int64_t)b * a.Hq + (int64_t)hk * a.g + head) * kHeadDim + 32 * L.G + V * L.part;
 #pragma unroll
     for (int v = 0; v < QRing<GP>::kLoads; ++v)
-        __builtin_amdgcn_global_load_lds(qp + 8 * v, (lds_ptr)(slot + 1024 * v), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qp + 8 * v, (lds_ptr)(slot + 1024 * v), 16, 0, kCachePolicyNonTemporal);
 }
 
 template <int GP>
@@ -548,14 +548,14 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
         if constexpr (BITS == 2) {
             const uint32_t off = 16 * (uint32_t)lane;
             if (lane < 32) {
-                dma16(baseA + kSub2K, off, st + 0);
-                dma16(baseB + kSub2K, off, st + 512);
-                dma16(baseA + kSub2V, off, st + 1024);
-                dma16(baseB + kSub2V, off, st + 1536);
+                dma16_stream(baseA + kSub2K, off, st + 0);
+                dma16_stream(baseB + kSub2K, off, st + 512);
+                dma16_stream(baseA + kSub2V, off, st + 1024);
+                dma16_stream(baseB + kSub2V, off, st + 1536);
             }
             // params: as for INT4, from the 2-bit subblock's param areas
             const uint32_t offP2 = offP4 - kSub4KP + kSub2KP;
-            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP2, st + 4096);
+            if (lane < 16) dma16_stream((lane & 4) ? baseB : baseA, offP2, st + 4096);
             return;
         }
         if constexpr (BITS == 3) {
@@ -564,34 +564,34 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
             // offsets 2048 (keys) and 2560 (values), params as for INT4: five loads
             const uint8_t *lo = lane < 32 ? baseA : baseB;
             const uint32_t off = 16 * (uint32_t)(lane & 31);
-            dma16(lo + kSub3K, off, st + 0);
-            dma16(lo + kSub3V, off, st + 1024);
+            dma16_stream(lo + kSub3K, off, st + 0);
+            dma16_stream(lo + kSub3V, off, st + 1024);
             if (lane < 32) {
                 const uint8_t *hi = lane < 16 ? baseA : baseB;
                 const uint32_t offh = 16 * (uint32_t)(lane & 15);
-                dma16(hi + kSub3KH, offh, st + 2048);
-                dma16(hi + kSub3VH, offh, st + 2560);
+                dma16_stream(hi + kSub3KH, offh, st + 2048);
+                dma16_stream(hi + kSub3VH, offh, st + 2560);
             }
             const uint32_t offP3 = offP4 - kSub4KP + kSub3KP;
-            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP3, st + 4096);
+            if (lane < 16) dma16_stream((lane & 4) ? baseB : baseA, offP3, st + 4096);
             return;
         }
-        dma16(baseA + kSub4K, offK, st + 0);
-        dma16(baseB + kSub4K, offK, st + 1024);
-        dma16(baseA + kSub4V, offV, st + 2048);
-        dma16(baseB + kSub4V, offV, st + 3072);
-        if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP4, st + 4096);
+        dma16_stream(baseA + kSub4K, offK, st + 0);
+        dma16_stream(baseB + kSub4K, offK, st + 1024);
+        dma16_stream(baseA + kSub4V, offV, st + 2048);
+        dma16_stream(baseB + kSub4V, offV, st + 3072);
+        if (lane < 16) dma16_stream((lane & 4) ? baseB : baseA, offP4, st + 4096);
     } else {
         // the low-nibble planes take the place of subblock A, the high-nibble
         // planes that of subblock B
         const uint32_t sub = (uint32_t)(c.r - c.rp.n4);
         const uint32_t idx = ((uint32_t)k.slot * (uint32_t)a.H + (uint32_t)c.hk) * (uint32_t)a.nr8 + sub;
         const uint8_t *base = a.int8_pool + (uint64_t)idx * kSub8Bytes;
-        dma16(base + kSub8KLo, offK, st + 0);
-        dma16(base + kSub8KHi, offK, st + 1024);
-        dma16(base + kSub8VLo, offV, st + 2048);
-        dma16(base + kSub8VHi, offV, st + 3072);
-        if (lane < 16 && (lane & 4) == 0) dma16(base, offP8, st + 4096);
+        dma16_stream(base + kSub8KLo, offK, st + 0);
+        dma16_stream(base + kSub8KHi, offK, st + 1024);
+        dma16_stream(base + kSub8VLo, offV, st + 2048);
+        dma16_stream(base + kSub8VHi, offV, st + 3072);
+        if (lane < 16 && (lane & 4) == 0) dma16_stream(base, offP8, st + 4096);
     }
 }
 
@@ -966,10 +966,10 @@ __device__ inline void issue_new_token(const DecodeArgs &a, const RowRegs &R, co
                                        int lane) {
     const int64_t row = (int64_t)c.b * a.H + c.hk;
     const uint16_t *src = (lane < 16 ? a.k_new : a.v_new) + row * kHeadDim + 8 * (lane & 15);
-    if (lane < 32) __builtin_amdgcn_global_load_lds(src, (lds_ptr)slot, 16, 0, 0);
+    if (lane < 32) __builtin_amdgcn_global_load_lds(src, (lds_ptr)slot, 16, 0, kCachePolicyNonTemporal);
     const int p = row_len(a, R, c.b) - 1;
     const int32_t *pe = a.block_table + (int64_t)row_slot(a, R, c.b) * a.bt_stride + (p >> a.logP);
-    if (lane == 0) __builtin_amdgcn_global_load_lds(pe, (lds_ptr)(slot + kKvPage), 4, 0, 0);
+    if (lane == 0) __builtin_amdgcn_global_load_lds(pe, (lds_ptr)(slot + kKvPage), 4, 0, kCachePolicyNonTemporal);
 }
 
 __device__ inline void append_new_token(const DecodeArgs &a, const RowRegs &R, const Cursor &c,
