@@ -90,7 +90,7 @@ def test_fused_protection_budgets(s, w):
     _check_pair(sep, fus, rows, f"budget s={s} w={w}")
 
 
-@pytest.mark.parametrize("g,Hkv", [(1, 4), (4, 2), (8, 2), (16, 1)])
+@pytest.mark.parametrize("g,Hkv", [(1, 4), (3, 2), (4, 2), (6, 2), (8, 2), (11, 1), (16, 1)])
 def test_fused_query_groups(g, Hkv):
     cfg = small_config([1, 20, 77, 160, 700], Hq=g * Hkv, Hkv=Hkv, h=128, s=4, w=64, seed=1300 + g)
     rows = list(range(cfg.batch))

@@ -68,7 +68,8 @@ def test_small_paged_cache_and_attention(h):
     assert err <= ATOL and err_lse <= ATOL
 
 
-@pytest.mark.parametrize("g,Hkv", [(1, 4), (2, 2), (4, 2), (8, 2), (16, 1)])
+# non-power-of-two groups pad to the next MFMA column count and leave columns unused
+@pytest.mark.parametrize("g,Hkv", [(1, 4), (2, 2), (3, 2), (4, 2), (5, 1), (7, 2), (8, 2), (12, 1), (16, 1)])
 def test_query_groups(g, Hkv):
     cfg = small_config([1, 40, 300, 777], Hq=g * Hkv, Hkv=Hkv, h=128, s=4, w=64, seed=200 + g)
     rows = list(range(cfg.batch))

@@ -64,7 +64,7 @@ def test_sub4bit_protection_budgets(s, w, bits):
 
 
 @pytest.mark.parametrize("bits", [2, 3])
-@pytest.mark.parametrize("g,Hkv", [(1, 4), (4, 2), (8, 2), (16, 1)])
+@pytest.mark.parametrize("g,Hkv", [(1, 4), (3, 2), (4, 2), (7, 1), (8, 2), (16, 1)])
 def test_sub4bit_query_groups(g, Hkv, bits):
     _check(small_config([1, 20, 77, 160, 700], Hq=g * Hkv, Hkv=Hkv, h=128, s=4, w=64, seed=3300 + g + 40 * bits,
                         bits=bits), f"{bits}-bit g={g}")
