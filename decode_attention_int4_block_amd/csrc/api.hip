@@ -42,9 +42,9 @@ constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
 // segment as this many units more than it streams.
 constexpr int32_t kSegWeight = 2;
 constexpr int kMaxDevices = 64;
-// per device, group class (g <= 4, <= 8, <= 16) and kernel (attention only, fused
-// append, attention over the 2-bit cache, attention over the 3-bit cache)
-std::atomic<int> g_max_workers[kMaxDevices][12];
+// per device, group class (g <= 4, <= 8, <= 16), main-cache width (4, 2, 3 bits)
+// and kernel (attention only, fused append)
+std::atomic<int> g_max_workers[kMaxDevices][18];
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -84,7 +84,7 @@ kvq_status max_workers(int g, bool fused, int bits, int *out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
-    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (bits == 2 ? 6 : (bits == 3 ? 9 : (fused ? 3 : 0)));
+    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (bits == 2 ? 6 : (bits == 3 ? 12 : 0)) + (fused ? 3 : 0);
     int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
         hipError_t e = kvq::decode_max_workers(g, fused, bits, &v);
@@ -177,7 +177,6 @@ size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num
     int workers = 0, workers_fused = 0;
     const int bits = bits_of(c);
     if (max_workers(g, false, bits, &workers) != KVQ_OK) return 0;
-    if (bits != 4) return ws_layout(c, B, g, workers).total;     // no fused kernel below 4 bits
     if (max_workers(g, true, bits, &workers_fused) != KVQ_OK) return 0;
     const size_t a = ws_layout(c, B, g, workers).total, b = ws_layout(c, B, g, workers_fused).total;
     return a > b ? a : b;
@@ -208,8 +207,6 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
-    if (fused && bits_of(c) != 4)
-        return fail(KVQ_ERR_UNSUPPORTED, "the fused append serves the 4-bit cache only (code_bits %d)", c->code_bits);
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
     int workers = 0;
     st = max_workers(g, fused, bits_of(c), &workers);

@@ -972,6 +972,7 @@ __device__ inline void issue_new_token(const DecodeArgs &a, const RowRegs &R, co
     if (lane == 0) __builtin_amdgcn_global_load_lds(pe, (lds_ptr)(slot + kKvPage), 4, 0, kCachePolicyNonTemporal);
 }
 
+template <int BITS>
 __device__ inline void append_new_token(const DecodeArgs &a, const RowRegs &R, const Cursor &c,
                                         const uint8_t *kv, uint8_t *st, int lane) {
     const int vd0 = 32 * (lane >> 4) + (lane & 15);
@@ -979,16 +980,25 @@ __device__ inline void append_new_token(const DecodeArgs &a, const RowRegs &R, c
     const uint32_t vlo = *reinterpret_cast<const uint16_t *>(kv + 256 + 2 * vd0);
     const uint32_t vhi = *reinterpret_cast<const uint16_t *>(kv + 256 + 2 * (vd0 + 16));
     const int page = uni((int)lds32(kv + kKvPage));
-    const TokenCodes tc = quantize_token(kw, vlo, vhi, a.h, a.inv_sqrt_h, lane);
+    const TokenCodes tc = quantize_token(kw, vlo, vhi, a.h, a.inv_sqrt_h, lane, (float)((1 << BITS) - 1));
     const int p = row_len(a, R, c.b) - 1;
     uint8_t *base4 = a.int4_pool +
-        ((size_t)((int64_t)page * a.H + c.hk) * (a.P >> 4) + ((p & (a.P - 1)) >> 4)) * kSub4Bytes;
+        ((size_t)((int64_t)page * a.H + c.hk) * (a.P >> 4) + ((p & (a.P - 1)) >> 4)) * main_sub_bytes(BITS);
     const bool int8 = c.rp.rn >= c.rp.n4;
     const int e = ((c.rp.rn - c.rp.n4) << 4) + c.rp.tn;
     uint8_t *base8 = int8
         ? a.int8_pool + ((size_t)((int64_t)row_slot(a, R, c.b) * a.H + c.hk) * a.nr8 + (e >> 4)) * kSub8Bytes
         : nullptr;
-    store_token(tc, base4, p & 15, base8, e & 15, int8, lane);
+    Sub2Token s2 = {0u, 0u, 0u, 0u};
+    if constexpr (BITS == 4) {
+        store_token(tc, base4, p & 15, base8, e & 15, int8, lane);
+    } else {
+        s2 = sub2_token<BITS>(tc, lane);
+        put_sub2_token<BITS>(s2, tc, base4 + kSub2K, base4 + (BITS == 3 ? kSub3V : kSub2V), base4 + kSub3KH,
+                             base4 + kSub3VH, base4 + (BITS == 3 ? kSub3KP : kSub2KP),
+                             base4 + (BITS == 3 ? kSub3VP : kSub2VP), p & 15, lane);
+        if (int8) store_token_int8(tc, base8, e & 15, lane);
+    }
     // the stage holds the step as the cache was before this token.  Key bytes
     // sit by lane (stage byte 256 (l / 16) + 16 t + l % 16 is subblock byte
     // 64 t + l), value bytes as in the subblock, params at kStKP / kStVP + 4 t.
@@ -1004,6 +1014,13 @@ __device__ inline void append_new_token(const DecodeArgs &a, const RowRegs &R, c
             *reinterpret_cast<uint32_t *>(st + kStKP + 4 * t) = tc.kp8;
             *reinterpret_cast<uint32_t *>(st + kStVP + 4 * t) = tc.vp8;
         }
+    } else if constexpr (BITS != 4) {
+        // a 2- / 3-bit step holds each area of subblocks A and B verbatim:
+        // low planes at 512 sb (keys) and 1024 + 512 sb (values), high planes
+        // at 2048 + 256 sb and 2560 + 256 sb, params as above
+        const int sb = t >> 4;
+        put_sub2_token<BITS>(s2, tc, st + 512 * sb, st + 1024 + 512 * sb, st + 2048 + 256 * sb, st + 2560 + 256 * sb,
+                             st + kStKP + 64 * sb, st + kStVP + 64 * sb, t & 15, lane);
     } else {
         const int sb = t >> 4, tt = t & 15;
         st[1024 * sb + 256 * (lane >> 4) + 16 * tt + (lane & 15)] = tc.k4;
@@ -1288,7 +1305,7 @@ void decode_split_kernel(DecodeArgs a) {
     if (P.u < u_end) look = read_pages(P);
     wait_vm_steps(issued - 1);
     if constexpr (APPEND) {
-        if (C.r == C.rp.rn) append_new_token(a, R, C, kvring, smem, lane);
+        if (C.r == C.rp.rn) append_new_token<BITS>(a, R, C, kvring, smem, lane);
     }
     StepRegs<GP> r = read_stage<GP, BITS>(smem, L, C.r < C.rp.n4);
     QRing<GP> qr = read_query<GP>(qring, lane);     // the first step opens a segment
@@ -1326,7 +1343,7 @@ void decode_split_kernel(DecodeArgs a) {
             wait_vm_steps(issued - i - 2);
             if constexpr (APPEND) {
                 if (C.r == C.rp.rn)
-                    append_new_token(a, R, C, kvring + snxt * kKvBytes, smem + snxt * kStageBytes, lane);
+                    append_new_token<BITS>(a, R, C, kvring + snxt * kKvBytes, smem + snxt * kStageBytes, lane);
             }
             r = read_stage<GP, BITS>(smem + snxt * kStageBytes, L, C.r < C.rp.n4);
             if (!open) qr = read_query<GP>(qring + snxt * QRing<GP>::kBytes, lane);
@@ -1570,17 +1587,22 @@ static int group_class(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
     const bool fused = a.k_new != nullptr;
     if (a.bits == 2) {
-        // the fused append is built for the 4-bit cache only (the host rejects it here)
-        switch (group_class(a.g)) {
+        switch (group_class(a.g) + (fused ? 1 : 0)) {
             case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
             case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
         }
     } else if (a.bits == 3) {
-        switch (group_class(a.g)) {
+        switch (group_class(a.g) + (fused ? 1 : 0)) {
             case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 3>), dim3(grid), dim3(64), 0, stream, a); break;
             case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 3>), dim3(grid), dim3(64), 0, stream, a); break;
         }
     } else {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
@@ -1609,8 +1631,12 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out) {
     int per_cu = 0;
     const int cls = group_class(g);
     const void *fn;
-    if (bits == 2)
+    if (bits == 2 && fused)
+        fn = cls == 4 ? split_fn<4, true, 2>() : (cls == 8 ? split_fn<8, true, 2>() : split_fn<16, true, 2>());
+    else if (bits == 2)
         fn = cls == 4 ? split_fn<4, false, 2>() : (cls == 8 ? split_fn<8, false, 2>() : split_fn<16, false, 2>());
+    else if (bits == 3 && fused)
+        fn = cls == 4 ? split_fn<4, true, 3>() : (cls == 8 ? split_fn<8, true, 3>() : split_fn<16, true, 3>());
     else if (bits == 3)
         fn = cls == 4 ? split_fn<4, false, 3>() : (cls == 8 ? split_fn<8, false, 3>() : split_fn<16, false, 3>());
     else if (fused)

@@ -178,38 +178,65 @@ __device__ inline uint32_t int3_value_hibits(uint8_t v4, int lane) {
            (((uint32_t)v4 >> 6) & 1u) << int3_value_hibit(cc, (2 * c + 1) & 3);
 }
 
+// One token's bytes in the 2- / 3-bit layouts, as this lane holds them: the
+// 2-bit key byte (valid in even lanes) and value byte (lanes with bit 4
+// clear), and at 3 bits the key high-plane dword (valid in lanes 16 G) and the
+// value high-plane byte (lanes 0-15).  Call with the whole wave.
+struct Sub2Token {
+    uint32_t kb, vb, kh, vh;
+};
+
+template <int BITS>
+__device__ inline Sub2Token sub2_token(const TokenCodes &t, int lane) {
+    const uint8_t lo2 = BITS == 3 ? 0x33u : 0xFFu;     // at 3 bits the low planes take bits 0-1
+    Sub2Token s;
+    s.kb = int2_key_byte((uint8_t)(t.k4 & lo2), lane);
+    s.vb = int2_value_byte((uint8_t)(t.v4 & lo2), lane);
+    s.kh = s.vh = 0u;
+    if constexpr (BITS == 3) {
+        uint32_t kh = int3_key_hibits(t.k4, lane);
+        kh |= (uint32_t)__shfl_xor((int)kh, 1, 64);
+        kh |= (uint32_t)__shfl_xor((int)kh, 2, 64);
+        kh |= (uint32_t)__shfl_xor((int)kh, 4, 64);
+        kh |= (uint32_t)__shfl_xor((int)kh, 8, 64);
+        uint32_t vh = int3_value_hibits(t.v4, lane);
+        vh |= (uint32_t)__shfl_xor((int)vh, 16, 64);
+        vh |= (uint32_t)__shfl_xor((int)vh, 32, 64);
+        s.kh = kh;
+        s.vh = vh;
+    }
+    return s;
+}
+
+// Places token tok (0-15) of a 2- / 3-bit subblock whose areas start at the
+// given addresses: key and value low planes, (3 bits) key and value high
+// planes, key and value params.  The same bytes go to the cache and to a
+// stage copy of the subblock, whose areas sit elsewhere.
+template <int BITS>
+__device__ inline void put_sub2_token(const Sub2Token &s, const TokenCodes &t, uint8_t *k, uint8_t *v, uint8_t *kh,
+                                      uint8_t *vh, uint8_t *kp, uint8_t *vp, int tok, int lane) {
+    if ((lane & 1) == 0) k[sub2_k_byte(tok, lane)] = (uint8_t)s.kb;
+    if (((lane >> 4) & 1) == 0) v[sub2_v_byte(tok, lane)] = (uint8_t)s.vb;
+    if constexpr (BITS == 3) {
+        if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(kh + 4 * ((lane >> 4) * 16 + tok)) = s.kh;
+        if (lane < 16) vh[4 * ((tok >> 2) * 16 + lane) + (tok & 3)] = (uint8_t)s.vh;
+    }
+    if (lane == 0) {
+        *reinterpret_cast<uint32_t *>(kp + 4 * tok) = t.kp4;
+        *reinterpret_cast<uint32_t *>(vp + 4 * tok) = t.vp4;
+    }
+}
+
 // Stores of one token into a 3-bit subblock.  Call with the whole wave.
 __device__ inline void store_token_int3(const TokenCodes &t, uint8_t *base3, int tok, int lane) {
-    const uint32_t kb = int2_key_byte((uint8_t)(t.k4 & 0x33u), lane);
-    const uint32_t vb = int2_value_byte((uint8_t)(t.v4 & 0x33u), lane);
-    if ((lane & 1) == 0) base3[kSub3K + sub2_k_byte(tok, lane)] = (uint8_t)kb;
-    if (((lane >> 4) & 1) == 0) base3[kSub3V + sub2_v_byte(tok, lane)] = (uint8_t)vb;
-    uint32_t kh = int3_key_hibits(t.k4, lane);
-    kh |= (uint32_t)__shfl_xor((int)kh, 1, 64);
-    kh |= (uint32_t)__shfl_xor((int)kh, 2, 64);
-    kh |= (uint32_t)__shfl_xor((int)kh, 4, 64);
-    kh |= (uint32_t)__shfl_xor((int)kh, 8, 64);
-    uint32_t vh = int3_value_hibits(t.v4, lane);
-    vh |= (uint32_t)__shfl_xor((int)vh, 16, 64);
-    vh |= (uint32_t)__shfl_xor((int)vh, 32, 64);
-    if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(base3 + kSub3KH + 4 * ((lane >> 4) * 16 + tok)) = kh;
-    if (lane < 16) base3[kSub3VH + 4 * ((tok >> 2) * 16 + lane) + (tok & 3)] = (uint8_t)vh;
-    if (lane == 0) {
-        *reinterpret_cast<uint32_t *>(base3 + kSub3KP + 4 * tok) = t.kp4;
-        *reinterpret_cast<uint32_t *>(base3 + kSub3VP + 4 * tok) = t.vp4;
-    }
+    put_sub2_token<3>(sub2_token<3>(t, lane), t, base3 + kSub3K, base3 + kSub3V, base3 + kSub3KH, base3 + kSub3VH,
+                      base3 + kSub3KP, base3 + kSub3VP, tok, lane);
 }
 
 // Stores of one token into a 2-bit subblock.  Call with the whole wave.
 __device__ inline void store_token_int2(const TokenCodes &t, uint8_t *base2, int tok, int lane) {
-    const uint32_t kb = int2_key_byte(t.k4, lane);
-    const uint32_t vb = int2_value_byte(t.v4, lane);
-    if ((lane & 1) == 0) base2[kSub2K + sub2_k_byte(tok, lane)] = (uint8_t)kb;
-    if (((lane >> 4) & 1) == 0) base2[kSub2V + sub2_v_byte(tok, lane)] = (uint8_t)vb;
-    if (lane == 0) {
-        *reinterpret_cast<uint32_t *>(base2 + kSub2KP + 4 * tok) = t.kp4;
-        *reinterpret_cast<uint32_t *>(base2 + kSub2VP + 4 * tok) = t.vp4;
-    }
+    put_sub2_token<2>(sub2_token<2>(t, lane), t, base2 + kSub2K, base2 + kSub2V, nullptr, nullptr, base2 + kSub2KP,
+                      base2 + kSub2VP, tok, lane);
 }
 
 // INT8 ring copy of one token (when write8).

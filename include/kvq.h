@@ -122,9 +122,8 @@
  *     [1600, 1664) value (scale, zero) fp16 pairs, 4 bytes per token.
  *   1664 bytes / (16 tokens * 256 elements) = 3.25 bits per element.
  *
- *   kv_quant_append and kv_decode_attn serve all three widths;
- *   kv_append_decode_attn and kv_prefill_attn return KVQ_ERR_UNSUPPORTED for
- *   code_bits = 2 or 3.
+ *   kv_quant_append, kv_decode_attn and kv_append_decode_attn serve all three
+ *   widths; kv_prefill_attn returns KVQ_ERR_UNSUPPORTED for code_bits = 2 or 3.
  *
  * Block table: int32 [num_slots][bt_stride], row = slot; entry i is the page
  * holding positions [i P, (i + 1) P) of that slot's sequence.  Only entries

@@ -134,8 +134,7 @@ def test_sub4bit_cache_sizes_and_limits(lib):
     p = ctypes.c_void_p(0x3000)
     for bits in (2, 3):
         d2 = _desc(int4_pool=0x1000, int8_pool=0x2000, code_bits=bits)
-        # the fused append and the prefill attention serve the 4-bit cache only
-        assert lib.kv_append_decode_attn(ctypes.byref(d2), p, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
+        # the prefill attention serves the 4-bit cache only
         assert lib.kv_prefill_attn(ctypes.byref(d2), p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 3
 
 

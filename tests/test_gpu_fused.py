@@ -106,15 +106,15 @@ def test_fused_page_sizes_and_empty_rows():
         _check_pair(sep, fus, rows, f"P={P} with empty rows")
 
 
-@pytest.mark.parametrize("s,w", [(4, 32), (4, 0), (0, 16)])
-def test_fused_consecutive_steps(s, w):
+@pytest.mark.parametrize("s,w,bits", [(4, 32, 4), (4, 0, 4), (0, 16, 4), (4, 32, 3), (0, 16, 2)])
+def test_fused_consecutive_steps(s, w, bits):
     """Forty steps in a row, one new token per row each: the recent ring wraps
     and positions move from the INT8 window into the INT4 region."""
     from decode_attention_int4_block_amd import kv_append_decode_attn, kv_decode_attn, kv_quant_append
     from workloads import seq_kv
     n = 40
     final = [41, 60, 77, 100, 140, 300]
-    cfg = small_config(final, h=128, s=s, w=w, seed=1500 + s + w)
+    cfg = small_config(final, h=128, s=s, w=w, seed=1500 + s + w + bits, bits=bits)
     rows = list(range(cfg.batch))
     sep = make_device_workload(cfg, keep=rows, poison=True, prefill=False)
     fus = make_device_workload(cfg, keep=rows, poison=True, prefill=False)
@@ -149,7 +149,36 @@ def test_fused_consecutive_steps(s, w):
         assert torch.equal(sep.cache.int4_pool, fus.cache.int4_pool), f"step {j}: INT4 pool differs"
         assert torch.equal(sep.cache.int8_pool, fus.cache.int8_pool), f"step {j}: INT8 pool differs"
         assert torch.equal(sep.out, fus.out) and torch.equal(sep.lse, fus.lse), f"step {j}: outputs differ"
-    _check_pair(sep, fus, rows, f"{n} consecutive steps s={s} w={w}")
+    _check_pair(sep, fus, rows, f"{n} consecutive steps s={s} w={w} {bits}-bit")
+
+
+# 2- and 3-bit main caches: the fused kernel stores the token in the 2-bit
+# layouts (plus the high planes at 3 bits) and patches its stage copy of them
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("g,Hkv", [(4, 2), (7, 1), (16, 1)])
+def test_fused_sub4bit_edge_lengths(bits, g, Hkv):
+    cfg = small_config(EDGE, Hq=g * Hkv, Hkv=Hkv, h=128, s=4, w=32, seed=1600 + 20 * bits + g, bits=bits)
+    rows = list(range(cfg.batch))
+    sep, fus = _pair(cfg, keep=rows)
+    _check_pair(sep, fus, rows, f"{bits}-bit g={g} edge lengths")
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("s,w", [(0, 0), (16, 0), (0, 16), (4, 4000)])
+def test_fused_sub4bit_protection_budgets(bits, s, w):
+    cfg = small_config([1, 17, 33, 160, 700], h=128, s=s, w=w, seed=1700 + s + w + bits, bits=bits)
+    rows = list(range(cfg.batch))
+    sep, fus = _pair(cfg, keep=rows)
+    _check_pair(sep, fus, rows, f"{bits}-bit s={s} w={w}")
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_fused_sub4bit_page_sizes_and_empty_rows(bits):
+    for P in (16, 64):
+        cfg = small_config([0, 1, 70, 1500, 0, 2049], P=P, h=64, s=4, w=128, seed=1800 + P + bits, bits=bits)
+        rows = list(range(cfg.batch))
+        sep, fus = _pair(cfg, keep=[b for b in rows if cfg.length_args[b] > 0])
+        _check_pair(sep, fus, rows, f"{bits}-bit P={P} with empty rows")
 
 
 def test_fused_full_size_step():
