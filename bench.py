@@ -212,9 +212,7 @@ def measure_variants(torch, cfg, steps, warmup, only=None):
             dw.decode_step()
             if ev:
                 ev[2].record()
-        # the fused append serves the 4-bit cache only
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)] \
-            if vcfg.code_bits == 4 else []
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i in range(len(fev)):
             dw.cache = copies[i % len(copies)]
             fev[i][0].record()
