@@ -181,9 +181,12 @@ def test_fused_sub4bit_page_sizes_and_empty_rows(bits):
         _check_pair(sep, fus, rows, f"{bits}-bit P={P} with empty rows")
 
 
-def test_fused_full_size_step():
-    """The 256-row Qwen3-8B batch in the benchmark's launch configuration."""
-    cfg = get_config("qwen3_8b_async_256")
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_fused_full_size_step(bits):
+    """The 256-row Qwen3-8B batch in the benchmark's launch configuration
+    (and the same batch over the 3- and 2-bit main caches)."""
+    import dataclasses
+    cfg = dataclasses.replace(get_config("qwen3_8b_async_256"), code_bits=bits)
     from workloads import build_workload
     wl = build_workload(cfg)
     L = wl.lengths
@@ -193,7 +196,10 @@ def test_fused_full_size_step():
     sep, fus = _pair(cfg, keep=rows, gen_device="cuda")
     assert torch.equal(sep.cache.int4_pool, fus.cache.int4_pool)
     assert torch.equal(sep.cache.int8_pool, fus.cache.int8_pool)
-    assert torch.equal(sep.out, fus.out) and torch.equal(sep.lse, fus.lse)
+    if _workers(sep) == _workers(fus):
+        assert torch.equal(sep.out, fus.out) and torch.equal(sep.lse, fus.lse)
+    else:
+        assert float((sep.out - fus.out).abs().max()) <= 1e-5
     err, err_lse, _ = compare_attention(fus, rows)
-    _report("qwen3_8b_async_256", rows=rows, max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
+    _report(f"qwen3_8b_async_256 {bits}-bit", rows=rows, max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
     assert err <= ATOL and err_lse <= ATOL
