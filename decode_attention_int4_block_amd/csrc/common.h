@@ -192,7 +192,7 @@ struct AppendArgs {
     uint8_t *int4_pool;
     uint8_t *int8_pool;
     int32_t H, P, h, s, w, nr8;
-    int32_t bits;       // main cache code width: 4 or 2
+    int32_t bits;       // main cache code width: 4, 3 or 2
     float inv_sqrt_h;   // fp32 value nearest to 1/sqrt(h)
 };
 
@@ -209,7 +209,7 @@ struct DecodeArgs {
     const uint16_t *k_new;  // [B][H][128] bf16 key / value each row appends at
     const uint16_t *v_new;  //   position ctx_len - 1 (fused append), or nullptr
     int32_t H, P, logP, h, s, w, nr8;
-    int32_t bits;                       // main cache code width: 4 or 2
+    int32_t bits;                       // main cache code width: 4, 3 or 2
     float inv_sqrt_h;
     int32_t max_workers, min_units;
     int32_t part_wt[4];                 // worker weights (Partition)

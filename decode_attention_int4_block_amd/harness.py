@@ -20,8 +20,11 @@ class DeviceWorkload:
     appends; its bf16 k/v are kept in `step_k`, `step_v` ([B, H_kv, 128]).
     """
 
-    def __init__(self, wl: Workload, device="cuda", gen_device=None, keep_host=()):
+    def __init__(self, wl: Workload, device="cuda", gen_device=None, keep_host=(), kv_fn=None):
+        """kv_fn(b) -> (k, v), each [L_b, H_kv, 128] bf16, replaces the workload's
+        drawn keys and values of row b (crafted inputs)."""
         cfg = wl.cfg
+        self.kv_fn = kv_fn
         self.wl = wl
         self.cfg = cfg
         self.device = torch.device(device)
@@ -72,7 +75,7 @@ class DeviceWorkload:
             L = int(self.lengths[b])
             if L == 0:
                 continue
-            k, v = seq_kv(wl, b, device=self.gen_device)
+            k, v = self.kv_fn(b) if self.kv_fn is not None else seq_kv(wl, b, device=self.gen_device)
             if b in self.keep_host:
                 self.host_kv[b] = (k.cpu(), v.cpu())
             self.step_k[b] = k[L - 1].to(self.device)

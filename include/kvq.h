@@ -188,6 +188,15 @@ size_t kvq_int8_pool_bytes(const kvq_cache *cache);
  * Positions within one call must be distinct per slot.  Each (token, head)
  * has exactly one writer; tokens of different calls on one stream are
  * ordered by the stream.
+ *
+ * Input domain: the stored scale and offset are fp16, so every quantized
+ * vector y (the rotated key, the value) must have |min y| <= 65504 and
+ * (max y - min y) / qmax <= 65504 (qmax = 15, 7 or 3 for the main cache, 255
+ * for the INT8 copy); with the rotation |y_i| <= sqrt(h) * max |k|, so keys
+ * with |k_i| <= 65504 / sqrt(h) are always inside.  Outside the domain the
+ * offset or scale is stored as +-inf and the token's dequantized values are
+ * not finite (no error is reported: device data is not checked).  NaN or Inf
+ * inputs are outside the domain as well.
  */
 kvq_status kv_quant_append(const kvq_cache *cache,
                            const uint16_t *k, const uint16_t *v,

@@ -72,13 +72,21 @@ def dequantize(codes, scale_bits, zero_bits) -> np.ndarray:
     return s * np.asarray(codes, dtype=np.float64) + z
 
 
-def tie_near(y, qmax: int, rel: float = 1e-6):
-    """Flags of elements whose integer code sits within `rel` (relative) of a rounding tie.
+def tie_flags(y, qmax: int, rel: float = 1e-6):
+    """Where a rounding decision of the quantizer sits within `rel` (relative) of a tie.
 
-    An element is flagged when its t_i lies within rel of a half-integer, or
-    when its vector's scale_f or mn lies within rel of an fp16 rounding
-    midpoint.  Such elements may legitimately round differently under any
-    other evaluation order; they are counted and reported by the parity tests.
+    Returns (el_flag [..., n], vec_flag [...]):
+
+    * el_flag: the element's quotient t_i lies within rel of a half-integer, so
+      its code (rint of t_i) may round either way under another evaluation
+      order of the same arithmetic;
+    * vec_flag: the vector's fp32 scale_f or its min lies within rel of the
+      midpoint between two fp16 neighbours, so its stored fp16 scale or offset
+      (and then every code of the vector) may round either way.
+
+    A code mismatch can come from either flag, a scale / offset mismatch only
+    from the vector flag.  With the zero-range guard (fp16 scale 0) no code is
+    decided by a quotient, so el_flag is False there.
     """
     y = np.asarray(y, dtype=np.float32)
     mn = y.min(axis=-1)
@@ -96,7 +104,14 @@ def tie_near(y, qmax: int, rel: float = 1e-6):
     frac = t - np.floor(t)
     el_flag = np.abs(frac - 0.5) <= rel * np.maximum(np.abs(t), 1.0)
     el_flag &= (sf != 0)[..., None]
-    return el_flag | vec_flag[..., None]
+    return el_flag, vec_flag
+
+
+def tie_near(y, qmax: int, rel: float = 1e-6):
+    """Per-element flags of codes that may round either way: the element's own
+    tie flag or its vector's (see tie_flags)."""
+    el, vec = tie_flags(y, qmax, rel)
+    return el | vec[..., None]
 
 
 def _near_f16_midpoint(x, rel):

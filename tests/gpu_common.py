@@ -9,7 +9,7 @@ import torch
 from oracle.attention import attend, unquantized_attention
 from oracle.cache import quantize_sequence, rotated_keys_f32
 from oracle.numerics import bf16_to_f32
-from oracle.quant import tie_near
+from oracle.quant import tie_flags
 from oracle.regions import ring_entry
 from workloads import WorkloadConfig, bf16_bits, build_workload
 
@@ -33,13 +33,14 @@ def check_workload_invariants(wl):
     assert np.all((wl.slots >= 0) & (wl.slots < wl.num_slots))
 
 
-def make_device_workload(cfg, keep=(), gen_device="cpu", prefill=True, poison=False):
+def make_device_workload(cfg, keep=(), gen_device="cpu", prefill=True, poison=False, kv_fn=None):
     """Build and fill a workload's cache.  poison=True first fills both pools with
-    0xFF bytes (fp16 NaN) so that any read of never-written cache bytes shows."""
+    0xFF bytes (fp16 NaN) so that any read of never-written cache bytes shows.
+    kv_fn(b) -> (k, v) replaces the drawn keys and values of row b."""
     from decode_attention_int4_block_amd.harness import DeviceWorkload
     wl = build_workload(cfg)
     check_workload_invariants(wl)
-    dw = DeviceWorkload(wl, device="cuda", gen_device=gen_device, keep_host=keep)
+    dw = DeviceWorkload(wl, device="cuda", gen_device=gen_device, keep_host=keep, kv_fn=kv_fn)
     if poison:
         dw.cache.int4_pool.fill_(0xFF)
         dw.cache.int8_pool.fill_(0xFF)
@@ -61,8 +62,16 @@ def _f16_eq(a, b):
 
 def compare_cache(dw, b, positions=None):
     """Compare the GPU cache of row b with the oracle's quantization of the same
-    bf16 inputs.  Returns dict of mismatch / tie counts; raises on a mismatch
-    that is not near a rounding tie."""
+    bf16 inputs.
+
+    Returns a dict of counts (it raises nothing; `assert_cache_exact` judges it):
+    codes and params compared, mismatches, and the mismatches forgiven as
+    rounding ties.  A code mismatch is forgiven only where the element's own
+    quotient, or its vector's fp32 scale or min, lies within 1e-6 relative of a
+    rounding midpoint (oracle.quant.tie_flags); a scale / offset mismatch only
+    on the vector flag.  `flagged` counts the elements the gate would forgive,
+    mismatched or not, so a test of crafted ties can show it reached them.
+    """
     from decode_attention_int4_block_amd.layout import (decode_sub2, decode_sub3, decode_sub4, decode_sub8,
                                                         sub4_index, sub8_index)
     wl = dw.wl
@@ -77,22 +86,32 @@ def compare_cache(dw, b, positions=None):
     P = wl.page_size
     slot = int(wl.slots[b])
     pos = np.arange(L) if positions is None else np.asarray(positions, np.int64)
-    stats = dict(int4_mismatch=0, int4_ties=0, int8_mismatch=0, int8_ties=0, params_mismatch=0)
+    stats = dict(codes=0, int4_mismatch=0, int4_ties=0, int8_mismatch=0, int8_ties=0,
+                 params=0, params_mismatch=0, params_ties=0, flagged=0)
     yk = rotated_keys_f32(kb, cfg.had_block)
     yv = bf16_to_f32(vb)
+
+    def judge(tag, got, y, codes, qmax):
+        el, vec = tie_flags(y, qmax)
+        tie = el | vec[..., None]
+        mism = got[tag] != codes
+        stats["codes"] += int(mism.size)
+        stats["flagged"] += int(tie.sum())
+        return mism, tie, vec
+
     for hk in range(H):
         pages = wl.block_table[slot, pos // P]
         idx = sub4_index(pages, hk, pos % P, H, P)
         got = decode_main(dw.int4_subblocks(idx), (pos % P) % 16)
         for kind, y, codes, sc, ze in (("k", yk, oc.k4, oc.k4_scale, oc.k4_zero),
                                        ("v", yv, oc.v4, oc.v4_scale, oc.v4_zero)):
-            ties = tie_near(y[pos, hk], qmain)
-            mism = got[kind] != codes[pos, hk]
-            stats["int4_ties"] += int((mism & ties).sum())
-            stats["int4_mismatch"] += int((mism & ~ties).sum())
+            mism, tie, vec = judge(kind, got, y[pos, hk], codes[pos, hk], qmain)
+            stats["int4_ties"] += int((mism & tie).sum())
+            stats["int4_mismatch"] += int((mism & ~tie).sum())
             pm = ~(_f16_eq(got[kind + "_scale"], sc[pos, hk]) & _f16_eq(got[kind + "_zero"], ze[pos, hk]))
-            pm &= ~ties.any(axis=1)
-            stats["params_mismatch"] += int(pm.sum())
+            stats["params"] += int(pm.size)
+            stats["params_ties"] += int((pm & vec).sum())
+            stats["params_mismatch"] += int((pm & ~vec).sum())
         if len(oc.pos8):
             ent = np.array([ring_entry(int(p), cfg.sink, cfg.recent) for p in oc.pos8])
             nr8 = (cfg.sink + cfg.recent + 15) // 16
@@ -100,14 +119,37 @@ def compare_cache(dw, b, positions=None):
             got8 = decode_sub8(dw.int8_subblocks(idx8), ent % 16)
             for kind, y, codes, sc, ze in (("k", yk, oc.k8, oc.k8_scale, oc.k8_zero),
                                            ("v", yv, oc.v8, oc.v8_scale, oc.v8_zero)):
-                ties = tie_near(y[oc.pos8, hk], 255)
-                mism = got8[kind] != codes[:, hk]
-                stats["int8_ties"] += int((mism & ties).sum())
-                stats["int8_mismatch"] += int((mism & ~ties).sum())
+                mism, tie, vec = judge(kind, got8, y[oc.pos8, hk], codes[:, hk], 255)
+                stats["int8_ties"] += int((mism & tie).sum())
+                stats["int8_mismatch"] += int((mism & ~tie).sum())
                 pm = ~(_f16_eq(got8[kind + "_scale"], sc[:, hk]) & _f16_eq(got8[kind + "_zero"], ze[:, hk]))
-                pm &= ~ties.any(axis=1)
-                stats["params_mismatch"] += int(pm.sum())
+                stats["params"] += int(pm.size)
+                stats["params_ties"] += int((pm & vec).sum())
+                stats["params_mismatch"] += int((pm & ~vec).sum())
     return stats
+
+
+def add_stats(tot, st):
+    for k, v in st.items():
+        tot[k] = tot.get(k, 0) + v
+    return tot
+
+
+# Mismatches the tie gate may forgive.  Both sides take every rounding decision
+# in the same fp32 / fp16 arithmetic in the same order, so the expected count is
+# 0; the gate covers an evaluation-order difference at a tie and nothing more.
+# At most 1 forgiven code per 1e5 compared, 1 forgiven (scale, offset) pair per
+# 1e4 (the vector flag's own rate is ~0.5%, see the oracle's pins).
+TIE_CODE_RATE = 1e-5
+TIE_PARAM_RATE = 1e-4
+
+
+def assert_cache_exact(st):
+    """Codes, scales and offsets bit-exact; forgiven ties counted and bounded."""
+    assert st["int4_mismatch"] == 0 and st["int8_mismatch"] == 0 and st["params_mismatch"] == 0, st
+    forgiven = st["int4_ties"] + st["int8_ties"]
+    assert forgiven <= TIE_CODE_RATE * max(st["codes"], 1), st
+    assert st["params_ties"] <= TIE_PARAM_RATE * max(st["params"], 1), st
 
 
 def compare_attention(dw, rows, report_unquantized=False):

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import ATOL, compare_attention, compare_cache, make_device_workload, small_config
+from gpu_common import ATOL, assert_cache_exact, compare_attention, compare_cache, make_device_workload, small_config
 from workloads import get_config
 
 pytestmark = pytest.mark.gpu
@@ -26,10 +26,6 @@ def _need_gpu():
 
 def _report(name, **kw):
     print(f"[fused] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
-
-
-def _assert_cache_exact(st):
-    assert st["int4_mismatch"] == 0 and st["int8_mismatch"] == 0 and st["params_mismatch"] == 0, st
 
 
 def _pair(cfg, keep=(), gen_device="cpu"):
@@ -62,7 +58,7 @@ def _check_pair(sep, fus, rows, name):
         assert d_out <= 1e-5, f"{name}: outputs differ by {d_out}"
     for b in rows:
         if int(fus.wl.lengths[b]) > 0:
-            _assert_cache_exact(compare_cache(fus, b))
+            assert_cache_exact(compare_cache(fus, b))
     err, err_lse, _ = compare_attention(fus, rows)
     _report(name, same_split=same_split, d_two_launch=f"{d_out:.1e}", max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
     assert err <= ATOL and err_lse <= ATOL

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import (ATOL, compare_attention, compare_cache, make_device_workload,
+from gpu_common import (ATOL, assert_cache_exact, compare_attention, compare_cache, make_device_workload,
                         small_config)
 from workloads import get_config
 
@@ -27,17 +27,13 @@ def _report(name, **kw):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
 
-def _assert_cache_exact(st):
-    assert st["int4_mismatch"] == 0 and st["int8_mismatch"] == 0 and st["params_mismatch"] == 0, st
-
-
 def test_tiny_single_step_cache_and_attention():
     """The tiny non-paged workload (1 x 1024, 8/2 heads, h=128, s=4, w=64)."""
     cfg = get_config("tiny_1x1024")
     dw = make_device_workload(cfg, keep=[0])
     st = compare_cache(dw, 0)
     _report("tiny cache", **st)
-    _assert_cache_exact(st)
+    assert_cache_exact(st)
     dw.decode_step()
     torch.cuda.synchronize()
     err, err_lse, unq = compare_attention(dw, [0], report_unquantized=True)
@@ -60,7 +56,7 @@ def test_small_paged_cache_and_attention(h):
         for k2, v2 in st.items():
             tot[k2] = tot.get(k2, 0) + v2
     _report(f"small h={h} cache", **tot)
-    _assert_cache_exact(tot)
+    assert_cache_exact(tot)
     dw.decode_step()
     torch.cuda.synchronize()
     err, err_lse, _ = compare_attention(dw, rows)
@@ -92,7 +88,7 @@ def test_protection_budgets(s, w):
     for b in rows:
         for k2, v2 in compare_cache(dw, b).items():
             tot[k2] = tot.get(k2, 0) + v2
-    _assert_cache_exact(tot)
+    assert_cache_exact(tot)
     dw.decode_step()
     torch.cuda.synchronize()
     err, err_lse, _ = compare_attention(dw, rows)
@@ -146,7 +142,7 @@ def test_bulk_append_equals_token_by_token():
     torch.cuda.synchronize()
     seq.host_kv = bulk.host_kv
     for b in range(cfg.batch):
-        _assert_cache_exact(compare_cache(seq, b))
+        assert_cache_exact(compare_cache(seq, b))
     bulk.decode_step()
     seq.decode_step()
     torch.cuda.synchronize()
@@ -188,7 +184,7 @@ def test_full_size_sampled_rows(name):
         for k2, v2 in compare_cache(dw, b, positions).items():
             tot[k2] = tot.get(k2, 0) + v2
     _report(f"{name} cache (sampled rows {rows})", **tot)
-    _assert_cache_exact(tot)
+    assert_cache_exact(tot)
     dw.decode_step()
     torch.cuda.synchronize()
     err, err_lse, unq = compare_attention(dw, rows, report_unquantized=True)

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import ATOL, compare_attention, compare_cache, make_device_workload, small_config
+from gpu_common import ATOL, assert_cache_exact, compare_attention, compare_cache, make_device_workload, small_config
 from workloads import get_config
 
 pytestmark = pytest.mark.gpu
@@ -27,10 +27,6 @@ def _report(name, **kw):
     print(f"[sub4bit] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
 
-def _assert_cache_exact(st):
-    assert st["int4_mismatch"] == 0 and st["int8_mismatch"] == 0 and st["params_mismatch"] == 0, st
-
-
 def _check(cfg, name, poison=False):
     rows = list(range(cfg.batch))
     keep = [b for b in rows if cfg.length_args[b] > 0]
@@ -39,7 +35,7 @@ def _check(cfg, name, poison=False):
     for b in keep:
         for k, v in compare_cache(dw, b).items():
             tot[k] = tot.get(k, 0) + v
-    _assert_cache_exact(tot)
+    assert_cache_exact(tot)
     dw.decode_step()
     torch.cuda.synchronize()
     err, err_lse, _ = compare_attention(dw, rows)
@@ -95,7 +91,7 @@ def test_sub4bit_full_size_sampled_rows(bits):
                                               rng.integers(0, Lb, size=min(Lb, 300))]))
         for k, v in compare_cache(dw, b, positions).items():
             tot[k] = tot.get(k, 0) + v
-    _assert_cache_exact(tot)
+    assert_cache_exact(tot)
     dw.decode_step()
     torch.cuda.synchronize()
     err, err_lse, unq = compare_attention(dw, rows, report_unquantized=True)

@@ -9,7 +9,7 @@ import pytest
 from oracle.hadamard import fwht_f32
 from oracle.numerics import f16_bits_to_f64
 from oracle.quant import (INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX, bytes_per_token_head, dequantize,
-                          pack_int2, pack_int3, pack_int4, qmax_of, quantize, tie_near, unpack_int2, unpack_int3,
+                          pack_int2, pack_int3, pack_int4, qmax_of, quantize, tie_flags, tie_near, unpack_int2, unpack_int3,
                           unpack_int4)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -213,3 +213,107 @@ def test_int2_cache_keeps_the_int8_protection():
     c2 = quantize_sequence(k, v, 64, 4, 16, main_bits=2)
     assert c2.k4.max() <= 3 and c2.v4.max() <= 3 and c4.k4.max() > 3
     assert np.array_equal(c2.pos8, c4.pos8) and np.array_equal(c2.k8, c4.k8) and np.array_equal(c2.v8, c4.v8)
+
+
+# --- the tie gate: which GPU / oracle differences a parity test may forgive ----
+
+def _f32(x):
+    return np.asarray(x, np.float32)
+
+
+def test_tie_flags_mark_an_exact_half_and_not_a_thousandth_away():
+    """A quotient t exactly at k + 1/2 is a rounding tie; 1e-3 away it is not.
+    The vector [0, 15, ...] has scale_f = 1 and zero 0 exactly (both fp16
+    values), so t_i = y_i."""
+    y = np.zeros((3, 128), np.float32)
+    y[:, 1] = 15.0
+    y[0, 2] = 7.5                  # exact tie
+    y[1, 2] = 7.501                # 1e-3 away
+    y[2, 2] = 7.4990               # 1e-3 away below
+    el, vec = tie_flags(y, INT4_QMAX)
+    assert not vec.any()
+    assert el[0, 2] and not el[1, 2] and not el[2, 2]
+    # grid points (t integral) are never ties
+    assert not el[:, :2].any() and not el[:, 3:].any()
+    # the codes themselves: 7.5 rounds to the even 8
+    c, _, _ = quantize(y, INT4_QMAX)
+    assert c[0, 2] == 8 and c[1, 2] == 8 and c[2, 2] == 7
+
+
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
+def test_tie_flags_every_half_integer_of_the_grid(qmax):
+    """All half-integers k + 1/2 (k < qmax) are flagged, all integers are not."""
+    y = np.zeros((1, 128), np.float32)
+    y[0, 1] = qmax                               # scale 1, zero 0
+    k = np.arange(min(qmax, 126))
+    y[0, 2:2 + len(k)] = k + 0.5
+    el, vec = tie_flags(y, qmax)
+    assert not vec.any()
+    assert el[0, 2:2 + len(k)].all()
+    assert not el[0, :2].any() and not el[0, 2 + len(k):].any()
+
+
+def test_tie_flags_mark_an_fp16_midpoint_scale_and_not_a_thousandth_away():
+    """scale_f exactly at the midpoint 1 + 2^-11 of the fp16 neighbours 1 and
+    1 + 2^-10 is a vector tie; a scale 1e-3 (relative) away is not."""
+    mid = 1.0 + 2.0 ** -11
+    y = np.zeros((2, 128), np.float32)
+    y[0, 1] = np.float32(15 * mid)                # exact in fp32, scale_f = mid exactly
+    assert np.float32(y[0, 1]) / np.float32(15) == np.float32(mid)
+    y[1, 1] = np.float32(15 * mid * (1 + 1e-3))
+    el, vec = tie_flags(y, INT4_QMAX)
+    assert vec[0] and not vec[1]
+
+
+def test_tie_flags_mark_an_fp16_midpoint_min_and_not_a_thousandth_away():
+    """The offset is fp16(min): a min at an fp16 midpoint is a vector tie."""
+    mid = -(1.0 + 2.0 ** -11)
+    y = np.zeros((2, 128), np.float32)
+    y[:, 1] = 15.0
+    y[0, 0] = np.float32(mid)
+    y[1, 0] = np.float32(mid * (1 + 1e-3))
+    el, vec = tie_flags(y, INT4_QMAX)
+    assert vec[0] and not vec[1]
+    # a vector tie flags every element of the vector in tie_near
+    near = tie_near(y, INT4_QMAX)
+    assert near[0].all()
+    assert near[1].sum() == el[1].sum()
+
+
+def test_tie_flags_guarded_vectors_have_no_element_ties():
+    """With the zero-range guard every code is 0: no quotient decides a code."""
+    y = np.full((2, 128), 0.5, np.float32)       # 0.5 would sit at t = k + 1/2 with scale 1
+    el, vec = tie_flags(y, INT4_QMAX)
+    assert not el.any()
+
+
+@pytest.mark.parametrize("qmax", [INT2_QMAX, INT3_QMAX, INT4_QMAX, INT8_QMAX])
+def test_tie_flags_are_rare_on_random_vectors(qmax):
+    """On the workloads' value distribution the gate forgives little: an element's
+    t lies within 1e-6 |t| of a half-integer with probability about 2e-6 |t|
+    (mean |t| about qmax / 2), and a vector's two fp16 roundings each fall within
+    1e-6 of a midpoint with probability about 2e-6 / 2^-10.  Bounds: 3e-6 (qmax + 1)
+    of the elements, 2% of the vectors."""
+    y = fwht_f32(_vectors(20000, 8), 128)
+    el, vec = tie_flags(y, qmax)
+    assert el.mean() < 3e-6 * (qmax + 1), el.mean()
+    assert vec.mean() < 0.02, vec.mean()
+    assert tie_near(y, qmax).mean() < 0.03
+
+
+def test_input_domain_edge_of_the_fp16_params():
+    """The stored params are fp16: at |min| = 65504 and range / qmax = 65504 they
+    are finite (the largest fp16 value); just past either the offset or the
+    scale rounds to infinity and the dequantized vector is no longer finite,
+    which is why the library states this input domain."""
+    inside = np.zeros((2, 128), np.float32)
+    inside[0, 0] = -65504.0                         # |min| at the fp16 maximum
+    inside[1, 1] = np.float32(15 * 65504.0)         # range / 15 at the fp16 maximum
+    c, sb, zb = quantize(inside, INT4_QMAX)
+    assert np.all(np.isfinite(dequantize(c, sb, zb)))
+    outside = np.zeros((2, 128), np.float32)
+    outside[0, 0] = -65536.0                        # rounds past the fp16 maximum
+    outside[1, 1] = np.float32(15 * 65536.0)
+    c, sb, zb = quantize(outside, INT4_QMAX)
+    assert not np.isfinite(dequantize(c, sb, zb)[0]).all()
+    assert not np.isfinite(dequantize(c, sb, zb)[1]).all()
