@@ -15,8 +15,8 @@ import torch
 from . import _lib
 from ._lib import KvqCache, KvqError
 
-__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_append_decode_attn", "kv_prefill_attn",
-           "KvqError"]
+__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_decode_attn_noalloc", "kv_append_decode_attn",
+           "kv_prefill_attn", "KvqError"]
 
 
 def _ptr(t):
@@ -117,6 +117,23 @@ def kv_decode_attn(cache: QuantKVCache, q, slot, block_table, ctx_len, out=None,
                                   block_table.shape[1], _ptr(ctx_len), B, _ptr(out), _ptr(lse),
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "kv_decode_attn")
+    return out, lse
+
+
+def kv_decode_attn_noalloc(cache: QuantKVCache, q, slot, block_table, ctx_len, out, lse, stream=None):
+    """kv_decode_attn with the library's static device scratch instead of a
+    workspace: the C call allocates nothing (out and lse are the caller's)."""
+    _dev_bf16(q, "q")
+    B, Hq = q.shape[0], q.shape[1]
+    _dev_i32(slot, "slot")
+    _dev_i32(block_table, "block_table")
+    _dev_i32(ctx_len, "ctx_len")
+    if slot.numel() != B or ctx_len.numel() != B:
+        raise ValueError("slot and ctx_len need one entry per row")
+    st = cache.lib.kv_decode_attn_noalloc(ctypes.byref(cache.desc), _ptr(q), Hq, _ptr(slot), _ptr(block_table),
+                                          block_table.shape[1], _ptr(ctx_len), B, _ptr(out), _ptr(lse),
+                                          _stream(stream))
+    _lib.check(st, "kv_decode_attn_noalloc")
     return out, lse
 
 

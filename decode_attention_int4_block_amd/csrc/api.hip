@@ -267,6 +267,64 @@ kvq_status kv_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_h
                          workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of kv_decode_attn_noalloc: the decode workspace (worker records,
+// chunk partials, pieces) in a device array that the code object brings along,
+// so that the call allocates nothing.  Each device holds its own copy at its
+// own address; host code must use that address (hipGetSymbolAddress), never
+// the array's name, which on the host is only a stand-in for the symbol.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+
+// Address of `scratch` on the current device, looked up once per device.
+kvq_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
+    uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        p = reinterpret_cast<uintptr_t>(ptr);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = reinterpret_cast<void *>(p);
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kv_decode_attn_noalloc(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads, const int32_t *slot,
+                                  const int32_t *block_table, int32_t bt_stride, const int32_t *ctx_len, int32_t B,
+                                  float *out, float *lse, void *stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (B < 0 || num_q_heads < 1 || num_q_heads % c->num_kv_heads || num_q_heads / c->num_kv_heads > 16)
+        return decode_launch(c, false, nullptr, nullptr, q, num_q_heads, slot, block_table, bt_stride, ctx_len, B,
+                             out, lse, nullptr, 0, stream);       // reports the argument error
+    if (B == 0) return ok();
+    if (!q || !slot || !block_table || !ctx_len || !out)
+        return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
+    const size_t need = kv_decode_attn_workspace_bytes(c, B, num_q_heads);
+    if (need == 0) return fail(KVQ_ERR_HIP, "workspace size query failed");
+    if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+        return fail(KVQ_ERR_WORKSPACE, "B = %d rows of %d query heads need %zu bytes of scratch; the static scratch "
+                    "holds %zu (use kv_decode_attn with a workspace)", B, num_q_heads, need,
+                    (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != KVQ_OK) return st;
+    return decode_launch(c, false, nullptr, nullptr, q, num_q_heads, slot, block_table, bt_stride, ctx_len, B, out,
+                         lse, ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 kvq_status kv_append_decode_attn(const kvq_cache *c, const uint16_t *k, const uint16_t *v, const uint16_t *q,
                                  int32_t num_q_heads, const int32_t *slot, const int32_t *block_table,
                                  int32_t bt_stride, const int32_t *ctx_len, int32_t B, float *out, float *lse,

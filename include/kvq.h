@@ -238,6 +238,33 @@ kvq_status kv_decode_attn(const kvq_cache *cache,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kv_decode_attn_noalloc -- kv_decode_attn without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results as kv_decode_attn; the workspace is a static device
+ * array of KVQ_NOALLOC_SCRATCH_BYTES that the library's code object holds on
+ * every device it runs on until the process ends.  The call allocates and frees
+ * nothing.
+ *
+ *   Limit: B rows of num_q_heads heads fit when kv_decode_attn_workspace_bytes
+ *   (cache, B, num_q_heads) <= KVQ_NOALLOC_SCRATCH_BYTES (e.g. 256 rows of 32
+ *   query heads over 8 KV heads need about 14 MB, 512 such rows about 23 MB);
+ *   larger requests return KVQ_ERR_WORKSPACE and enqueue nothing.
+ *   Every call on one device shares that device's array: calls that can run
+ *   at the same time on one device (different streams, or host threads with
+ *   no ordering between their streams) race and give wrong results; calls on
+ *   one stream are ordered and safe.  Nothing in the array needs clearing
+ *   between calls (each launch writes what it later reads).
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvq_status kv_decode_attn_noalloc(const kvq_cache *cache,
+                                  const uint16_t *q, int32_t num_q_heads,
+                                  const int32_t *slot,
+                                  const int32_t *block_table, int32_t bt_stride,
+                                  const int32_t *ctx_len, int32_t B,
+                                  float *out, float *lse, void *stream);
+
+/*
  * kv_append_decode_attn -- one decode step with the append fused in: every
  * row b with ctx_len[b] >= 1 first appends its new token (key k[b], value
  * v[b]) at position ctx_len[b] - 1 of slot[b], quantized exactly as

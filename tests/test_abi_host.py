@@ -91,6 +91,21 @@ def test_decode_argument_checks(lib):
     assert lib.kv_decode_attn(ctypes.byref(d), p, 32, p, p, 4, p, 2, p, None, None, 1 << 30, None) == 4
 
 
+def test_noalloc_argument_checks(lib):
+    """The no-allocation entry point rejects bad arguments on the host, before
+    it looks up its scratch or touches a device."""
+    d = _desc(int4_pool=0x1000, int8_pool=0x2000)
+    p = ctypes.c_void_p(0x3000)
+    f = lib.kv_decode_attn_noalloc
+    assert f(ctypes.byref(d), p, 256, p, p, 4, p, 2, p, None, None) == 3
+    assert f(ctypes.byref(d), p, 12, p, p, 4, p, 2, p, None, None) == 2
+    assert f(ctypes.byref(d), p, 32, p, p, 4, p, -1, p, None, None) == 2
+    assert f(ctypes.byref(d), p, 32, p, p, 4, p, 0, p, None, None) == 0
+    assert f(ctypes.byref(d), None, 32, p, p, 4, p, 2, p, None, None) == 1
+    assert f(ctypes.byref(d), p, 32, p, p, 4, p, 2, None, None, None) == 1
+    assert f(None, p, 32, p, p, 4, p, 2, p, None, None) == 1
+
+
 def test_fused_argument_checks(lib):
     d = _desc(int4_pool=0x1000, int8_pool=0x2000)
     p = ctypes.c_void_p(0x3000)
