@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import KvqCache, KvqError
 
-__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_decode_attn_noalloc", "kv_append_decode_attn",
+__all__ = ["QuantKVCache", "kv_quant_append", "kv_decode_attn", "kv_decode_attn_noalloc", "kv_decode_read_ceiling",
+           "kv_append_decode_attn",
            "kv_prefill_attn", "KvqError"]
 
 
@@ -118,6 +119,22 @@ def kv_decode_attn(cache: QuantKVCache, q, slot, block_table, ctx_len, out=None,
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "kv_decode_attn")
     return out, lse
+
+
+def kv_decode_read_ceiling(cache: QuantKVCache, q, slot, block_table, ctx_len, workspace=None, stream=None):
+    """The memory traffic of kv_decode_attn without its arithmetic (a measured
+    bandwidth ceiling for the same access pattern); computes nothing."""
+    _dev_bf16(q, "q")
+    B, Hq = q.shape[0], q.shape[1]
+    _dev_i32(slot, "slot")
+    _dev_i32(block_table, "block_table")
+    _dev_i32(ctx_len, "ctx_len")
+    if workspace is None:
+        workspace = cache.new_workspace(B, Hq)
+    st = cache.lib.kv_decode_read_ceiling(ctypes.byref(cache.desc), _ptr(q), Hq, _ptr(slot), _ptr(block_table),
+                                          block_table.shape[1], _ptr(ctx_len), B, _ptr(workspace),
+                                          workspace.numel(), _stream(stream))
+    _lib.check(st, "kv_decode_read_ceiling")
 
 
 def kv_decode_attn_noalloc(cache: QuantKVCache, q, slot, block_table, ctx_len, out, lse, stream=None):

@@ -38,6 +38,8 @@ SIGNATURES = {
     "kv_decode_attn_workspace_bytes": (c_sz, [ctypes.POINTER(KvqCache), c_i32, c_i32]),
     "kv_decode_attn": (c_i32, [ctypes.POINTER(KvqCache), c_vp, c_i32, c_vp, c_vp, c_i32,
                                c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "kv_decode_read_ceiling": (c_i32, [ctypes.POINTER(KvqCache), c_vp, c_i32, c_vp, c_vp, c_i32,
+                                       c_vp, c_i32, c_vp, c_sz, c_vp]),
     "kv_decode_attn_noalloc": (c_i32, [ctypes.POINTER(KvqCache), c_vp, c_i32, c_vp, c_vp, c_i32,
                                        c_vp, c_i32, c_vp, c_vp, c_vp]),
     "kv_append_decode_attn": (c_i32, [ctypes.POINTER(KvqCache), c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,

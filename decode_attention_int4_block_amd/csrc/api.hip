@@ -191,7 +191,7 @@ namespace {
 kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, const uint16_t *v_new,
                          const uint16_t *q, int32_t num_q_heads, const int32_t *slot, const int32_t *block_table,
                          int32_t bt_stride, const int32_t *ctx_len, int32_t B, float *out, float *lse,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+                         void *workspace, size_t workspace_bytes, void *stream, bool ceiling = false) {
     kvq_status st = check_cache(c);
     if (st != KVQ_OK) return st;
     if (B < 0) return fail(KVQ_ERR_SHAPE, "B = %d < 0", B);
@@ -202,8 +202,9 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     if (g > 16) return fail(KVQ_ERR_UNSUPPORTED, "query group %d > 16", g);
     if (B == 0) return ok();
     if ((int64_t)B * num_q_heads > ((int64_t)1 << 31) - 1) return fail(KVQ_ERR_SHAPE, "B * num_q_heads too large");
-    if (!q || !slot || !block_table || !ctx_len || !out || (fused && (!k_new || !v_new)))
+    if (!q || !slot || !block_table || !ctx_len || (!out && !ceiling) || (fused && (!k_new || !v_new)))
         return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
+    if (ceiling && g > 8) return fail(KVQ_ERR_UNSUPPORTED, "the read ceiling covers query groups up to 8");
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
@@ -250,7 +251,8 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.ws_piece = reinterpret_cast<float *>(ws + l.piece_off);
     a.out = out;
     a.lse = lse;
-    hipError_t e = kvq::launch_decode(a, workers, static_cast<hipStream_t>(stream));
+    hipError_t e = ceiling ? kvq::launch_decode_read_ceiling(a, workers, static_cast<hipStream_t>(stream))
+                           : kvq::launch_decode(a, workers, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -323,6 +325,13 @@ kvq_status kv_decode_attn_noalloc(const kvq_cache *c, const uint16_t *q, int32_t
     if (st != KVQ_OK) return st;
     return decode_launch(c, false, nullptr, nullptr, q, num_q_heads, slot, block_table, bt_stride, ctx_len, B, out,
                          lse, ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+kvq_status kv_decode_read_ceiling(const kvq_cache *c, const uint16_t *q, int32_t num_q_heads, const int32_t *slot,
+                                  const int32_t *block_table, int32_t bt_stride, const int32_t *ctx_len, int32_t B,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_launch(c, false, nullptr, nullptr, q, num_q_heads, slot, block_table, bt_stride, ctx_len, B, nullptr,
+                         nullptr, workspace, workspace_bytes, stream, true);
 }
 
 kvq_status kv_append_decode_attn(const kvq_cache *c, const uint16_t *k, const uint16_t *v, const uint16_t *q,

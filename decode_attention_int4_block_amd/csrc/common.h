@@ -246,6 +246,7 @@ struct PrefillArgs {
 hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream);
+hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t stream);
 hipError_t decode_max_workers(int g, bool fused, int bits, int *out);
 
 }  // namespace kvq

@@ -1078,7 +1078,11 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int GP, bool APPEND, int BITS>
+// MEM = true builds the kernel's memory skeleton: the same prologue, work
+// split, page gathers, DMA ring, waits and stage reads, without the arithmetic
+// and without outputs -- the bandwidth this access pattern reaches on the
+// device, as a measured ceiling for the full kernel.
+template <int GP, bool APPEND, int BITS, bool MEM = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a) {
     using SL = SmemLayout<GP, APPEND>;
@@ -1311,9 +1315,15 @@ void decode_split_kernel(DecodeArgs a) {
     QRing<GP> qr = read_query<GP>(qring, lane);     // the first step opens a segment
     wait_lgkm0();
     look = uniform(look);
+    uint32_t sink = 0;          // MEM: what the stage reads returned, kept live
     for (int i = 0; C.u < u_end; ++i) {
         const int scur = i % kStages, snxt = (i + 1) % kStages;
         const bool int4 = C.r < C.rp.n4;
+        if constexpr (MEM) {
+            sink ^= r.kA[0] ^ r.kB[1] ^ r.vA[2] ^ r.vB[3] ^ r.kp[0] ^ r.vp[0] ^ qr.w[0][0];
+            if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
+            cursor_next(a, R, C);
+        } else {
         if (!open) {
             // this step starts a segment: finish the previous one first
             if (pend) {
@@ -1338,6 +1348,7 @@ void decode_split_kernel(DecodeArgs a) {
         E = C;
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
         cursor_next(a, R, C);
+        }
         // the next step's stage (its DMA is i + 1's, issued three steps ago)
         if (C.u < u_end) {
             wait_vm_steps(issued - i - 2);
@@ -1364,6 +1375,11 @@ void decode_split_kernel(DecodeArgs a) {
         wait_lgkm0();
         look = uniform(look);
     }
+    if constexpr (MEM) {
+        // practically never true, but not provably so: the reads stay
+        if (sink == 0x9E3779B9u + (uint32_t)a.B) a.ws_header[1] = (int32_t)sink;
+        return;
+    }
     if (pend) {
         vpart<GP, BITS>(c, L, kp);
         end_segment(E);
@@ -1385,7 +1401,8 @@ void decode_split_kernel(DecodeArgs a) {
 // chunk partial, and counts the folded pieces on the segment (an agent-scope
 // acquire-release add: the helpers run on different XCDs); the helper that
 // completes the count folds the chunk partials.  Pieces and chunks are folded in
-// worker order, so the result is the same whoever finishes last.
+// worker order, so the result is the same whoever finishes last.  Each of these
+// folds is shared by the kCombWaves waves of the workgroup (block_fold_heads).
 //
 // Lane l handles query heads l / 16 (g <= 4), or 8 k + l / 16 and 8 k + 4 +
 // l / 16, and dims 8 (l % 16) .. + 8 of a piece laid out as
@@ -1450,32 +1467,6 @@ __device__ inline void fold_pieces(MergeAcc (&r)[NH], PtrFn ptr, int cnt, const 
     }
 }
 
-// Folds the pieces for every head of the group and hands each head's result
-// to out(r, j): one pass of single heads for g <= 4, else passes over pairs of
-// head quartets (lane l takes heads hg + l / 16 and hg + 4 + l / 16).
-template <typename PtrFn, typename OutFn>
-__device__ inline void fold_heads(int g, int lane, int part, int cnt, PtrFn ptr, OutFn out) {
-    if (g <= 4) {
-        const int j = lane >> 4;
-        MergeAcc r[1];
-        merge_init(r[0]);
-        const int jj[1] = {j < g ? j : 0};
-        fold_pieces<1>(r, ptr, cnt, jj, part);
-        if (j < g) out(r[0], j);
-        return;
-    }
-    for (int hg = 0; hg < g; hg += 8) {
-        const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
-        const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
-        MergeAcc r[2];
-        merge_init(r[0]);
-        merge_init(r[1]);
-        fold_pieces<2>(r, ptr, cnt, jj, part);
-        if (j[0] < g) out(r[0], j[0]);
-        if (j[1] < g) out(r[1], j[1]);
-    }
-}
-
 // Normalized output (and lse) of head j from a fold.
 __device__ inline void merge_write(const DecodeArgs &a, const MergeAcc &r, int b, int hk, int j, int part) {
     float *o = a.out + ((int64_t)b * a.Hq + (int64_t)hk * a.g + j) * kHeadDim + 8 * part;
@@ -1514,9 +1505,89 @@ __device__ inline int wave_min(int x) {
     return uni(x);
 }
 
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+// A combine workgroup is kCombWaves waves.  A fold of more pieces than one
+// round trip of one wave carries is split into kCombWaves contiguous ranges,
+// one per wave; wave 0 then merges the waves' partials in wave order, so the
+// result does not depend on timing.
+constexpr int kCombWaves = 4;
+
+struct CombShared {
+    MergeAcc part[kCombWaves][2][64];   // per wave, per head slot, per lane
+    int before;                         // the helper's count before its add
+};
+
+// r <- fold of (r, o): both rescaled to the larger running max.
+__device__ inline void merge_acc(MergeAcc &r, const MergeAcc &o) {
+    const float Mn = fmaxf(r.M, o.M);
+    if (Mn == kNegInf) return;
+    const float fr = r.M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(r.M - Mn);
+    const float fo = o.M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(o.M - Mn);
+    r.Ls = fmaf(r.Ls, fr, o.Ls * fo);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.acc[e] = fmaf(r.acc[e], fr, o.acc[e] * fo);
+    r.M = Mn;
+}
+
+// Folds pieces ptr(0) .. ptr(cnt - 1) for every head of the group with the
+// whole workgroup and hands each head's result to out(r, j) in wave 0: one
+// pass of single heads for g <= 4, else passes over pairs of head quartets
+// (lane l takes heads hg + l / 16 and hg + 4 + l / 16).  Every wave of the
+// workgroup must call it with the same cnt (it holds workgroup barriers).
+template <typename PtrFn, typename OutFn>
+__device__ inline void block_fold_heads(int g, int wave, int lane, int part, int cnt, PtrFn ptr, OutFn out,
+                                        CombShared &sh) {
+    const int per_trip = g <= 4 ? kCombBatch : kCombBatch / 2;
+    const int nw = cnt <= per_trip ? 1 : kCombWaves;
+    const int lo = wave < nw ? wave * cnt / nw : 0;
+    const int hi = wave < nw ? (wave + 1) * cnt / nw : 0;
+    auto sub = [&](int k) { return ptr(lo + k); };
+    if (g <= 4) {
+        const int j = lane >> 4;
+        MergeAcc r[1];
+        merge_init(r[0]);
+        const int jj[1] = {j < g ? j : 0};
+        if (hi > lo) fold_pieces<1>(r, sub, hi - lo, jj, part);
+        if (nw > 1) {
+            sh.part[wave][0][lane] = r[0];
+            __syncthreads();
+            if (wave == 0)
+                for (int k = 1; k < nw; ++k) merge_acc(r[0], sh.part[k][0][lane]);
+            __syncthreads();
+        }
+        if (wave == 0 && j < g) out(r[0], j);
+        return;
+    }
+    for (int hg = 0; hg < g; hg += 8) {
+        const int j[2] = {hg + (lane >> 4), hg + 4 + (lane >> 4)};
+        const int jj[2] = {j[0] < g ? j[0] : 0, j[1] < g ? j[1] : 0};
+        MergeAcc r[2];
+        merge_init(r[0]);
+        merge_init(r[1]);
+        if (hi > lo) fold_pieces<2>(r, sub, hi - lo, jj, part);
+        if (nw > 1) {
+            sh.part[wave][0][lane] = r[0];
+            sh.part[wave][1][lane] = r[1];
+            __syncthreads();
+            if (wave == 0) {
+                for (int k = 1; k < nw; ++k) {
+                    merge_acc(r[0], sh.part[k][0][lane]);
+                    merge_acc(r[1], sh.part[k][1][lane]);
+                }
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+            if (j[0] < g) out(r[0], j[0]);
+            if (j[1] < g) out(r[1], j[1]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeArgs a) {
     constexpr int T = kChunkPieces;
-    const int lane = threadIdx.x;
+    __shared__ CombShared sh;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int g = a.g;
     const int part = lane & 15;
     const int64_t nseg = (int64_t)a.B * a.H;
@@ -1529,16 +1600,18 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
         const int64_t wf = ldc(a.ws_first, seg), wl = ldc(a.ws_last, seg);
         const RowPlan rp = row_plan(Lb, a.s, a.w);
         if (rp.cost == 0) {
-            for (int i = lane; i < g * kHeadDim; i += 64)
-                a.out[((int64_t)b * a.Hq + (int64_t)hk * g) * kHeadDim + i] = 0.0f;
-            if (a.lse && lane < g) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + lane] = kNegInf;
+            if (wave == 0) {
+                for (int i = lane; i < g * kHeadDim; i += 64)
+                    a.out[((int64_t)b * a.Hq + (int64_t)hk * g) * kHeadDim + i] = 0.0f;
+                if (a.lse && lane < g) a.lse[(int64_t)b * a.Hq + (int64_t)hk * g + lane] = kNegInf;
+            }
             return;
         }
         const int n = (int)(wl - wf + 1);
         if (n == 1 || n > T) return;            // finished by its only worker / folded by the helpers
         const float *basep = a.ws_piece + (wf + seg) * piece_elems;
-        fold_heads(g, lane, part, n, [&](int k) { return basep + k * piece_elems; },
-                   [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); });
+        block_fold_heads(g, wave, lane, part, n, [&](int k) { return basep + k * piece_elems; },
+                         [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); }, sh);
         return;
     }
     // helper: the pieces of workers [w0, w0 + T)
@@ -1553,7 +1626,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     if (v >= 0 && a.ws_last[v] - a.ws_first[v] + 1 <= T) v = -1;
     int prev = -1;
     for (;;) {
-        // the long segments of these workers' pieces, in increasing order
+        // the long segments of these workers' pieces, in increasing order (the
+        // same in every wave: each wave reads the same records)
         const int s = wave_min(v > prev ? v : 0x7fffffff);
         if (s == 0x7fffffff) break;
         prev = s;
@@ -1564,18 +1638,29 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
         const int64_t wb = (w0 + T - 1 < wl ? w0 + T - 1 : wl);
         const float *basep = a.ws_piece + (wa + s) * piece_elems;
         float *chunk = a.ws_l2 + (jc + s) * piece_elems;
-        fold_heads(g, lane, part, (int)(wb - wa + 1), [&](int k) { return basep + k * piece_elems; },
-                   [&](const MergeAcc &r, int j) { merge_store(r, chunk, j, part); });
-        int before = 0;
-        if (lane == 0)
-            before = __hip_atomic_fetch_add(a.ws_count + s, (int)(wb - wa + 1), __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        before = uni(before);
+        block_fold_heads(g, wave, lane, part, (int)(wb - wa + 1), [&](int k) { return basep + k * piece_elems; },
+                         [&](const MergeAcc &r, int j) { merge_store(r, chunk, j, part); }, sh);
+        // wave 0 stored the chunk partial; its release-acquire add publishes it
+        // and finds whether this helper completes the segment
+        if (wave == 0) {
+            int before = 0;
+            if (lane == 0)
+                before = __hip_atomic_fetch_add(a.ws_count + s, (int)(wb - wa + 1), __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            before = uni(before);
+            if (lane == 0) sh.before = before;
+        }
+        __syncthreads();
+        const int before = sh.before;
+        __syncthreads();
         if (before + (int)(wb - wa + 1) != n) continue;
-        // the last helper of the segment folds its chunk partials
+        // the last helper of the segment folds its chunk partials (written by
+        // helpers on other XCDs): every wave acquires before reading them
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const int64_t jf = wf / T, jl = wl / T;
         const float *c0 = a.ws_l2 + (jf + s) * piece_elems;
-        fold_heads(g, lane, part, (int)(jl - jf + 1), [&](int k) { return c0 + k * piece_elems; },
-                   [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); });
+        block_fold_heads(g, wave, lane, part, (int)(jl - jf + 1), [&](int k) { return c0 + k * piece_elems; },
+                         [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); }, sh);
     }
 }
 
@@ -1617,7 +1702,23 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int helpers = (grid + kChunkPieces - 1) / kChunkPieces;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H + helpers), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H + helpers), dim3(64 * kCombWaves), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t stream) {
+    const int cls = group_class(a.g);
+    if (cls == 16) return hipErrorNotSupported;
+    if (a.bits == 2) {
+        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, true>), dim3(grid), dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, true>), dim3(grid), dim3(64), 0, stream, a);
+    } else if (a.bits == 3) {
+        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, true>), dim3(grid), dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, true>), dim3(grid), dim3(64), 0, stream, a);
+    } else {
+        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, true>), dim3(grid), dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, true>), dim3(grid), dim3(64), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -238,6 +238,24 @@ kvq_status kv_decode_attn(const kvq_cache *cache,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kv_decode_read_ceiling -- a measurement, not part of the method: the memory
+ * traffic of kv_decode_attn without its arithmetic.  Same arguments as
+ * kv_decode_attn minus out and lse; the same work split over the same number
+ * of waves, the same block-table gathers, direct-to-LDS step copies, waits
+ * and LDS reads, so it reads every byte kv_decode_attn reads, in the same
+ * order, and computes and writes nothing (the workspace header may be
+ * touched).  Its duration is the bandwidth this access pattern reaches on the
+ * device: a ceiling to put kv_decode_attn's own against.  Query groups up to 8
+ * (KVQ_ERR_UNSUPPORTED above).
+ */
+kvq_status kv_decode_read_ceiling(const kvq_cache *cache,
+                                  const uint16_t *q, int32_t num_q_heads,
+                                  const int32_t *slot,
+                                  const int32_t *block_table, int32_t bt_stride,
+                                  const int32_t *ctx_len, int32_t B,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kv_decode_attn_noalloc -- kv_decode_attn without a workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
