@@ -182,3 +182,101 @@ def unpack_int3(packed) -> np.ndarray:
 def bytes_per_token_head(head_dim: int, bits: int) -> int:
     """K+V bytes of one (token, KV head): codes plus an fp16 scale and offset each."""
     return 2 * (head_dim * bits // 8 + 4)
+
+
+# --- keys with a bit width per RoPE-block group ----------------------------------
+#
+# RoPE-Aware Bit Allocation for KV-Cache Quantization (Block-GTQ), Abstract: a
+# key's logit contribution splits over two-dimensional RoPE frequency blocks,
+# so integer bit widths are allocated per block.  Reading (packing only; the
+# allocation itself is an input): the 64 rotate-half RoPE blocks (f, f + 64)
+# form four groups of 16, group j holding frequencies 8 j .. 8 j + 7 and
+# 32 + 8 j .. 32 + 8 j + 7, i.e. the dims d with (d mod 32) // 8 == j; each
+# group has a width b_j in {2, 3, 4}.  One per-token affine pair is kept, as
+# in the 4-bit cache: U = fp16(fp32(mx - mn) / 15), Z = fp16(mn).  A group of
+# width b uses the step 2^(4 - b) U and the offset ((2^(4 - b) - 1) / 2) U, so
+# its 2^b levels sit centred in the 4-bit span [Z, Z + 15 U]; with every width
+# 4 this is the 4-bit quantizer exactly.
+ROPE_GROUPS = 4
+
+
+def rope_group_of_dim(d):
+    """Group (0-3) of rotated key dim d (numpy array or int)."""
+    return (np.asarray(d) % 32) // 8
+
+
+def group_widths_per_dim(key_bits, n=128):
+    """Width of each of the n dims for the four group widths key_bits."""
+    kb = np.asarray(key_bits, dtype=np.int64)
+    if kb.shape != (ROPE_GROUPS,) or not np.all((kb >= 2) & (kb <= 4)):
+        raise ValueError(f"key_bits must be four widths in {{2, 3, 4}}, got {key_bits}")
+    return kb[rope_group_of_dim(np.arange(n))]
+
+
+def quantize_grouped(y, key_bits):
+    """Quantize fp32 keys y[..., 128] with the group widths key_bits.
+
+    Returns (codes uint8 [..., 128], scale_bits uint16 [...] (U), zero_bits
+    uint16 [...] (Z)).  Decisions in fp32: Z_b = fp32(Z + fp32(o_b U)),
+    t = fp32(fp32(y - Z_b) / fp32(m_b U)), c = clamp(rint(t), 0, 2^b - 1) with
+    m_b = 2^(4 - b), o_b = (m_b - 1) / 2; every code is 0 when U is 0.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    b = group_widths_per_dim(key_bits, y.shape[-1])
+    mn = y.min(axis=-1)
+    mx = y.max(axis=-1)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        scale_f = (mx - mn) / np.float32(15)
+    ub = f32_to_f16_bits(scale_f)
+    zb = f32_to_f16_bits(mn)
+    U = f16_bits_to_f32(ub)[..., None]
+    Z = f16_bits_to_f32(zb)[..., None]
+    m = (2.0 ** (4 - b)).astype(np.float32)
+    o = ((m - 1) / 2).astype(np.float32)
+    step = (m * U).astype(np.float32)                    # exact: U times a power of two
+    zb_ = (Z + (o * U).astype(np.float32)).astype(np.float32)
+    guard = U == 0
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        t = ((y - zb_).astype(np.float32) / np.where(guard, np.float32(1), step)).astype(np.float32)
+    c = np.clip(np.rint(t), 0, (1 << b) - 1)
+    c = np.where(guard, 0, c)
+    return c.astype(np.uint8), ub, zb
+
+
+def dequantize_grouped(codes, scale_bits, zero_bits, key_bits) -> np.ndarray:
+    """Z + U (o_b + m_b c) in fp64."""
+    c = np.asarray(codes, dtype=np.float64)
+    b = group_widths_per_dim(key_bits, c.shape[-1])
+    m = 2.0 ** (4 - b)
+    U = f16_bits_to_f64(scale_bits)[..., None]
+    Z = f16_bits_to_f64(zero_bits)[..., None]
+    return Z + U * ((m - 1) / 2 + m * c)
+
+
+def grouped_tie_flags(y, key_bits, rel: float = 1e-6):
+    """tie_flags for the grouped quantizer: an element whose quotient t lies within
+    rel of a half-integer, and vectors whose fp32 range / 15 or min lies within
+    rel of an fp16 midpoint."""
+    y = np.asarray(y, dtype=np.float32)
+    b = group_widths_per_dim(key_bits, y.shape[-1])
+    mn = y.min(axis=-1)
+    mx = y.max(axis=-1)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        scale_f = (mx - mn) / np.float32(15)
+    vec = _near_f16_midpoint(scale_f, rel) | _near_f16_midpoint(mn, rel)
+    U = f16_bits_to_f32(f32_to_f16_bits(scale_f))[..., None]
+    Z = f16_bits_to_f32(f32_to_f16_bits(mn))[..., None]
+    m = (2.0 ** (4 - b)).astype(np.float32)
+    o = ((m - 1) / 2).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        t = ((y - (Z + (o * U).astype(np.float32)).astype(np.float32)) /
+             np.where(U == 0, np.float32(1), (m * U).astype(np.float32))).astype(np.float64)
+    el = (np.abs(t - np.floor(t) - 0.5) <= rel * np.maximum(np.abs(t), 1.0)) & (U != 0)
+    return el, vec
+
+
+def grouped_key_bytes_per_token(key_bits, head_dim: int = 128) -> int:
+    """Key bytes of one (token, KV head) with group widths key_bits: 32 dims of
+    each group at its width, plus the fp16 scale and offset."""
+    b = group_widths_per_dim(key_bits, head_dim)
+    return int(b.sum()) // 8 + 4
