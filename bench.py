@@ -50,6 +50,10 @@ def decode_bytes(wl):
     c = wl.cfg
     n4, n8 = region_sizes(wl.lengths, c.sink, c.recent)
     main = {2: BYTES_INT2, 3: BYTES_INT3}.get(c.code_bits, BYTES_INT4)
+    if c.key_bits:
+        # keys with a width per RoPE-block group: 32 dims per group at its width
+        # plus fp16 scale / offset, values at code_bits
+        main = 4 * sum(c.key_bits) + 4 + 16 * c.code_bits + 4
     kv = int((c.num_kv_heads * (main * n4 + BYTES_INT8 * n8)).sum())
     P = wl.page_size
     lo4, hi4 = c.sink, wl.lengths - c.recent
@@ -229,6 +233,8 @@ def budget_variants(cfg, max_len):
         ("KV8 everywhere (s+w >= L)", dict(sink=cfg.sink, recent=max(max_len - cfg.sink, cfg.recent))),
         ("K3V3: 3-bit main cache (s=%d, w=%d)" % (cfg.sink, cfg.recent), dict(code_bits=3)),
         ("K2V2: 2-bit main cache (s=%d, w=%d)" % (cfg.sink, cfg.recent), dict(code_bits=2)),
+        ("K(4,3,3,2)V3: key widths per RoPE-block group, h=8 (the bytes of K3V3)",
+         dict(code_bits=3, key_bits=(4, 3, 3, 2), had_block=8)),
     ]
 
 
@@ -253,7 +259,8 @@ def measure_variants(torch, cfg, steps, warmup, only=None):
         if db["total"] < (2 << 30):
             for _ in range(3):
                 c2 = QuantKVCache(vcfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
-                                  vcfg.had_block, vcfg.sink, vcfg.recent, code_bits=vcfg.code_bits)
+                                  vcfg.had_block, vcfg.sink, vcfg.recent, code_bits=vcfg.code_bits,
+                                  key_bits=vcfg.key_bits or None)
                 c2.int4_pool.copy_(dw.cache.int4_pool)
                 c2.int8_pool.copy_(dw.cache.int8_pool)
                 copies.append(c2)
@@ -269,7 +276,8 @@ def measure_variants(torch, cfg, steps, warmup, only=None):
             dw.decode_step()
             if ev:
                 ev[2].record()
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        # the fused launch does not serve grouped key widths
+        fev = [] if vcfg.key_bits else [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i in range(len(fev)):
             dw.cache = copies[i % len(copies)]
             fev[i][0].record()
@@ -281,7 +289,7 @@ def measure_variants(torch, cfg, steps, warmup, only=None):
         fus = np.array([e[0].elapsed_time(e[1]) for e in fev]) * 1e3 if fev else None
         us = float(np.median(dec))
         res.append(dict(variant=tag, sink=vcfg.sink, recent=vcfg.recent, had_block=vcfg.had_block,
-                        code_bits=vcfg.code_bits,
+                        code_bits=vcfg.code_bits, key_bits=list(vcfg.key_bits) or None,
                         decode_algorithmic_bytes=db["total"], decode_us=round(us, 2),
                         append_us=round(float(np.median(app)), 2),
                         fused_us=round(float(np.median(fus)), 2) if fus is not None else None,
@@ -719,9 +727,9 @@ def main():
                             for name in OTHER_WORKLOADS if name != cfg.name]
     if not args.no_sub4bit:
         # the 3- and 2-bit main caches (same lengths, seeds and INT8 protection): decode time and bytes
-        for tag in ("K3V3", "K2V2"):
+        for tag, key in (("K3V3", "k3v3"), ("K2V2", "k2v2"), ("K(4,3,3,2)V3", "grouped_keys_k4332_v3")):
             kx = measure_variants(torch, cfg, steps=max(5, min(args.steps, 20)), warmup=3, only=tag)
-            rec[tag.lower()] = kx[0] if kx else None
+            rec[key] = kx[0] if kx else None
     if not args.no_prefill:
         rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2,
                                          cpu=not args.no_cpu_baseline)

@@ -26,6 +26,7 @@ class KvqCache(ctypes.Structure):
         ("int4_pool", c_vp),
         ("int8_pool", c_vp),
         ("code_bits", c_i32),
+        ("key_bits", c_i32 * 4),
     ]
 
 

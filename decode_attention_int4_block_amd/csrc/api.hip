@@ -43,8 +43,9 @@ constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
 constexpr int32_t kSegWeight = 2;
 constexpr int kMaxDevices = 64;
 // per device, group class (g <= 4, <= 8, <= 16), main-cache width (4, 2, 3 bits)
-// and kernel (attention only, fused append)
-std::atomic<int> g_max_workers[kMaxDevices][18];
+// and kernel (attention only, fused append); then the grouped-key kernels
+// (attention only, g <= 4 or <= 8, value width)
+std::atomic<int> g_max_workers[kMaxDevices][24];
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -62,6 +63,16 @@ kvq_status check_cache(const kvq_cache *c) {
     if ((int64_t)c->sink + c->recent > (1 << 20)) return fail(KVQ_ERR_SHAPE, "sink + recent too large");
     if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 3 && c->code_bits != 4)
         return fail(KVQ_ERR_UNSUPPORTED, "code_bits %d: the main cache holds 4-, 3- or 2-bit codes", c->code_bits);
+    if (c->key_bits[0] != 0 || c->key_bits[1] != 0 || c->key_bits[2] != 0 || c->key_bits[3] != 0) {
+        for (int j = 0; j < 4; ++j)
+            if (c->key_bits[j] < 2 || c->key_bits[j] > 4)
+                return fail(KVQ_ERR_UNSUPPORTED, "key_bits[%d] = %d: group widths are 2, 3 or 4", j, c->key_bits[j]);
+        const bool equal = c->key_bits[0] == c->key_bits[1] && c->key_bits[1] == c->key_bits[2] &&
+                           c->key_bits[2] == c->key_bits[3];
+        if (!equal && c->had_block > 8)
+            return fail(KVQ_ERR_UNSUPPORTED, "had_block %d > 8 with different group widths: a rotation block "
+                        "would span two RoPE-block groups", c->had_block);
+    }
     // the kernels index subblocks with 32-bit integers
     const uint64_t subs4 = (uint64_t)c->num_pages * (uint64_t)c->num_kv_heads * (uint64_t)(c->page_size / kvq::kSub);
     const uint64_t subs8 = (uint64_t)c->num_slots * (uint64_t)c->num_kv_heads *
@@ -74,20 +85,45 @@ kvq_status check_cache(const kvq_cache *c) {
 
 int bits_of(const kvq_cache *c) { return c->code_bits == 2 || c->code_bits == 3 ? c->code_bits : 4; }
 
+bool grouped_of(const kvq_cache *c) { return c->key_bits[0] != 0; }
+
+// Grouped keys: the key area offsets and the subblock bytes (include/kvq.h).
+struct GroupLayout {
+    int32_t off[4], key_area, sub_bytes;
+};
+
+GroupLayout group_layout(const kvq_cache *c) {
+    GroupLayout g;
+    int o = 0;
+    for (int j = 0; j < 4; ++j) {
+        g.off[j] = o;
+        o += 64 * c->key_bits[j];
+    }
+    g.key_area = o;
+    g.sub_bytes = o + kvq::value_area_bytes(bits_of(c)) + 128;
+    return g;
+}
+
+size_t main_sub_bytes_of(const kvq_cache *c) {
+    return grouped_of(c) ? (size_t)group_layout(c).sub_bytes : (size_t)kvq::main_sub_bytes(bits_of(c));
+}
+
 int nr8_of(const kvq_cache *c) { return kvq::ceil_div(c->sink + c->recent, kvq::kSub); }
 
 float inv_sqrt(int h) { return (float)(1.0 / sqrt((double)h)); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-kvq_status max_workers(int g, bool fused, int bits, int *out) {
+kvq_status max_workers(int g, bool fused, int bits, int *out, bool grouped = false) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
-    const int cls = (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + (bits == 2 ? 6 : (bits == 3 ? 12 : 0)) + (fused ? 3 : 0);
+    const int bi = bits == 2 ? 1 : (bits == 3 ? 2 : 0);
+    const int cls = grouped ? 18 + (g <= 4 ? 0 : 3) + bi
+                            : (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + 6 * bi + (fused ? 3 : 0);
     int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
-        hipError_t e = kvq::decode_max_workers(g, fused, bits, &v);
+        hipError_t e = kvq::decode_max_workers(g, fused, bits, &v, grouped);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         g_max_workers[dev][cls].store(v, std::memory_order_relaxed);
     }
@@ -122,7 +158,7 @@ extern "C" {
 
 size_t kvq_int4_pool_bytes(const kvq_cache *c) {
     if (check_cache(c) != KVQ_OK) return 0;
-    return (size_t)c->num_pages * c->num_kv_heads * (c->page_size / kvq::kSub) * kvq::main_sub_bytes(bits_of(c));
+    return (size_t)c->num_pages * c->num_kv_heads * (c->page_size / kvq::kSub) * main_sub_bytes_of(c);
 }
 
 size_t kvq_int8_pool_bytes(const kvq_cache *c) {
@@ -164,7 +200,14 @@ kvq_status kv_quant_append(const kvq_cache *c, const uint16_t *k, const uint16_t
     a.nr8 = nr8_of(c);
     a.bits = bits_of(c);
     a.inv_sqrt_h = inv_sqrt(c->had_block);
-    hipError_t e = kvq::launch_quant_append(a, static_cast<hipStream_t>(stream));
+    const GroupLayout gl = group_layout(c);
+    for (int j = 0; j < 4; ++j) {
+        a.key_bits[j] = c->key_bits[j];
+        a.kg_off[j] = gl.off[j];
+    }
+    a.key_area = gl.key_area;
+    a.sub_bytes = gl.sub_bytes;
+    hipError_t e = kvq::launch_quant_append(a, static_cast<hipStream_t>(stream), grouped_of(c));
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "quant-append launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -176,7 +219,8 @@ size_t kv_decode_attn_workspace_bytes(const kvq_cache *c, int32_t B, int32_t num
     // large enough for both kernels (attention only and fused append)
     int workers = 0, workers_fused = 0;
     const int bits = bits_of(c);
-    if (max_workers(g, false, bits, &workers) != KVQ_OK) return 0;
+    if (grouped_of(c) && g > 8) return 0;
+    if (max_workers(g, false, bits, &workers, grouped_of(c)) != KVQ_OK) return 0;
     if (max_workers(g, true, bits, &workers_fused) != KVQ_OK) return 0;
     const size_t a = ws_layout(c, B, g, workers).total, b = ws_layout(c, B, g, workers_fused).total;
     return a > b ? a : b;
@@ -205,12 +249,16 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     if (!q || !slot || !block_table || !ctx_len || (!out && !ceiling) || (fused && (!k_new || !v_new)))
         return fail(KVQ_ERR_NULL, "a required device pointer is NULL");
     if (ceiling && g > 8) return fail(KVQ_ERR_UNSUPPORTED, "the read ceiling covers query groups up to 8");
+    const bool grouped = grouped_of(c);
+    if (grouped && (fused || ceiling))
+        return fail(KVQ_ERR_UNSUPPORTED, "grouped key widths are served by kv_quant_append + kv_decode_attn");
+    if (grouped && g > 8) return fail(KVQ_ERR_UNSUPPORTED, "grouped key widths: query group %d > 8", g);
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
     int workers = 0;
-    st = max_workers(g, fused, bits_of(c), &workers);
+    st = max_workers(g, fused, bits_of(c), &workers, grouped);
     if (st != KVQ_OK) return st;
     const WsLayout l = ws_layout(c, B, g, workers);
     if (workspace_bytes < l.total)
@@ -238,6 +286,13 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.nr8 = nr8_of(c);
     a.bits = bits_of(c);
     a.inv_sqrt_h = inv_sqrt(c->had_block);
+    const GroupLayout gl = group_layout(c);
+    for (int j = 0; j < 4; ++j) {
+        a.key_bits[j] = c->key_bits[j];
+        a.kg_off[j] = gl.off[j];
+    }
+    a.key_area = gl.key_area;
+    a.sub_bytes = gl.sub_bytes;
     a.max_workers = workers;
     a.min_units = kMinUnitsPerWorker;
     for (int i = 0; i < 4; ++i) a.part_wt[i] = kPartWeights[i];
@@ -252,7 +307,7 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.out = out;
     a.lse = lse;
     hipError_t e = ceiling ? kvq::launch_decode_read_ceiling(a, workers, static_cast<hipStream_t>(stream))
-                           : kvq::launch_decode(a, workers, static_cast<hipStream_t>(stream));
+                           : kvq::launch_decode(a, workers, static_cast<hipStream_t>(stream), grouped);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -360,8 +415,9 @@ kvq_status kv_prefill_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
-    if (bits_of(c) != 4)
-        return fail(KVQ_ERR_UNSUPPORTED, "prefill attention reads the 4-bit cache only (code_bits %d)", c->code_bits);
+    if (bits_of(c) != 4 || grouped_of(c))
+        return fail(KVQ_ERR_UNSUPPORTED, "prefill attention reads the 4-bit cache only (code_bits %d%s)", c->code_bits,
+                    grouped_of(c) ? ", grouped key widths" : "");
     kvq::PrefillArgs a;
     a.q = q;
     a.Hq = num_q_heads;

@@ -49,6 +49,14 @@ __host__ __device__ constexpr int main_sub_bytes(int bits) {
     return bits == 2 ? kSub2Bytes : (bits == 3 ? kSub3Bytes : kSub4Bytes);
 }
 
+// Main cache with keys of a width per RoPE-block group (key_bits): group j
+// of the keys is the dims d with (d mod 32) / 8 == j.  A subblock holds the
+// group key areas (64 key_bits[j] bytes each, in group order), the value area
+// of the value width, then the key and value params (layout in include/kvq.h).
+__host__ __device__ constexpr int value_area_bytes(int bits) {
+    return bits == 2 ? 512 : (bits == 3 ? 768 : 1024);
+}
+
 // Workspace of the decode attention: header, per-row cost prefix, partial pieces.
 constexpr int kPieceStride = 132;           // floats per (piece, query head): m, l, 0, 0, acc[128]
 constexpr size_t kWsHeaderBytes = 256;
@@ -192,8 +200,12 @@ struct AppendArgs {
     uint8_t *int4_pool;
     uint8_t *int8_pool;
     int32_t H, P, h, s, w, nr8;
-    int32_t bits;       // main cache code width: 4, 3 or 2
+    int32_t bits;       // main cache code width: 4, 3 or 2 (the values' with grouped keys)
     float inv_sqrt_h;   // fp32 value nearest to 1/sqrt(h)
+    int32_t key_bits[4];    // grouped keys: width of each RoPE-block group (KG launches)
+    int32_t kg_off[4];      // grouped keys: byte offset of each group's key area
+    int32_t key_area;       // grouped keys: bytes of the key area
+    int32_t sub_bytes;      // grouped keys: bytes of a main-cache subblock
 };
 
 struct DecodeArgs {
@@ -214,6 +226,10 @@ struct DecodeArgs {
     int32_t max_workers, min_units;
     int32_t part_wt[4];                 // worker weights (Partition)
     int32_t seg_wt;                     // weight-only units counted before each segment
+    int32_t key_bits[4];    // grouped keys: width of each RoPE-block group (KG launches)
+    int32_t kg_off[4];      // grouped keys: byte offset of each group's key area
+    int32_t key_area;       // grouped keys: bytes of the key area
+    int32_t sub_bytes;      // grouped keys: bytes of a main-cache subblock
     int32_t *ws_header;     // [0] workers of this launch
     int32_t *ws_first;      // [B*H] worker that attended the segment's first unit
     int32_t *ws_last;       // [B*H] worker that attended the segment's last unit
@@ -243,10 +259,10 @@ struct PrefillArgs {
     float *lse;                 // [N][Hq] or nullptr
 };
 
-hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream, bool grouped = false);
 hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream, bool grouped = false);
 hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t stream);
-hipError_t decode_max_workers(int g, bool fused, int bits, int *out);
+hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool grouped = false);
 
 }  // namespace kvq

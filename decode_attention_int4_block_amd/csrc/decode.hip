@@ -141,6 +141,7 @@ struct SegCtx {
     half8 q4[GC<GP>::kQ][4];   // query operands (INT4 nibble order; INT8 keys are split into nibbles)
     float K1;           // 2^(24 - e) * log2(e) / sqrt(128), wave-uniform
     float Rh;           // sum(q~ of this lane's head) * 2^(e - 24)
+    float Ko;           // grouped keys: sum(o_d q~_d) * 2^(e - 24) over this lane's head (else 0)
     float mK;           // running max of this lane's head (log2 units)
     float lsum, zsum;   // sums of p and of p * zero_v over this lane's scores
     floatx4 O[8];       // acc[row 4G+i][16 t + n], odd tiles scaled by 16
@@ -330,7 +331,7 @@ __device__ inline QRing<GP> read_query(const uint8_t *slot, int lane) {
     return q;
 }
 
-template <int GP>
+template <int GP, bool KG = false>
 __device__ inline void build_query(const DecodeArgs &a, const QRing<GP> &qr, const LaneCtx<GP> &L, SegCtx<GP> &c) {
     constexpr int V = GC<GP>::kVPL;
     constexpr int CPL = V / 8;            // chunks of 8 dims per lane (= kNP)
@@ -382,11 +383,23 @@ __device__ inline void build_query(const DecodeArgs &a, const QRing<GP> &qr, con
 #pragma unroll
         for (int i = 0; i < V; ++i) x[i] = butterfly<32>(x[i], L.lane);
     }
-    float sum = 0.0f, amax = 0.0f;
+    float sum = 0.0f, amax = 0.0f, osum = 0.0f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         sum += x[i];
         amax = fmaxf(amax, fabsf(x[i]));
+    }
+    if constexpr (KG) {
+        // grouped keys: the levels of a width-b group sit o_b U = (2^(4-b) - 1) U / 2
+        // above Z, a per-head constant of the score (dim 32 G + V part + i is in
+        // group (V part + i) / 8)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int jg = (V * L.part + i) >> 3;
+            const int b = jg == 0 ? a.key_bits[0] : (jg == 1 ? a.key_bits[1] : (jg == 2 ? a.key_bits[2] : a.key_bits[3]));
+            osum = fmaf((float)((1 << (4 - b)) - 1) * 0.5f, x[i], osum);
+        }
+        osum = head_sum<GP>(osum) * a.inv_sqrt_h;
     }
     sum = head_sum<GP>(sum) * a.inv_sqrt_h;
     amax = max_rows(amax);
@@ -401,6 +414,7 @@ __device__ inline void build_query(const DecodeArgs &a, const QRing<GP> &qr, con
     const float c0 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
     c.K1 = ldexpf(c0, 24 - e);
     c.Rh = ldexpf(sum, e - 24);
+    c.Ko = KG ? ldexpf(osum, e - 24) : 0.0f;
     // chunks of 8 dims in the nibble order of a code dword:
     // dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
     uint32_t H[CPL][4], Lo[CPL][4];
@@ -528,11 +542,11 @@ __device__ inline void softmax_dense(SegCtx<GP> &c, const LaneCtx<GP> &L, const 
 // (keys) and 1024 / 1536 (values), and its params like an INT4 step.  A 3-bit
 // step copies its low planes the same way and its two 256-byte high planes to
 // 2048 (keys) and 2560 (values).
-template <int BITS>
+template <int BITS, bool KG = false>
 __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lookup &k, uint8_t *st,
                                   uint32_t offK, uint32_t offV, uint32_t offP4, uint32_t offP8, int lane) {
     if (c.r < c.rp.n4) {
-        constexpr uint32_t kSubBytes = (uint32_t)main_sub_bytes(BITS);
+        const uint32_t kSubBytes = KG ? (uint32_t)a.sub_bytes : (uint32_t)main_sub_bytes(BITS);
         const int pos0 = (c.rp.k0 + c.r) * 32;
         // subblock indices fit 32 bits (the descriptor check bounds the pools);
         // a page holds 1 << (logP - 4) subblocks of a KV head
@@ -545,6 +559,34 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
         const uint8_t *baseB = pos0 + 16 >= c.rp.hi4 ? baseA
             : sh > 0 ? baseA + kSubBytes
             : a.int4_pool + (uint64_t)((uint32_t)k.pageB * (uint32_t)a.H + (uint32_t)c.hk) * kSubBytes;
+        if constexpr (KG) {
+            // grouped keys: the key areas of A and B verbatim to 0 / 1024 (4 sum(b)
+            // lanes of 16 B each, at least 32), the value areas to 2048 (4 bits: A
+            // 2048, B 3072; 2 and 3 bits: low planes A 2048, B 2560, high planes
+            // A 3072, B 3328), the params as for INT4: five loads
+            const uint32_t off = 16 * (uint32_t)lane;
+            if ((int)off < a.key_area) {
+                dma16_stream(baseA, off, st + 0);
+                dma16_stream(baseB, off, st + 1024);
+            }
+            const uint8_t *va = baseA + a.key_area, *vb = baseB + a.key_area;
+            if constexpr (BITS == 4) {
+                dma16_stream(va, off, st + 2048);
+                dma16_stream(vb, off, st + 3072);
+            } else if constexpr (BITS == 2) {
+                if (lane < 32) {
+                    dma16_stream(va, off, st + 2048);
+                    dma16_stream(vb, off, st + 2560);
+                }
+            } else {
+                dma16_stream(lane < 32 ? va : vb, 16 * (uint32_t)(lane & 31), st + 2048);
+                if (lane < 32) dma16_stream((lane < 16 ? va : vb) + 512, 16 * (uint32_t)(lane & 15), st + 3072);
+            }
+            const uint32_t offPg = (uint32_t)(a.key_area + value_area_bytes(BITS)) + ((lane & 8) ? 64u : 0u) +
+                                   (uint32_t)(lane & 3) * 16u;
+            if (lane < 16) dma16_stream((lane & 4) ? baseB : baseA, offPg, st + 4096);
+            return;
+        }
         if constexpr (BITS == 2) {
             const uint32_t off = 16 * (uint32_t)lane;
             if (lane < 32) {
@@ -600,11 +642,46 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // main2: a 2- or 3-bit main-cache step (8 bytes of low-plane codes per lane and
 // quarter; at 3 bits the lane's high-plane dword goes to word 2).
-template <int GP, int BITS>
-__device__ inline StepRegs<GP> read_stage(const uint8_t *st, const LaneCtx<GP> &L, bool main2) {
+__device__ inline uint32_t lds16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
+
+// KG: grouped keys.  A main-cache step then holds, per group i, this lane's
+// slot of the group's key area in kA[i] / kB[i] (subblocks A / B): the nibble
+// dword (width 4), the 16-bit field word (width 2), or the field word with the
+// high-bit byte in bits 16-23 (width 3); values as the value width's step, at
+// the stage offsets the grouped copy uses.
+template <int GP, int BITS, bool KG = false>
+__device__ inline StepRegs<GP> read_stage(const DecodeArgs &a, const uint8_t *st, const LaneCtx<GP> &L, bool main2) {
     StepRegs<GP> r;
     const int lane = L.lane;
-    if ((BITS == 2 || BITS == 3) && main2) {
+    if (KG && main2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = a.key_bits[i];
+            const uint8_t *g = st + a.kg_off[i];
+            if (b == 4) {
+                r.kA[i] = lds32(g + 4 * lane);
+                r.kB[i] = lds32(g + 1024 + 4 * lane);
+            } else {
+                r.kA[i] = lds16(g + 2 * lane);
+                r.kB[i] = lds16(g + 1024 + 2 * lane);
+                if (b == 3) {
+                    r.kA[i] |= (uint32_t)g[128 + lane] << 16;
+                    r.kB[i] |= (uint32_t)g[1024 + 128 + lane] << 16;
+                }
+            }
+        }
+        if constexpr (BITS == 4) {
+            r.vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
+            r.vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
+        } else {
+            const u32x2 va = *reinterpret_cast<const u32x2 *>(st + 2048 + lane * 8);
+            const u32x2 vb = *reinterpret_cast<const u32x2 *>(st + 2560 + lane * 8);
+            const uint32_t vha = BITS == 3 ? lds32(st + 3072 + 4 * lane) : 0u;
+            const uint32_t vhb = BITS == 3 ? lds32(st + 3328 + 4 * lane) : 0u;
+            r.vA = u32x4{va[0], va[1], vha, 0u};
+            r.vB = u32x4{vb[0], vb[1], vhb, 0u};
+        }
+    } else if ((BITS == 2 || BITS == 3) && main2) {
         const u32x2 ka = *reinterpret_cast<const u32x2 *>(st + lane * 8);
         const u32x2 kb = *reinterpret_cast<const u32x2 *>(st + 512 + lane * 8);
         const u32x2 va = *reinterpret_cast<const u32x2 *>(st + 1024 + lane * 8);
@@ -716,13 +793,48 @@ __device__ inline uint32_t int3_value_field(uint32_t x, uint32_t hv, int cc, int
     return int2_field(x, f) | (h & ((f & 1) ? 0x00400040u : 0x00040004u));
 }
 
-template <int GP, int BITS>
-__device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r, bool main2) {
+// Grouped keys: the MFMA operand of one group's slot word x, each code c as the
+// f16 subnormal (m c) 2^-24 (m = 2^(4 - b)) in the nibble order of the 4-bit
+// operand -- dims (0, 4), (1, 5) x 16, (2, 6), (3, 7) x 16 of the group's 8 --
+// so that the query operands serve every width.
+__device__ inline half8 group_key_operand(uint32_t x, int b) {
+    if (b == 4) {
+        const uint32_t x8 = x >> 8;
+        return pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
+    }
+    // bytes 0 and 1 (dims 0-3, 4-7 at bits 2f) to the two 16-bit halves
+    const uint32_t y = (x & 0xFFu) | ((x & 0xFF00u) << 8);
+    if (b == 2)
+        return pack8((y << 2) & 0x000C000Cu, (y << 4) & 0x00C000C0u, (y >> 2) & 0x000C000Cu, y & 0x00C000C0u);
+    // width 3: 2 c = 2 lo + 8 hi; the high bits of dims 0-3 / 4-7 to bits 0-3 / 16-19
+    const uint32_t h = x >> 16;
+    const uint32_t H = (h & 0x0Fu) | ((h & 0xF0u) << 12);
+    return pack8(((y << 1) & 0x00060006u) | ((H << 3) & 0x00080008u),
+                 ((y << 3) & 0x00600060u) | ((H << 6) & 0x00800080u),
+                 ((y >> 3) & 0x00060006u) | ((H << 1) & 0x00080008u),
+                 ((y >> 1) & 0x00600060u) | ((H << 4) & 0x00800080u));
+}
+
+template <int GP, int BITS, bool KG = false>
+__device__ inline KAcc<GP> kpart_mfma(const DecodeArgs &a, const SegCtx<GP> &c, const StepRegs<GP> &r, bool main2) {
     constexpr int kQ = GC<GP>::kQ;
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
     KAcc<GP> k;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) k.dA[q] = k.dB[q] = zero4;
+    if (KG && main2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = a.key_bits[i];
+            const half8 ak = group_key_operand(r.kA[i], b), bk = group_key_operand(r.kB[i], b);
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
+                k.dB[q] = mfma16(bk, c.q4[q][i], k.dB[q]);
+            }
+        }
+        return k;
+    }
     if ((BITS == 2 || BITS == 3) && main2) {
         // chunk i: dword i / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
 #pragma unroll
@@ -755,7 +867,7 @@ __device__ inline KAcc<GP> kpart_mfma(const SegCtx<GP> &c, const StepRegs<GP> &r
 
 // Scores of a step from its key accumulators: hi + lo columns, the dense
 // layout, scale/offset, validity.
-template <int GP>
+template <int GP, bool KG = false>
 __device__ inline KOut<GP> kpart_tail(const SegCtx<GP> &c, const LaneCtx<GP> &L, const StepRegs<GP> &r,
                                       const KAcc<GP> &ka, bool int8, int base, int lo, int hi) {
     constexpr int kQ = GC<GP>::kQ, NE = GC<GP>::kNE;
@@ -780,7 +892,8 @@ __device__ inline KOut<GP> kpart_tail(const SegCtx<GP> &c, const LaneCtx<GP> &L,
         // (possibly NaN as fp16): computed anyway, then dropped by a select
         // (never multiplied by zero)
         const bool ok = (uint32_t)L.tok4[e] + off < span;
-        const float ts = tscore(d[e], r.kp[e], c.Rh);
+        // grouped keys: the levels' offsets o_b U, a per-head constant (main-cache steps only)
+        const float ts = tscore(KG && !int8 ? d[e] + c.Ko : d[e], r.kp[e], c.Rh);
         k.t[e] = ok ? ts : kNegInf;
         k.vp[e] = ok ? r.vp[e] : 0u;
     }
@@ -1082,7 +1195,9 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
 // split, page gathers, DMA ring, waits and stage reads, without the arithmetic
 // and without outputs -- the bandwidth this access pattern reaches on the
 // device, as a measured ceiling for the full kernel.
-template <int GP, bool APPEND, int BITS, bool MEM = false>
+// KG = true: the main cache holds keys with a width per RoPE-block group
+// (a.key_bits) and values of width BITS.
+template <int GP, bool APPEND, int BITS, bool MEM = false, bool KG = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecodeArgs a) {
     using SL = SmemLayout<GP, APPEND>;
@@ -1265,7 +1380,7 @@ void decode_split_kernel(DecodeArgs a) {
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + s * kKvBytes, lane);
             }
-            issue_step<BITS>(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
+            issue_step<BITS, KG>(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
             cursor_next(a, R, P);
             ++issued;
             advance_half(P);
@@ -1311,7 +1426,7 @@ void decode_split_kernel(DecodeArgs a) {
     if constexpr (APPEND) {
         if (C.r == C.rp.rn) append_new_token<BITS>(a, R, C, kvring, smem, lane);
     }
-    StepRegs<GP> r = read_stage<GP, BITS>(smem, L, C.r < C.rp.n4);
+    StepRegs<GP> r = read_stage<GP, BITS, KG>(a, smem, L, C.r < C.rp.n4);
     QRing<GP> qr = read_query<GP>(qring, lane);     // the first step opens a segment
     wait_lgkm0();
     look = uniform(look);
@@ -1333,7 +1448,7 @@ void decode_split_kernel(DecodeArgs a) {
             }
             // a segment's first step finds mK = -inf and scales O, lsum and
             // zsum (finite leftovers of the previous segment) by 0
-            build_query<GP>(a, qr, L, c);
+            build_query<GP, KG>(a, qr, L, c);
             c.mK = kNegInf;
             open = true;
         }
@@ -1341,9 +1456,9 @@ void decode_split_kernel(DecodeArgs a) {
         const int sbase = int4 ? (C.rp.k0 + C.r) * 32 : e0;
         const int slo = int4 ? C.rp.lo4 : 0;
         const int shi = int4 ? C.rp.hi4 : min(C.rp.n8e, e0 + 16);
-        const KAcc<GP> ka = kpart_mfma<GP, BITS>(c, r, int4);
+        const KAcc<GP> ka = kpart_mfma<GP, BITS, KG>(a, c, r, int4);
         if (pend) vpart<GP, BITS>(c, L, kp);    // previous step, same segment
-        kp = kpart_tail<GP>(c, L, r, ka, !int4, sbase, slo, shi);
+        kp = kpart_tail<GP, KG>(c, L, r, ka, !int4, sbase, slo, shi);
         pend = true;
         E = C;
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
@@ -1356,7 +1471,7 @@ void decode_split_kernel(DecodeArgs a) {
                 if (C.r == C.rp.rn)
                     append_new_token<BITS>(a, R, C, kvring + snxt * kKvBytes, smem + snxt * kStageBytes, lane);
             }
-            r = read_stage<GP, BITS>(smem + snxt * kStageBytes, L, C.r < C.rp.n4);
+            r = read_stage<GP, BITS, KG>(a, smem + snxt * kStageBytes, L, C.r < C.rp.n4);
             if (!open) qr = read_query<GP>(qring + snxt * QRing<GP>::kBytes, lane);
         }
         // producer: step P into the slot this iteration's step was read from
@@ -1366,7 +1481,7 @@ void decode_split_kernel(DecodeArgs a) {
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + scur * kKvBytes, lane);
             }
-            issue_step<BITS>(a, P, look, smem + scur * kStageBytes, offK, offV, offP4, offP8, lane);
+            issue_step<BITS, KG>(a, P, look, smem + scur * kStageBytes, offK, offV, offP4, offP8, lane);
             cursor_next(a, R, P);
             ++issued;
             advance_half(P);
@@ -1664,14 +1779,29 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
     }
 }
 
-template <int GP, bool APPEND, int BITS>
-static const void *split_fn() { return reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS>); }
+template <int GP, bool APPEND, int BITS, bool KG = false>
+static const void *split_fn() {
+    return reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS, false, KG>);
+}
 
 static int group_class(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 
-hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream, bool grouped) {
     const bool fused = a.k_new != nullptr;
-    if (a.bits == 2) {
+    if (grouped) {
+        // grouped keys: attention only, query groups up to 8 (checked by the caller)
+        const bool g4 = group_class(a.g) == 4;
+        if (a.bits == 2) {
+            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, false, true>), dim3(grid), dim3(64), 0, stream, a);
+            else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, false, true>), dim3(grid), dim3(64), 0, stream, a);
+        } else if (a.bits == 3) {
+            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, false, true>), dim3(grid), dim3(64), 0, stream, a);
+            else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, false, true>), dim3(grid), dim3(64), 0, stream, a);
+        } else {
+            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, false, true>), dim3(grid), dim3(64), 0, stream, a);
+            else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, false, true>), dim3(grid), dim3(64), 0, stream, a);
+        }
+    } else if (a.bits == 2) {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
             case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
             case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
@@ -1722,7 +1852,7 @@ hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t decode_max_workers(int g, bool fused, int bits, int *out) {
+hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool grouped) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -1732,7 +1862,11 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out) {
     int per_cu = 0;
     const int cls = group_class(g);
     const void *fn;
-    if (bits == 2 && fused)
+    if (grouped)
+        fn = bits == 2 ? (cls == 4 ? split_fn<4, false, 2, true>() : split_fn<8, false, 2, true>())
+           : bits == 3 ? (cls == 4 ? split_fn<4, false, 3, true>() : split_fn<8, false, 3, true>())
+                       : (cls == 4 ? split_fn<4, false, 4, true>() : split_fn<8, false, 4, true>());
+    else if (bits == 2 && fused)
         fn = cls == 4 ? split_fn<4, true, 2>() : (cls == 8 ? split_fn<8, true, 2>() : split_fn<16, true, 2>());
     else if (bits == 2)
         fn = cls == 4 ? split_fn<4, false, 2>() : (cls == 8 ? split_fn<8, false, 2>() : split_fn<16, false, 2>());

@@ -47,6 +47,21 @@ __device__ inline uint32_t qcode(float y, const QParams &p, float qmax) {
     return (uint32_t)r;
 }
 
+// Code of a key dim whose RoPE-block group has width b (grouped keys): the
+// step is 2^(4 - b) U and the levels are centred in the 4-bit span, so Z_b =
+// Z + (2^(4 - b) - 1) U / 2 (p holds U and Z, the 4-bit params).
+__device__ inline uint32_t gcode(float y, const QParams &p, int b) {
+#pragma clang fp contract(off)
+    if (p.sf == 0.0f) return 0u;
+    const float m = (float)(1 << (4 - b));
+    const float o = (m - 1.0f) * 0.5f;
+    const float zb = p.zf + o * p.sf;
+    float t = __fdiv_rn(y - zb, m * p.sf);
+    float r = rintf(t);
+    r = fminf(fmaxf(r, 0.0f), (float)((1 << b) - 1));
+    return (uint32_t)r;
+}
+
 __device__ inline uint32_t qparam_word(const QParams &p) {
     return (uint32_t)__half_as_ushort(p.sh) | ((uint32_t)__half_as_ushort(p.zh) << 16);
 }
@@ -63,8 +78,11 @@ struct TokenCodes {
 // kw: this lane's bf16 pair of key dims 2l, 2l+1; vlo, vhi: its value dims
 // n + 32c and n + 16 + 32c (bf16 bits).  qmain: levels - 1 of the main cache
 // (15, or 7 / 3 for the 3- / 2-bit caches).
+//
+// kbits != 0: grouped keys, this lane's key dims having width kbits; the key
+// params are then the 4-bit ones (U, Z) and the codes come from gcode.
 __device__ inline TokenCodes quantize_token(uint32_t kw, uint32_t vlo, uint32_t vhi, int h, float inv_sqrt_h,
-                                            int lane, float qmain = 15.0f) {
+                                            int lane, float qmain = 15.0f, int kbits = 0) {
 #pragma clang fp contract(off)
     // ---- keys: fp32 block Hadamard, strides 1, 2, ..., h/2 ascending --------
     float x0 = bf16_to_f32(kw & 0xFFFFu);
@@ -93,9 +111,12 @@ __device__ inline TokenCodes quantize_token(uint32_t kw, uint32_t vlo, uint32_t 
     const float vmx = wave_max(fmaxf(v0, v1));
     TokenCodes t;
     {
-        const QParams kp = qparams(kmn, kmx, qmain);
+        const QParams kp = qparams(kmn, kmx, kbits ? 15.0f : qmain);
         const QParams vp = qparams(vmn, vmx, qmain);
-        t.k4 = (uint8_t)(qcode(x0, kp, qmain) | (qcode(x1, kp, qmain) << 4));
+        if (kbits)
+            t.k4 = (uint8_t)(gcode(x0, kp, kbits) | (gcode(x1, kp, kbits) << 4));
+        else
+            t.k4 = (uint8_t)(qcode(x0, kp, qmain) | (qcode(x1, kp, qmain) << 4));
         t.v4 = (uint8_t)(qcode(v0, vp, qmain) | (qcode(v1, vp, qmain) << 4));
         t.kp4 = qparam_word(kp);
         t.vp4 = qparam_word(vp);
@@ -237,6 +258,56 @@ __device__ inline void store_token_int3(const TokenCodes &t, uint8_t *base3, int
 __device__ inline void store_token_int2(const TokenCodes &t, uint8_t *base2, int tok, int lane) {
     put_sub2_token<2>(sub2_token<2>(t, lane), t, base2 + kSub2K, base2 + kSub2V, nullptr, nullptr, base2 + kSub2KP,
                       base2 + kSub2VP, tok, lane);
+}
+
+// Grouped keys: the RoPE-block group of this lane's key dims 2l, 2l + 1.
+__device__ inline int key_group_of_lane(int lane) { return (lane & 15) >> 2; }
+
+// Stores of one token into a grouped-key subblock (layout in include/kvq.h):
+// this lane's key codes (dims e, e + 1 of slot 16 G + tok, e = 2 (l % 4)) at
+// their group's width, the value codes at BITS (the value area starts at
+// a.key_area), the params.  The key bytes of width 2 and 3 join the codes of
+// two or four lanes by shuffles, so every lane must call it.
+template <int BITS>
+__device__ inline void store_token_grouped(const TokenCodes &t, uint8_t *base, int tok, int lane,
+                                           const int32_t (&key_bits)[4], const int32_t (&kg_off)[4],
+                                           int key_area) {
+    const int j = key_group_of_lane(lane);
+    const int b = j == 0 ? key_bits[0] : (j == 1 ? key_bits[1] : (j == 2 ? key_bits[2] : key_bits[3]));
+    const int off = j == 0 ? kg_off[0] : (j == 1 ? kg_off[1] : (j == 2 ? kg_off[2] : kg_off[3]));
+    const int s = 16 * (lane >> 4) + tok;
+    const int k = lane & 3;
+    const uint32_t c0 = t.k4 & 15u, c1 = (uint32_t)t.k4 >> 4;
+    // two-bit fields of dims e, e + 1 in their byte (width 2 codes, or the low
+    // bits of width 3), joined with the other lane of the byte
+    uint32_t lo = (((c0 & 3u) | ((c1 & 3u) << 2)) << (4 * (k & 1)));
+    lo |= (uint32_t)__shfl_xor((int)lo, 1, 64);
+    // bit 2 of dims e, e + 1 at bits e, e + 1 of the slot's high byte
+    uint32_t hi = (((c0 >> 2) & 1u) | (((c1 >> 2) & 1u) << 1)) << (2 * k);
+    hi |= (uint32_t)__shfl_xor((int)hi, 1, 64);
+    hi |= (uint32_t)__shfl_xor((int)hi, 2, 64);
+    uint8_t *kg = base + off;
+    if (b == 4) {
+        kg[4 * s + k] = t.k4;
+    } else {
+        if ((k & 1) == 0) kg[2 * s + (k >> 1)] = (uint8_t)lo;
+        if (b == 3 && k == 0) kg[128 + s] = (uint8_t)hi;
+    }
+    uint8_t *va = base + key_area;
+    if constexpr (BITS == 4) {
+        va[sub_v_byte(tok, lane)] = t.v4;
+    } else {
+        const Sub2Token s2 = sub2_token<BITS>(t, lane);
+        if (((lane >> 4) & 1) == 0) va[sub2_v_byte(tok, lane)] = (uint8_t)s2.vb;
+        if constexpr (BITS == 3) {
+            if (lane < 16) va[512 + 4 * ((tok >> 2) * 16 + lane) + (tok & 3)] = (uint8_t)s2.vh;
+        }
+    }
+    if (lane == 0) {
+        uint8_t *pp = va + value_area_bytes(BITS);
+        *reinterpret_cast<uint32_t *>(pp + 4 * tok) = t.kp4;
+        *reinterpret_cast<uint32_t *>(pp + 64 + 4 * tok) = t.vp4;
+    }
 }
 
 // INT8 ring copy of one token (when write8).

@@ -32,7 +32,8 @@ class DeviceWorkload:
         B = cfg.batch
         self.B = B
         self.cache = QuantKVCache(cfg.num_kv_heads, wl.page_size, max(wl.num_pages, 1), wl.num_slots,
-                                  cfg.had_block, cfg.sink, cfg.recent, device=self.device, code_bits=cfg.code_bits)
+                                  cfg.had_block, cfg.sink, cfg.recent, device=self.device, code_bits=cfg.code_bits,
+                                  key_bits=cfg.key_bits or None)
         self.block_table = torch.from_numpy(wl.block_table).to(self.device)
         self.slots = torch.from_numpy(wl.slots.astype(np.int32)).to(self.device)
         self.lengths = wl.lengths.astype(np.int64)
@@ -121,8 +122,10 @@ class DeviceWorkload:
     # --- inspection helpers (host copies of what the GPU wrote) ----------------
     def int4_subblocks(self, idx: np.ndarray) -> np.ndarray:
         """Main-cache subblocks (INT4, or 3- / 2-bit when the cache holds such codes)."""
-        from .layout import SUB2_BYTES, SUB3_BYTES, SUB4_BYTES
+        from .layout import SUB2_BYTES, SUB3_BYTES, SUB4_BYTES, subg_bytes
         nb = {2: SUB2_BYTES, 3: SUB3_BYTES}.get(self.cache.code_bits, SUB4_BYTES)
+        if self.cache.key_bits:
+            nb = subg_bytes(self.cache.key_bits, self.cache.code_bits)
         pool = self.cache.int4_pool[: (self.cache.int4_pool.numel() // nb) * nb]
         t = torch.from_numpy(np.asarray(idx, np.int64)).to(self.device)
         return pool.view(-1, nb).index_select(0, t).cpu().numpy()

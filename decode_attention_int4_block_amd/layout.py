@@ -140,3 +140,56 @@ def decode_sub3(blocks: np.ndarray, tok) -> dict:
         off = 1280 + 4 * (G * 16 + n) + r
         vc[:, d] |= ((blocks[rows, off] >> bit) & 1) << 2
     return dict(k=kc, v=vc, **_params(blocks, t, 1536, 1600))
+
+
+# --- keys with a width per RoPE-block group ----------------------------------
+
+
+def subg_bytes(key_bits, vbits: int) -> int:
+    """Bytes of a grouped-key subblock: key areas, value area, params."""
+    return 64 * int(sum(key_bits)) + {2: 512, 3: 768}.get(vbits, 1024) + 128
+
+
+def decode_subg(blocks: np.ndarray, tok, key_bits, vbits: int) -> dict:
+    """Codes and fp16 params of token `tok` (0..15) of each grouped-key subblock:
+    group j's key area at 64 (key_bits[0] + .. + key_bits[j-1]), slot 16 G + t
+    holding dims 32 G + 8 j + e (width 4: a nibble dword; width 2: two bytes,
+    dim 4 k + f at bits 2 f of byte k; width 3: those low bits, then a byte at
+    +128 with bit 2 of dim e at bit e), then the value area in the value
+    width's layout and the key / value params."""
+    nb = subg_bytes(key_bits, vbits)
+    blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, nb)
+    t = np.asarray(tok, dtype=np.int64).reshape(-1)
+    rows = np.arange(blocks.shape[0])
+    N = blocks.shape[0]
+    kc = np.zeros((N, 128), np.uint8)
+    off = 0
+    for j, b in enumerate(key_bits):
+        for G in range(4):
+            s_ = 16 * G + t
+            for e in range(8):
+                d = 32 * G + 8 * j + e
+                if b == 4:
+                    byte = blocks[rows, off + 4 * s_ + e // 2]
+                    kc[:, d] = (byte >> (4 * (e % 2))) & 0xF
+                else:
+                    byte = blocks[rows, off + 2 * s_ + e // 4]
+                    c = (byte >> (2 * (e % 4))) & 3
+                    if b == 3:
+                        c = c | (((blocks[rows, off + 128 + s_] >> e) & 1) << 2)
+                    kc[:, d] = c
+        off += 64 * b
+    ka = off
+    va_bytes = {2: 512, 3: 768}.get(vbits, 1024)
+    if vbits == 4:
+        vc = _nibbles_v(blocks, rows[:, None], ka, t)
+    else:
+        _, vc = _int2_codes(blocks, t, 0, ka)
+        if vbits == 3:
+            G, r = t // 4, t % 4
+            for d in range(128):
+                n, f, cc = d % 16, (d // 16) % 4, d // 64
+                bit = ((2, 6, 3, 7) if cc == 0 else (0, 4, 1, 5))[f]
+                o = ka + 512 + 4 * (G * 16 + n) + r
+                vc[:, d] |= ((blocks[rows, o] >> bit) & 1) << 2
+    return dict(k=kc, v=vc, **_params(blocks, t, ka + va_bytes, ka + va_bytes + 64))

@@ -125,6 +125,35 @@
  *   kv_quant_append, kv_decode_attn and kv_append_decode_attn serve all three
  *   widths; kv_prefill_attn returns KVQ_ERR_UNSUPPORTED for code_bits = 2 or 3.
  *
+ * Keys with a bit width per RoPE-block group (key_bits; RoPE-Aware Bit
+ * Allocation for KV-Cache Quantization, Abstract: integer bit widths per RoPE
+ * frequency block, served from a packed cache; the allocation is the caller's).
+ *   Groups: rotated key dim d belongs to group (d mod 32) / 8, so group j holds
+ *   the rotate-half RoPE blocks (f, f + 64) with f in 8 j .. 8 j + 7 and
+ *   32 + 8 j .. 32 + 8 j + 7; key_bits[j] in {2, 3, 4}.  Unless all four widths
+ *   are equal, had_block must be at most 8 so that each Hadamard block stays
+ *   inside one group.
+ *   Quantization of the main-cache keys: the per-token U = fp16(fp32(mx - mn) /
+ *   15) and Z = fp16(mn) of the 4-bit cache; a dim of width b has m = 2^(4 - b),
+ *   o = (m - 1) / 2, Z_b = fp32(Z + o U), code = 0 if U == 0, else
+ *   clamp(rint(fp32(fp32(y - Z_b) / (m U))), 0, 2^b - 1); dequantized
+ *   y = Z + U (o + m code).  Widths (4, 4, 4, 4) give the 4-bit codes exactly.
+ *   Values keep code_bits; the INT8 side cache does not change.
+ *   Subblock of 16 tokens (KA = 64 (key_bits[0] + .. + key_bits[3]); VA = 1024,
+ *   768 or 512 for 4-, 3- or 2-bit values; subblock bytes KA + VA + 128):
+ *     [0, KA) key codes, group j at O_j = 64 (key_bits[0] + .. + key_bits[j-1]);
+ *       slot s = 16 G + t (G = 0..3, token t) holds dims 32 G + 8 j + e, e = 0..7:
+ *       width 4: bytes O_j + 4 s + k hold dims 2k (low nibble), 2k + 1 (high);
+ *       width 2: bytes O_j + 2 s + k hold dims 4k + f at bits 2f .. 2f + 1;
+ *       width 3: the low two bits as width 2, then byte O_j + 128 + s holds
+ *                bit 2 of dim e's code at bit e;
+ *     [KA, KA + VA) value codes in the code_bits value layout above (3 bits:
+ *       the 2-bit value layout of the low bits, then the value high plane);
+ *     [KA + VA, + 64) key (U, Z) fp16 pairs, [KA + VA + 64, + 64) value
+ *       (scale, zero) fp16 pairs, 4 bytes per token.
+ *   kv_quant_append and kv_decode_attn serve grouped keys for query groups up
+ *   to 8; kv_append_decode_attn and kv_prefill_attn return KVQ_ERR_UNSUPPORTED.
+ *
  * Block table: int32 [num_slots][bt_stride], row = slot; entry i is the page
  * holding positions [i P, (i + 1) P) of that slot's sequence.  Only entries
  * i < ceil(L / P) are read.
@@ -166,6 +195,9 @@ typedef struct {
     int32_t code_bits;       /* width of the main (paged) cache's codes: 4, or 3
                                 or 2 for the sub-4-bit caches (0 means 4).  The
                                 INT8 side cache is the same for all.              */
+    int32_t key_bits[4];     /* all 0: keys take code_bits.  Otherwise the width
+                                of each RoPE-block group of the main-cache keys,
+                                each in {2, 3, 4} (values keep code_bits)         */
 } kvq_cache;
 
 /* Bytes of the INT4 pool / INT8 side cache for this descriptor (0 on bad input). */

@@ -9,17 +9,18 @@ import torch
 from oracle.attention import attend, unquantized_attention
 from oracle.cache import quantize_sequence, rotated_keys_f32
 from oracle.numerics import bf16_to_f32
-from oracle.quant import tie_flags
+from oracle.quant import grouped_tie_flags, tie_flags
 from oracle.regions import ring_entry
 from workloads import WorkloadConfig, bf16_bits, build_workload
 
 ATOL = 2e-3
 
 
-def small_config(lengths, *, Hq=8, Hkv=2, P=16, h=64, s=4, w=32, seed=77, name="small", bits=4):
+def small_config(lengths, *, Hq=8, Hkv=2, P=16, h=64, s=4, w=32, seed=77, name="small", bits=4, key_bits=()):
     return WorkloadConfig(name=name, batch=len(lengths), num_q_heads=Hq, num_kv_heads=Hkv,
                           head_dim=128, lengths="explicit", length_args=tuple(int(x) for x in lengths),
-                          page_size=P, had_block=h, sink=s, recent=w, seed=seed, code_bits=bits)
+                          page_size=P, had_block=h, sink=s, recent=w, seed=seed, code_bits=bits,
+                          key_bits=tuple(key_bits))
 
 
 def check_workload_invariants(wl):
@@ -73,15 +74,19 @@ def compare_cache(dw, b, positions=None):
     mismatched or not, so a test of crafted ties can show it reached them.
     """
     from decode_attention_int4_block_amd.layout import (decode_sub2, decode_sub3, decode_sub4, decode_sub8,
-                                                        sub4_index, sub8_index)
+                                                        decode_subg, sub4_index, sub8_index)
     wl = dw.wl
     cfg = wl.cfg
     L = int(wl.lengths[b])
     k, v = dw.host_kv[b]
     kb, vb = bf16_bits(k), bf16_bits(v)
-    oc = quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent, main_bits=cfg.code_bits)
+    key_bits = tuple(cfg.key_bits) or None
+    oc = quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent, main_bits=cfg.code_bits, key_bits=key_bits)
     qmain = (1 << cfg.code_bits) - 1
     decode_main = {2: decode_sub2, 3: decode_sub3}.get(cfg.code_bits, decode_sub4)
+    if key_bits:
+        def decode_main(blocks, tok):
+            return decode_subg(blocks, tok, key_bits, cfg.code_bits)
     H = cfg.num_kv_heads
     P = wl.page_size
     slot = int(wl.slots[b])
@@ -92,7 +97,7 @@ def compare_cache(dw, b, positions=None):
     yv = bf16_to_f32(vb)
 
     def judge(tag, got, y, codes, qmax):
-        el, vec = tie_flags(y, qmax)
+        el, vec = grouped_tie_flags(y, key_bits) if (tag == "k" and qmax != 255 and key_bits) else tie_flags(y, qmax)
         tie = el | vec[..., None]
         mism = got[tag] != codes
         stats["codes"] += int(mism.size)
@@ -168,7 +173,7 @@ def compare_attention(dw, rows, report_unquantized=False):
         k, v = dw.host_kv[b]
         kb, vb = bf16_bits(k), bf16_bits(v)
         ref, ref_lse = attend(qb[b], quantize_sequence(kb, vb, cfg.had_block, cfg.sink, cfg.recent,
-                                                       main_bits=cfg.code_bits))
+                                                       main_bits=cfg.code_bits, key_bits=tuple(cfg.key_bits) or None))
         assert np.isfinite(out[b]).all() and np.isfinite(lse[b]).all(), f"non-finite output in row {b}"
         worst = max(worst, float(np.abs(out[b] - ref).max()))
         worst_lse = max(worst_lse, float(np.abs(lse[b] - ref_lse).max()))
@@ -176,3 +181,25 @@ def compare_attention(dw, rows, report_unquantized=False):
             u, _ = unquantized_attention(qb[b], kb, vb)
             worst_unq = max(worst_unq, float(np.abs(out[b] - u).max()))
     return worst, worst_lse, worst_unq
+
+
+def attention_error_scaled(dw, rows):
+    """Worst |GPU - oracle| / max(1, v_max / 256) over the rows (outputs and lse),
+    for crafted rows whose values reach 6e4: fp32 sums of values that large carry
+    absolute errors above 2e-3, so the bound is relative to their magnitude."""
+    from oracle.cache import dequantized_kv
+    cfg = dw.cfg
+    out = dw.out.cpu().numpy()
+    lse = dw.lse.cpu().numpy()
+    qb = bf16_bits(dw.q)
+    worst = 0.0
+    for b in rows:
+        k, v = dw.host_kv[b]
+        oc = quantize_sequence(bf16_bits(k), bf16_bits(v), cfg.had_block, cfg.sink, cfg.recent,
+                               main_bits=cfg.code_bits, key_bits=tuple(cfg.key_bits) or None)
+        ref, ref_lse = attend(qb[b], oc)
+        assert np.isfinite(out[b]).all() and np.isfinite(lse[b]).all(), f"non-finite output in row {b}"
+        _, V = dequantized_kv(oc)
+        scale = max(1.0, float(np.abs(V).max()) / 256.0)
+        worst = max(worst, float(np.abs(out[b] - ref).max()) / scale, float(np.abs(lse[b] - ref_lse).max()))
+    return worst

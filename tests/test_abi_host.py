@@ -153,6 +153,32 @@ def test_sub4bit_cache_sizes_and_limits(lib):
         assert lib.kv_prefill_attn(ctypes.byref(d2), p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 3
 
 
+def test_grouped_key_cache_sizes_and_limits(lib):
+    """Keys with a width per RoPE-block group: subblock bytes 64 sum(key_bits) +
+    the value area + 128 (include/kvq.h), widths in {2, 3, 4}, rotation blocks
+    inside a group, and the entry points that do not serve such caches."""
+    import ctypes as C
+    kb = lambda *w: (C.c_int32 * 4)(*w)
+    d = _desc(code_bits=3, key_bits=kb(4, 3, 3, 2), had_block=8)
+    assert lib.kvq_int4_pool_bytes(C.byref(d)) == 100 * 8 * (64 * 12 + 768 + 128)
+    # 104 bytes per (token, KV head), the cost of a uniform 3-bit cache
+    assert (64 * 12 + 768 + 128) // 16 == 104
+    assert lib.kvq_int4_pool_bytes(C.byref(_desc(code_bits=4, key_bits=kb(4, 4, 4, 4)))) == 100 * 8 * 2176
+    assert lib.kvq_int4_pool_bytes(C.byref(_desc(code_bits=2, key_bits=kb(2, 2, 2, 2)))) == 100 * 8 * (512 + 512 + 128)
+    for bad in ((1, 4, 4, 4), (4, 5, 4, 4), (4, 4, 4, 0)):
+        assert lib.kvq_int4_pool_bytes(C.byref(_desc(key_bits=kb(*bad), had_block=8))) == 0
+    # different widths need had_block <= 8; equal widths take any
+    assert lib.kvq_int4_pool_bytes(C.byref(_desc(key_bits=kb(4, 3, 3, 2), had_block=16))) == 0
+    assert lib.kvq_int4_pool_bytes(C.byref(_desc(key_bits=kb(3, 3, 3, 3), had_block=128))) > 0
+    p = C.c_void_p(0x3000)
+    dg = _desc(int4_pool=0x1000, int8_pool=0x2000, code_bits=3, key_bits=kb(4, 3, 3, 2), had_block=8)
+    assert lib.kv_prefill_attn(C.byref(dg), p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 3
+    assert lib.kv_append_decode_attn(C.byref(dg), p, p, p, 32, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
+    assert lib.kv_decode_read_ceiling(C.byref(dg), p, 32, p, p, 4, p, 2, p, 1 << 30, None) == 3
+    # query groups above 8 are not served
+    assert lib.kv_decode_attn(C.byref(dg), p, 128, p, p, 4, p, 2, p, None, p, 1 << 30, None) == 3
+
+
 def test_status_strings(lib):
     for s in range(6):
         assert lib.kvq_status_string(s)

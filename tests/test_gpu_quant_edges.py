@@ -22,9 +22,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import ATOL, add_stats, assert_cache_exact, compare_cache, make_device_workload, small_config
-from oracle.attention import attend
-from oracle.cache import dequantized_kv, quantize_sequence
+from gpu_common import (ATOL, add_stats, assert_cache_exact, attention_error_scaled, compare_cache,
+                        make_device_workload, small_config)
+from oracle.cache import quantize_sequence
 from workloads import bf16_bits
 from workloads.edge import edge_kv
 
@@ -43,26 +43,6 @@ def _report(name, **kw):
 
 # sinks only, inside the window, and rows with an INT4 region
 LENGTHS = [1, 2, 5, 33, 37, 70, 200, 301]
-
-
-def _attention_error(dw, rows):
-    """Worst |GPU - oracle| / max(1, v_max / 256) over the rows, and whether every
-    output is finite."""
-    cfg = dw.cfg
-    out = dw.out.cpu().numpy()
-    lse = dw.lse.cpu().numpy()
-    qb = bf16_bits(dw.q)
-    worst = 0.0
-    for b in rows:
-        k, v = dw.host_kv[b]
-        oc = quantize_sequence(bf16_bits(k), bf16_bits(v), cfg.had_block, cfg.sink, cfg.recent,
-                               main_bits=cfg.code_bits)
-        ref, ref_lse = attend(qb[b], oc)
-        assert np.isfinite(out[b]).all() and np.isfinite(lse[b]).all(), f"non-finite output in row {b}"
-        _, V = dequantized_kv(oc)
-        scale = max(1.0, float(np.abs(V).max()) / 256.0)
-        worst = max(worst, float(np.abs(out[b] - ref).max()) / scale, float(np.abs(lse[b] - ref_lse).max()))
-    return worst
 
 
 @pytest.mark.parametrize("bits", [4, 3, 2])
@@ -103,6 +83,6 @@ def test_crafted_rows_append_and_attend(h, bits):
         guarded += int(((oc.k4_scale & 0x7FFF) == 0).sum() + ((oc.v4_scale & 0x7FFF) == 0).sum())
     assert guarded > 0, "no vector took the zero-range guard"
     for name, dw in (("two-launch", sep), ("fused", fus)):
-        err = _attention_error(dw, rows)
+        err = attention_error_scaled(dw, rows)
         _report(f"h={h} bits={bits} {name} attention", scaled_max_abs=f"{err:.2e}", guarded_vectors=guarded)
         assert err <= ATOL

@@ -31,6 +31,7 @@ class WorkloadConfig:
     outlier_scale: float = 20.0
     rope_base: float = 1.0e6
     code_bits: int = 4      # width of the main cache's codes (4, or 3 or 2 for the sub-4-bit caches)
+    key_bits: tuple = ()    # key width per RoPE-block group (four of 2-4; values keep code_bits), or ()
     extra: dict = field(default_factory=dict)
 
     @property
