@@ -30,12 +30,14 @@ kvq_status ok() {
 
 constexpr int kMinUnitsPerWorker = 8;
 // Work split over the resident waves (two per SIMD), weighted by their measured
-// speed on MI355X (per-wave timestamps over the Qwen3-8B batch, four boxes):
-// the SIMD's issue arbitration favours the wave dispatched first -- workgroups
-// [0, W/2) -- by ~30%, and workgroups are dispatched round-robin over the 8
-// XCDs, of which the odd-numbered ones (odd w) stream ~6% slower.  Weights:
-// {first half, even w}, {first, odd}, {second, even}, {second, odd}.
-constexpr int32_t kPartWeights[4] = {139, 131, 103, 97};
+// speed on MI355X (per-wave timestamps over the Qwen3-8B batch): the SIMD's
+// issue arbitration favours the older of its two waves -- that of the
+// workgroup dispatched first to the CU, workers [0, W/2) -- by ~35% per step,
+// the second workgroup starts its first step ~3 us later, and workgroups are
+// dispatched round-robin over the 8 XCDs, of which the odd-numbered ones (odd
+// workgroup index) stream ~3% slower.  Weights (units per worker, relative):
+// {first half, even workgroup}, {first, odd}, {second, even}, {second, odd}.
+constexpr int32_t kPartWeights[4] = {139, 135, 99, 96};
 // A segment's start (query build) and end (reduction, piece or output stores)
 // take about as long as two steps of one wave (regression of the per-wave
 // durations on units and segments, Qwen3-8B batch), so the split counts each

@@ -133,17 +133,33 @@ __host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_
     return w < max_workers ? w : max_workers;
 }
 
+// Workers (one wave each) per workgroup of the split kernel.  A workgroup's
+// waves are placed on different SIMDs of one CU, so with two workgroups per CU
+// every SIMD runs one wave of each, and the wave of the workgroup dispatched
+// first is the older one on every SIMD.  (With one-wave workgroups the SIMD of
+// each wave varies from launch to launch, and some SIMDs receive two waves of
+// the first-dispatched set, which then share its issue slots.)
+constexpr int kSplitWaves = 4;
+
 // Weighted split of the units over W workers: worker w takes a share in
-// proportion to wt[2 r + (w & 1)], where r = (w >= W / 2), so that waves of
-// different measured speed (dispatch order, XCD) finish together.  With fewer
-// units than W full workers need, an even split over the workers needed.
+// proportion to wt[2 r + o], where r = (w >= W / 2) and o = the parity of its
+// workgroup w / kSplitWaves, so that waves of different measured speed
+// (dispatch order, XCD) finish together.  With fewer units than W full
+// workers need, an even split over the workers needed.
 struct Partition {
     int64_t total, W, half;
     int64_t wt[4];
     int64_t csum;           // cumulative weight of all W workers
 };
 
-__host__ __device__ inline int64_t count_even(int64_t a, int64_t b) { return (b + 1) / 2 - (a + 1) / 2; }
+// Workers of [0, n) in even-numbered workgroups.
+__host__ __device__ inline int64_t even_wg_workers(int64_t n) {
+    constexpr int64_t S = kSplitWaves;
+    const int64_t rem = n % (2 * S);
+    return n / (2 * S) * S + (rem < S ? rem : S);
+}
+
+__host__ __device__ inline int64_t count_even(int64_t a, int64_t b) { return even_wg_workers(b) - even_wg_workers(a); }
 
 // Cumulative weight of the workers [0, w).
 __host__ __device__ inline int64_t part_cum(const Partition &p, int64_t w) {

@@ -1197,13 +1197,26 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
 // device, as a measured ceiling for the full kernel.
 // KG = true: the main cache holds keys with a width per RoPE-block group
 // (a.key_bits) and values of width BITS.
+//
+// Two waves per SIMD (at most 256 registers each), except the 16-head group
+// kernels with the fused append or a 2- / 3-bit cache: those need more than
+// 256, and at one wave per SIMD the compiler keeps the rest in the
+// accumulation registers instead of spilling to scratch memory.
+template <int GP, bool APPEND, int BITS>
+constexpr int kSplitMinWaves = (GP == 16 && (APPEND || BITS != 4)) ? 1 : 2;
+
 template <int GP, bool APPEND, int BITS, bool MEM = false, bool KG = false>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kSplitWaves)
+__attribute__((amdgpu_waves_per_eu(kSplitMinWaves<GP, APPEND, BITS>, 2)))
 void decode_split_kernel(DecodeArgs a) {
     using SL = SmemLayout<GP, APPEND>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SL::kRequest];
-    const int lane = threadIdx.x;
-    const int64_t wid = blockIdx.x;
+    // kSplitWaves independent workers per workgroup (no barriers), each with
+    // its own slice of the workgroup's LDS
+    __shared__ __attribute__((aligned(16))) uint8_t smem_wg[kSplitWaves * SL::kRequest];
+    const int lane = threadIdx.x & 63;
+    const int wave = uni((int)(threadIdx.x >> 6));
+    const int64_t wid = (int64_t)blockIdx.x * kSplitWaves + wave;
+    uint8_t *const smem = smem_wg + wave * SL::kRequest;
 
     // Exclusive prefix of the row costs (units of all KV heads of a row).  The
     // rows of the register table take one load round trip and four
@@ -1792,41 +1805,41 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream, bool
         // grouped keys: attention only, query groups up to 8 (checked by the caller)
         const bool g4 = group_class(a.g) == 4;
         if (a.bits == 2) {
-            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, false, true>), dim3(grid), dim3(64), 0, stream, a);
-            else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, false, true>), dim3(grid), dim3(64), 0, stream, a);
+            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+            else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
         } else if (a.bits == 3) {
-            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, false, true>), dim3(grid), dim3(64), 0, stream, a);
-            else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, false, true>), dim3(grid), dim3(64), 0, stream, a);
+            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+            else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
         } else {
-            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, false, true>), dim3(grid), dim3(64), 0, stream, a);
-            else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, false, true>), dim3(grid), dim3(64), 0, stream, a);
+            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+            else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
         }
     } else if (a.bits == 2) {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid), dim3(64), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 2>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
         }
     } else if (a.bits == 3) {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 3>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 3>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 3>), dim3(grid), dim3(64), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 3>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
         }
     } else {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 4>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 4>), dim3(grid), dim3(64), 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 4>), dim3(grid), dim3(64), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 4>), dim3(grid), dim3(64), 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
         }
     }
     hipError_t e = hipGetLastError();
@@ -1840,14 +1853,14 @@ hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t
     const int cls = group_class(a.g);
     if (cls == 16) return hipErrorNotSupported;
     if (a.bits == 2) {
-        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, true>), dim3(grid), dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, true>), dim3(grid), dim3(64), 0, stream, a);
+        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+        else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
     } else if (a.bits == 3) {
-        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, true>), dim3(grid), dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, true>), dim3(grid), dim3(64), 0, stream, a);
+        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+        else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
     } else {
-        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, true>), dim3(grid), dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, true>), dim3(grid), dim3(64), 0, stream, a);
+        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+        else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -1878,7 +1891,7 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool groupe
         fn = cls == 4 ? split_fn<4, true, 4>() : (cls == 8 ? split_fn<8, true, 4>() : split_fn<16, true, 4>());
     else
         fn = cls == 4 ? split_fn<4, false, 4>() : (cls == 8 ? split_fn<8, false, 4>() : split_fn<16, false, 4>());
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kSplitWaves, 0);
     if (e != hipSuccess) return e;
     // The split kernel relies on every worker being resident at once (a worker
     // that starts late finishes late).  Measured on MI355X, a workgroup's LDS
@@ -1894,7 +1907,7 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool groupe
         if (by_lds < per_cu) per_cu = by_lds;
     }
     if (per_cu < 1) per_cu = 1;
-    *out = cus * per_cu;
+    *out = cus * per_cu * kSplitWaves;      // workers (waves)
     return hipSuccess;
 }
 
