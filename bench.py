@@ -264,6 +264,11 @@ def measure_variants(torch, cfg, steps, warmup, only=None):
                 c2.int4_pool.copy_(dw.cache.int4_pool)
                 c2.int8_pool.copy_(dw.cache.int8_pool)
                 copies.append(c2)
+        def two_launch(i):
+            dw.cache = copies[i % len(copies)]
+            dw.append_step()
+            dw.decode_step()
+        prewarm(torch, two_launch)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for i in range(warmup + steps):
             dw.cache = copies[i % len(copies)]
@@ -348,9 +353,34 @@ def _copies_for(nbytes):
     return int(min(16, max(4, -(-(640 << 20) // max(nbytes, 1)))))
 
 
+# GPU time of back-to-back launches run before each timed measurement.  Measured
+# on MI355X (shader clock from s_memtime against the 100 MHz real-time counter):
+# after an idle spell the clock sits near 2.16 GHz, the first milliseconds of
+# sustained launches run up to 30% slower than the settled rate, and the clock
+# settles near 2.38 GHz after 20-30 ms.  A few warm-up steps therefore time the
+# ramp, not the rate of a sustained decode loop.
+PREWARM_MS = 60.0
+
+
+def prewarm(torch, fn, ms=PREWARM_MS):
+    """Runs fn(i) back to back for about `ms` of GPU time (count from one timed
+    launch) and waits for it; returns the number of launches."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn(0)
+    e1.record()
+    torch.cuda.synchronize()
+    n = int(min(20000, max(1, np.ceil(ms / max(e0.elapsed_time(e1), 1e-3)))))
+    for i in range(1, n + 1):
+        fn(i)
+    torch.cuda.synchronize()
+    return n + 1
+
+
 def time_launches(torch, stream, fn, layers, n, warmup=2):
     """Median and p10 / p90 of n launches of fn(cache) timed one by one with HIP
-    events on the launch stream, cycling the cache copies."""
+    events on the launch stream, cycling the cache copies, after the pre-warm."""
+    prewarm(torch, lambda i: fn(layers[i % len(layers)]))
     for i in range(warmup):
         fn(layers[i % len(layers)])
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -491,6 +521,7 @@ def measure_prefill(torch, steps, warmup, cpu=False):
     def launch():
         kv_prefill_attn(dw.cache, q, q_start, dw.slots, dw.block_table, dw.ctx_len, int(T.max()), out=out, lse=lse)
 
+    prewarm(torch, lambda i: launch())
     for _ in range(warmup):
         launch()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -599,6 +630,7 @@ def main():
             dw.decode_step()
 
     copy_gbps = device_copy_rate(torch, calibration=args.calibration_copy)
+    prewarm_launches = prewarm(torch, lambda i: step(i))
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -666,6 +698,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": {"gpu_ms": PREWARM_MS, "launches": prewarm_launches,
+                    "why": "untimed back-to-back steps before the warm-up, so that the timed steps run at the "
+                           "shader clock of a sustained decode loop (it settles 20-30 ms into sustained load)"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
