@@ -268,7 +268,8 @@ def measure_variants(torch, cfg, steps, warmup, only=None):
             dw.cache = copies[i % len(copies)]
             dw.append_step()
             dw.decode_step()
-        prewarm(torch, two_launch)
+        prewarm(torch, two_launch, sync=False)
+        torch.cuda._sleep(SPIN_CYCLES)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for i in range(warmup + steps):
             dw.cache = copies[i % len(copies)]
@@ -362,9 +363,16 @@ def _copies_for(nbytes):
 PREWARM_MS = 60.0
 
 
-def prewarm(torch, fn, ms=PREWARM_MS):
+# A queued spin kernel of this many shader cycles (~2 ms) ahead of per-launch
+# timings: the timed launches queue behind it, so that the events time the
+# kernels and not the host's launch rate (a 5-us append is launched slower than
+# it runs).
+SPIN_CYCLES = 5_000_000
+
+
+def prewarm(torch, fn, ms=PREWARM_MS, sync=True):
     """Runs fn(i) back to back for about `ms` of GPU time (count from one timed
-    launch) and waits for it; returns the number of launches."""
+    launch), waits for it unless sync is False; returns the number of launches."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     fn(0)
@@ -373,16 +381,18 @@ def prewarm(torch, fn, ms=PREWARM_MS):
     n = int(min(20000, max(1, np.ceil(ms / max(e0.elapsed_time(e1), 1e-3)))))
     for i in range(1, n + 1):
         fn(i)
-    torch.cuda.synchronize()
+    if sync:
+        torch.cuda.synchronize()
     return n + 1
 
 
 def time_launches(torch, stream, fn, layers, n, warmup=2):
     """Median and p10 / p90 of n launches of fn(cache) timed one by one with HIP
     events on the launch stream, cycling the cache copies, after the pre-warm."""
-    prewarm(torch, lambda i: fn(layers[i % len(layers)]))
+    prewarm(torch, lambda i: fn(layers[i % len(layers)]), sync=False)
     for i in range(warmup):
         fn(layers[i % len(layers)])
+    torch.cuda._sleep(SPIN_CYCLES)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i, (e0, e1) in enumerate(evs):
         e0.record(stream)
@@ -499,14 +509,17 @@ def prefill_cpu_baseline(wl, q, T, budget_s=6.0):
                        f"took another {t_quant:.1f} s)")
 
 
-def measure_prefill(torch, steps, warmup, cpu=False):
+def measure_prefill(torch, steps, warmup, cpu=False, code_bits=4):
     """kv_prefill_attn on the re-prefill workload: the last `chunk` positions of each
-    sequence attended again as causal query rows over the quantized cache."""
+    sequence attended again as causal query rows over the quantized cache (main
+    cache of code_bits 4, 3 or 2)."""
     from decode_attention_int4_block_amd import kv_prefill_attn
     from decode_attention_int4_block_amd.harness import DeviceWorkload
     from workloads import build_workload, chunk_queries, get_config
 
     cfg = get_config(PREFILL_WORKLOAD)
+    if code_bits != 4:
+        cfg = cfg.scaled(code_bits=code_bits)
     wl = build_workload(cfg)
     dw = DeviceWorkload(wl, device="cuda", gen_device="cuda")
     dw.prefill(include_step_token=True)
@@ -536,11 +549,12 @@ def measure_prefill(torch, steps, warmup, cpu=False):
     flops = attended * cfg.num_q_heads * 4 * cfg.head_dim
     # unique cache bytes the chunks' causal prefixes cover (every position up to L)
     n4, n8 = region_sizes(L, cfg.sink, cfg.recent)
-    kv_unique = int((cfg.num_kv_heads * (BYTES_INT4 * n4 + BYTES_INT8 * n8)).sum())
+    b_main = {4: BYTES_INT4, 3: BYTES_INT3, 2: BYTES_INT2}[code_bits]
+    kv_unique = int((cfg.num_kv_heads * (b_main * n4 + BYTES_INT8 * n8)).sum())
     mean_us = float(us.mean())
     achieved = flops / (mean_us * 1e-6) / 1e12
     rec = {
-        "workload": cfg.name, "sequences": cfg.batch, "chunk_rows": [int(x) for x in T],
+        "workload": cfg.name, "code_bits": code_bits, "sequences": cfg.batch, "chunk_rows": [int(x) for x in T],
         "lengths": [int(x) for x in L], "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
         "had_block": cfg.had_block, "sink": cfg.sink, "recent": cfg.recent, "page_size": wl.page_size,
         "launches": steps, "us_mean": round(mean_us, 2),
@@ -554,7 +568,8 @@ def measure_prefill(torch, steps, warmup, cpu=False):
     }
     if cpu:
         rec["cpu_baseline"] = prefill_cpu_baseline(wl, q.cpu(), T)
-    print(f"[bench] prefill {cfg.name}: {mean_us:.1f} us, {achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    print(f"[bench] prefill {cfg.name} ({code_bits}-bit): {mean_us:.1f} us, {achieved:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
     del dw, q, out, lse
     torch.cuda.empty_cache()
     return rec
@@ -649,7 +664,8 @@ def main():
     step_gpu_ms = ev_start.elapsed_time(ev_end) / args.steps
 
     # untimed breakdown passes: each launch of the two-launch path between
-    # events, and the fused launch between events
+    # events, and the fused launch between events, queued behind a spin kernel
+    torch.cuda._sleep(SPIN_CYCLES)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         dw.cache = layers[i % len(layers)]
@@ -768,6 +784,14 @@ def main():
     if not args.no_prefill:
         rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2,
                                          cpu=not args.no_cpu_baseline)
+        # the same re-prefill over the 3- and 2-bit main caches
+        rec["prefill"]["sub4bit"] = []
+        for bits in (3, 2):
+            px = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2, code_bits=bits)
+            rec["prefill"]["sub4bit"].append({k: px[k] for k in ("code_bits", "us_mean", "us_p10_p90",
+                                                                  "algorithmic_flops", "kv_bytes_unique")}
+                                             | {"achieved_TFLOPs": px["roofline"]["achieved"],
+                                                "frac_of_fp16_mfma_peak": px["roofline"]["frac"]})
     if args.variants:
         del layers
         dw.cache = None

@@ -48,6 +48,7 @@ constexpr int kMaxDevices = 64;
 // and kernel (attention only, fused append); then the grouped-key kernels
 // (attention only, g <= 4 or <= 8, value width)
 std::atomic<int> g_max_workers[kMaxDevices][24];
+std::atomic<int> g_cus[kMaxDevices];     // compute units per device
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -128,6 +129,20 @@ kvq_status max_workers(int g, bool fused, int bits, int *out, bool grouped = fal
         hipError_t e = kvq::decode_max_workers(g, fused, bits, &v, grouped);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         g_max_workers[dev][cls].store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return KVQ_OK;
+}
+
+kvq_status cu_count(int *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+            return fail(KVQ_ERR_HIP, "compute unit count query failed");
+        g_cus[dev].store(v, std::memory_order_relaxed);
     }
     *out = v;
     return KVQ_OK;
@@ -297,7 +312,13 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.sub_bytes = gl.sub_bytes;
     a.max_workers = workers;
     a.min_units = kMinUnitsPerWorker;
-    for (int i = 0; i < 4; ++i) a.part_wt[i] = kPartWeights[i];
+    // the weights describe two split workgroups per CU (an older and a younger
+    // wave on every SIMD); with one per CU every wave runs alone on its SIMD
+    int cus = 0;
+    st = cu_count(&cus);
+    if (st != KVQ_OK) return st;
+    const bool paired = (int64_t)workers >= 2LL * kvq::kSplitWaves * cus;
+    for (int i = 0; i < 4; ++i) a.part_wt[i] = paired ? kPartWeights[i] : 1;
     a.seg_wt = kSegWeight;
     a.ws_header = reinterpret_cast<int32_t *>(ws);
     a.ws_first = reinterpret_cast<int32_t *>(ws + l.first_off);
@@ -417,9 +438,8 @@ kvq_status kv_prefill_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_
     if (!c->int4_pool) return fail(KVQ_ERR_NULL, "int4_pool is NULL");
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
-    if (bits_of(c) != 4 || grouped_of(c))
-        return fail(KVQ_ERR_UNSUPPORTED, "prefill attention reads the 4-bit cache only (code_bits %d%s)", c->code_bits,
-                    grouped_of(c) ? ", grouped key widths" : "");
+    if (grouped_of(c))
+        return fail(KVQ_ERR_UNSUPPORTED, "prefill attention does not read grouped key widths");
     kvq::PrefillArgs a;
     a.q = q;
     a.Hq = num_q_heads;
@@ -440,6 +460,7 @@ kvq_status kv_prefill_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_
     a.s = c->sink;
     a.w = c->recent;
     a.nr8 = nr8_of(c);
+    a.bits = bits_of(c);
     a.inv_sqrt_h = inv_sqrt(c->had_block);
     a.out = out;
     a.lse = lse;

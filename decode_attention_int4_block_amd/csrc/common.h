@@ -270,6 +270,7 @@ struct PrefillArgs {
     const uint8_t *int4_pool;
     const uint8_t *int8_pool;
     int32_t H, P, logP, h, s, w, nr8;
+    int32_t bits;               // main cache code width: 4, 3 or 2
     float inv_sqrt_h;
     float *out;                 // [N][Hq][128]
     float *lse;                 // [N][Hq] or nullptr

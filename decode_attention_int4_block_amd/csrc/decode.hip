@@ -638,7 +638,6 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
 }
 
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // main2: a 2- or 3-bit main-cache step (8 bytes of low-plane codes per lane and
 // quarter; at 3 bits the lane's high-plane dword goes to word 2).
@@ -756,42 +755,6 @@ template <int GP>
 struct KAcc {
     floatx4 dA[GC<GP>::kQ], dB[GC<GP>::kQ];
 };
-
-// 2-bit codes of one dword half-pair as the four f16 subnormal pairs the INT4
-// nibble masks give: field f of bytes 0 and 2 (dims f and 4 + f of a chunk)
-// scaled 1 for even f and 16 for odd f, so that the same query operand (and the
-// same value tile scaling) serves both widths.
-__device__ inline uint32_t int2_field(uint32_t x, int f) {
-    switch (f) {
-        case 0: return x & 0x00030003u;
-        case 1: return (x << 2) & 0x00300030u;
-        case 2: return (x >> 4) & 0x00030003u;
-        default: return (x >> 2) & 0x00300030u;
-    }
-}
-__device__ inline half8 int2_chunk(uint32_t x) {
-    return pack8(int2_field(x, 0), int2_field(x, 1), int2_field(x, 2), int2_field(x, 3));
-}
-// 3-bit codes: a 2-bit field with its high bit ORed in at value 4 (bit 2 or 6
-// of each half, next to the field's two bits).  h holds the high bits of the
-// field's codes at bits 2 / 6 (+ 16) for the even / odd fields, or 8 above.
-__device__ inline uint32_t int3_field(uint32_t x, uint32_t h, int f) {
-    const uint32_t hs = f < 2 ? h : h >> 8;
-    return int2_field(x, f) | (hs & ((f & 1) ? 0x00400040u : 0x00040004u));
-}
-// key chunk i: the high-plane dword shifted to its bytes (key plane layout in quant.h)
-__device__ inline half8 int3_key_chunk(uint32_t x, uint32_t hh, int i) {
-    const uint32_t h = i == 0 ? hh : (i == 1 ? hh >> 1 : (i == 2 ? hh << 2 : hh << 1));
-    return pack8(int3_field(x, h, 0), int3_field(x, h, 1), int3_field(x, h, 2), int3_field(x, h, 3));
-}
-// value field f of low-plane dword cc, bytes (0, 2) (odd = false) or (1, 3): the
-// high byte's bit for (cc, f) moved to bit 2 / 6 (value plane layout in quant.h)
-__device__ inline uint32_t int3_value_field(uint32_t x, uint32_t hv, int cc, int f, bool odd) {
-    const int g = cc == 0 ? (0x7362 >> (4 * f)) & 15 : (0x5140 >> (4 * f)) & 15;
-    const int s = g + (odd ? 8 : 0) - ((f & 1) ? 6 : 2);
-    const uint32_t h = s >= 0 ? hv >> s : hv << (-s);
-    return int2_field(x, f) | (h & ((f & 1) ? 0x00400040u : 0x00040004u));
-}
 
 // Grouped keys: the MFMA operand of one group's slot word x, each code c as the
 // f16 subnormal (m c) 2^-24 (m = 2^(4 - b)) in the nibble order of the 4-bit

@@ -62,26 +62,54 @@ __device__ inline StepPages step_pages(const PrefillArgs &a, const RowPlan &rp, 
 
 // 5 direct-to-LDS loads of step r of the tile into stage st (the decode kernel's
 // step copy: key codes gathered by lane, value codes verbatim, params of both
-// halves at kStKP / kStVP + 4 t).
+// halves at kStKP / kStVP + 4 t).  BITS = 2 or 3: the main cache's low planes
+// of subblocks A / B to 0 / 512 (keys) and 1024 / 1536 (values), at 3 bits the
+// high planes to 2048 / 2304 (keys) and 2560 / 2816 (values), the params as
+// for 4 bits -- still five loads.
+template <int BITS>
 __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &rp, int n4, int slot, int hk, int r,
                                           StepPages pg, uint8_t *st, uint32_t offK, uint32_t offV, uint32_t offP4,
                                           uint32_t offP8, int lane) {
     if (r < n4) {
+        constexpr size_t kSubBytes = (size_t)main_sub_bytes(BITS);
         const int pos0 = (rp.k0 + r) * 32;
         const int subs = a.P >> 4;
         const uint8_t *baseA = a.int4_pool +
-            ((size_t)((int64_t)pg.A * a.H + hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSub4Bytes;
+            ((size_t)((int64_t)pg.A * a.H + hk) * subs + ((pos0 & (a.P - 1)) >> 4)) * kSubBytes;
         // subblock B past the INT4 region is never used; re-read A (valid memory)
         const uint8_t *baseB = baseA;
         if (pg.B >= 0) {
             baseB = a.int4_pool +
-                ((size_t)((int64_t)pg.B * a.H + hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSub4Bytes;
+                ((size_t)((int64_t)pg.B * a.H + hk) * subs + (((pos0 + 16) & (a.P - 1)) >> 4)) * kSubBytes;
         }
-        dma16(baseA + kSub4K, offK, st + 0);
-        dma16(baseB + kSub4K, offK, st + 1024);
-        dma16(baseA + kSub4V, offV, st + 2048);
-        dma16(baseB + kSub4V, offV, st + 3072);
-        if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP4, st + 4096);
+        if constexpr (BITS == 2) {
+            const uint32_t off = 16 * (uint32_t)lane;
+            if (lane < 32) {
+                dma16(baseA + kSub2K, off, st + 0);
+                dma16(baseB + kSub2K, off, st + 512);
+                dma16(baseA + kSub2V, off, st + 1024);
+                dma16(baseB + kSub2V, off, st + 1536);
+            }
+            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP4 - kSub4KP + kSub2KP, st + 4096);
+        } else if constexpr (BITS == 3) {
+            const uint8_t *lo = lane < 32 ? baseA : baseB;
+            const uint32_t off = 16 * (uint32_t)(lane & 31);
+            dma16(lo + kSub3K, off, st + 0);
+            dma16(lo + kSub3V, off, st + 1024);
+            if (lane < 32) {
+                const uint8_t *hi = lane < 16 ? baseA : baseB;
+                const uint32_t offh = 16 * (uint32_t)(lane & 15);
+                dma16(hi + kSub3KH, offh, st + 2048);
+                dma16(hi + kSub3VH, offh, st + 2560);
+            }
+            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP4 - kSub4KP + kSub3KP, st + 4096);
+        } else {
+            dma16(baseA + kSub4K, offK, st + 0);
+            dma16(baseB + kSub4K, offK, st + 1024);
+            dma16(baseA + kSub4V, offV, st + 2048);
+            dma16(baseB + kSub4V, offV, st + 3072);
+            if (lane < 16) dma16((lane & 4) ? baseB : baseA, offP4, st + 4096);
+        }
     } else {
         const uint8_t *base = a.int8_pool + ((size_t)((int64_t)slot * a.H + hk) * a.nr8 + (r - n4)) * kSub8Bytes;
         dma16(base + kSub8KLo, offK, st + 0);
@@ -94,6 +122,8 @@ __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &r
 
 }  // namespace
 
+// BITS: width of the main cache's codes (4, 3 or 2; KV4-RL, "Future Directions").
+template <int BITS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
@@ -203,7 +233,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int s = 0; s < kStages; ++s) {
         if (s < nsteps) {
-            issue_prefill_step(a, rp, n4, slot, hk, s, step_pages(a, rp, n4, slot, s), smem + s * kStageBytes, offK,
+            issue_prefill_step<BITS>(a, rp, n4, slot, hk, s, step_pages(a, rp, n4, slot, s), smem + s * kStageBytes, offK,
                                offV, offP4, offP8, lane);
             ++issued;
         }
@@ -219,17 +249,36 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < nsteps; ++i) {
         wait_vm_steps(issued - i - 1);
         uint8_t *st = smem + (i % kStages) * kStageBytes;
-        const u32x4 kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
-        const u32x4 kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
-        const u32x4 vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
-        const u32x4 vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
+        // a 2- or 3-bit main-cache step: 8 bytes of low-plane codes per lane and
+        // subblock in words 0-1, the lane's high-plane dword in word 2
+        const bool main2 = BITS != 4 && i < n4;
+        u32x4 kA, kB, vA, vB;
+        if (main2) {
+            const u32x2 ka = *reinterpret_cast<const u32x2 *>(st + lane * 8);
+            const u32x2 kb = *reinterpret_cast<const u32x2 *>(st + 512 + lane * 8);
+            const u32x2 va = *reinterpret_cast<const u32x2 *>(st + 1024 + lane * 8);
+            const u32x2 vb = *reinterpret_cast<const u32x2 *>(st + 1536 + lane * 8);
+            const uint32_t kha = BITS == 3 ? lds32(st + 2048 + 4 * lane) : 0u;
+            const uint32_t khb = BITS == 3 ? lds32(st + 2304 + 4 * lane) : 0u;
+            const uint32_t vha = BITS == 3 ? lds32(st + 2560 + 4 * lane) : 0u;
+            const uint32_t vhb = BITS == 3 ? lds32(st + 2816 + 4 * lane) : 0u;
+            kA = u32x4{ka[0], ka[1], kha, 0u};
+            kB = u32x4{kb[0], kb[1], khb, 0u};
+            vA = u32x4{va[0], va[1], vha, 0u};
+            vB = u32x4{vb[0], vb[1], vhb, 0u};
+        } else {
+            kA = *reinterpret_cast<const u32x4 *>(st + lane * 16);
+            kB = *reinterpret_cast<const u32x4 *>(st + 1024 + lane * 16);
+            vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
+            vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
+        }
         const u32x4 kpA = *reinterpret_cast<const u32x4 *>(st + kStKP + 16 * G);
         const u32x4 kpB = *reinterpret_cast<const u32x4 *>(st + kStKP + 64 + 16 * G);
         const u32x4 vpA = *reinterpret_cast<const u32x4 *>(st + kStVP + 16 * G);
         const u32x4 vpB = *reinterpret_cast<const u32x4 *>(st + kStVP + 64 + 16 * G);
         wait_lgkm0();
         if (i + kStages < nsteps) {
-            issue_prefill_step(a, rp, n4, slot, hk, i + kStages, next, st, offK, offV, offP4, offP8, lane);
+            issue_prefill_step<BITS>(a, rp, n4, slot, hk, i + kStages, next, st, offK, offV, offP4, offP8, lane);
             ++issued;
             next = step_pages(a, rp, n4, slot, i + kStages + 1);
         }
@@ -237,16 +286,30 @@ void prefill_kernel(PrefillArgs a) {
 
         // scores of tokens 4G + j (A half) and 16 + 4G + j (B half) for column n
         floatx4 hA = zero4, lA = zero4, hB = zero4, lB = zero4;
+        if (main2) {
+            // chunk c: dword c / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t x = kA[c], x8 = x >> 8;
-            const half8 ak = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
-            const uint32_t y = kB[c], y8 = y >> 8;
-            const half8 bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
-            hA = mfma16(ak, qh[c], hA);
-            lA = mfma16(ak, ql[c], lA);
-            hB = mfma16(bk, qh[c], hB);
-            lB = mfma16(bk, ql[c], lB);
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t xa = kA[c >> 1] >> (8 * (c & 1)), xb = kB[c >> 1] >> (8 * (c & 1));
+                const half8 ak = BITS == 3 ? int3_key_chunk(xa, kA[2], c) : int2_chunk(xa);
+                const half8 bk = BITS == 3 ? int3_key_chunk(xb, kB[2], c) : int2_chunk(xb);
+                hA = mfma16(ak, qh[c], hA);
+                lA = mfma16(ak, ql[c], lA);
+                hB = mfma16(bk, qh[c], hB);
+                lB = mfma16(bk, ql[c], lB);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t x = kA[c], x8 = x >> 8;
+                const half8 ak = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
+                const uint32_t y = kB[c], y8 = y >> 8;
+                const half8 bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
+                hA = mfma16(ak, qh[c], hA);
+                lA = mfma16(ak, ql[c], lA);
+                hB = mfma16(bk, qh[c], hB);
+                lB = mfma16(bk, ql[c], lB);
+            }
         }
         float t[8];
         uint32_t vp[8];
@@ -331,15 +394,33 @@ void prefill_kernel(PrefillArgs a) {
         split2<256>(pv[4], pv[6], H2, L2);
         split2<256>(pv[5], pv[7], H3, L3);
         const half8 ph = pack8(H0, H1, H2, H3), pl = pack8(L0, L1, L2, L3);
+        if (main2) {
+            // dword cc, field f: dims 16 (4 cc + f) + n, tile 4 cc + f (odd tiles
+            // scaled by 16 as the 4-bit ones)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t x = vA[c], x8 = x >> 8, y = vB[c], y8 = y >> 8;
-            const half8 ve = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
-            const half8 vo = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
-            Oh[2 * c] = mfma16(ph, ve, Oh[2 * c]);
-            Ol[2 * c] = mfma16(pl, ve, Ol[2 * c]);
-            Oh[2 * c + 1] = mfma16(ph, vo, Oh[2 * c + 1]);
-            Ol[2 * c + 1] = mfma16(pl, vo, Ol[2 * c + 1]);
+            for (int cc = 0; cc < 2; ++cc) {
+                const uint32_t x = vA[cc], x8 = x >> 8, y = vB[cc], y8 = y >> 8;
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const half8 vt = BITS == 3
+                        ? pack8(int3_value_field(x, vA[2], cc, f, false), int3_value_field(x8, vA[2], cc, f, true),
+                                int3_value_field(y, vB[2], cc, f, false), int3_value_field(y8, vB[2], cc, f, true))
+                        : pack8(int2_field(x, f), int2_field(x8, f), int2_field(y, f), int2_field(y8, f));
+                    Oh[4 * cc + f] = mfma16(ph, vt, Oh[4 * cc + f]);
+                    Ol[4 * cc + f] = mfma16(pl, vt, Ol[4 * cc + f]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t x = vA[c], x8 = x >> 8, y = vB[c], y8 = y >> 8;
+                const half8 ve = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
+                const half8 vo = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
+                Oh[2 * c] = mfma16(ph, ve, Oh[2 * c]);
+                Ol[2 * c] = mfma16(pl, ve, Ol[2 * c]);
+                Oh[2 * c + 1] = mfma16(ph, vo, Oh[2 * c + 1]);
+                Ol[2 * c + 1] = mfma16(pl, vo, Ol[2 * c + 1]);
+            }
         }
     }
 
@@ -367,7 +448,13 @@ void prefill_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream) {
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)tiles, (unsigned)a.H, (unsigned)a.B), dim3(64), 0, stream, a);
+    const dim3 grid((unsigned)tiles, (unsigned)a.H, (unsigned)a.B);
+    if (a.bits == 2)
+        hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(64), 0, stream, a);
+    else if (a.bits == 3)
+        hipLaunchKernelGGL(prefill_kernel<3>, grid, dim3(64), 0, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -127,6 +128,46 @@ __device__ inline uint32_t lds32(const uint8_t *p) { return *reinterpret_cast<co
 // score (log2 units / K1) of one token from its raw code dot product d
 __device__ inline float tscore(float d, uint32_t kp, float Rh) {
     return fmaf(d, h_lo(kp), h_hi(kp) * Rh);
+}
+
+// ---- 2- and 3-bit main-cache codes as MFMA operands (decode and prefill) ----
+// The step copies of both kernels put a 2- or 3-bit step in LDS the same way:
+// lane (G, n) reads 8 bytes of low-plane key codes (token n, dims 32 G ..) and
+// 8 of value codes, plus a high-plane dword each at 3 bits.
+// 2-bit codes of one dword half-pair as the four f16 subnormal pairs the INT4
+// nibble masks give: field f of bytes 0 and 2 (dims f and 4 + f of a chunk)
+// scaled 1 for even f and 16 for odd f, so that the same query operand (and the
+// same value tile scaling) serves both widths.
+__device__ inline uint32_t int2_field(uint32_t x, int f) {
+    switch (f) {
+        case 0: return x & 0x00030003u;
+        case 1: return (x << 2) & 0x00300030u;
+        case 2: return (x >> 4) & 0x00030003u;
+        default: return (x >> 2) & 0x00300030u;
+    }
+}
+__device__ inline half8 int2_chunk(uint32_t x) {
+    return pack8(int2_field(x, 0), int2_field(x, 1), int2_field(x, 2), int2_field(x, 3));
+}
+// 3-bit codes: a 2-bit field with its high bit ORed in at value 4 (bit 2 or 6
+// of each half, next to the field's two bits).  h holds the high bits of the
+// field's codes at bits 2 / 6 (+ 16) for the even / odd fields, or 8 above.
+__device__ inline uint32_t int3_field(uint32_t x, uint32_t h, int f) {
+    const uint32_t hs = f < 2 ? h : h >> 8;
+    return int2_field(x, f) | (hs & ((f & 1) ? 0x00400040u : 0x00040004u));
+}
+// key chunk i: the high-plane dword shifted to its bytes (key plane layout in quant.h)
+__device__ inline half8 int3_key_chunk(uint32_t x, uint32_t hh, int i) {
+    const uint32_t h = i == 0 ? hh : (i == 1 ? hh >> 1 : (i == 2 ? hh << 2 : hh << 1));
+    return pack8(int3_field(x, h, 0), int3_field(x, h, 1), int3_field(x, h, 2), int3_field(x, h, 3));
+}
+// value field f of low-plane dword cc, bytes (0, 2) (odd = false) or (1, 3): the
+// high byte's bit for (cc, f) moved to bit 2 / 6 (value plane layout in quant.h)
+__device__ inline uint32_t int3_value_field(uint32_t x, uint32_t hv, int cc, int f, bool odd) {
+    const int g = cc == 0 ? (0x7362 >> (4 * f)) & 15 : (0x5140 >> (4 * f)) & 15;
+    const int s = g + (odd ? 8 : 0) - ((f & 1) ? 6 : 2);
+    const uint32_t h = s >= 0 ? hv >> s : hv << (-s);
+    return int2_field(x, f) | (h & ((f & 1) ? 0x00400040u : 0x00040004u));
 }
 
 }  // namespace kvq

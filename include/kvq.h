@@ -122,8 +122,8 @@
  *     [1600, 1664) value (scale, zero) fp16 pairs, 4 bytes per token.
  *   1664 bytes / (16 tokens * 256 elements) = 3.25 bits per element.
  *
- *   kv_quant_append, kv_decode_attn and kv_append_decode_attn serve all three
- *   widths; kv_prefill_attn returns KVQ_ERR_UNSUPPORTED for code_bits = 2 or 3.
+ *   kv_quant_append, kv_decode_attn, kv_append_decode_attn and kv_prefill_attn
+ *   serve all three widths.
  *
  * Keys with a bit width per RoPE-block group (key_bits; RoPE-Aware Bit
  * Allocation for KV-Cache Quantization, Abstract: integer bit widths per RoPE
@@ -364,12 +364,14 @@ kvq_status kv_append_decode_attn(const kvq_cache *cache,
  *                at position p = ctx_len[b] - T_b + t and gets
  *                softmax(q.k / sqrt(128)) v over positions [0, p], each key and
  *                value as the cache holds it at length ctx_len[b] (the INT8
- *                copy for the sinks and the last `recent` positions, INT4
- *                elsewhere).  Its last row equals kv_decode_attn's output.
+ *                copy for the sinks and the last `recent` positions, the main
+ *                cache of code_bits 4, 3 or 2 elsewhere).  Its last row equals
+ *                kv_decode_attn's output.
  *   lse          fp32 [N][num_q_heads] (device) or NULL.
  *
  * No workspace.  Returns KVQ_OK without launching when B == 0 or max_rows == 0.
- * B and num_kv_heads must not exceed 65535.
+ * B and num_kv_heads must not exceed 65535.  A cache with grouped key widths
+ * (key_bits) returns KVQ_ERR_UNSUPPORTED.
  */
 kvq_status kv_prefill_attn(const kvq_cache *cache,
                            const uint16_t *q, int32_t num_q_heads,

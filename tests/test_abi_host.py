@@ -149,8 +149,10 @@ def test_sub4bit_cache_sizes_and_limits(lib):
     p = ctypes.c_void_p(0x3000)
     for bits in (2, 3):
         d2 = _desc(int4_pool=0x1000, int8_pool=0x2000, code_bits=bits)
-        # the prefill attention serves the 4-bit cache only
-        assert lib.kv_prefill_attn(ctypes.byref(d2), p, 32, p, 8, p, p, 4, p, 2, p, None, None) == 3
+        # the prefill attention serves these widths: its argument checks apply as
+        # for 4 bits (a launch needs a GPU, so only the rejections are called here)
+        assert lib.kv_prefill_attn(ctypes.byref(d2), p, 32, p, 8, p, p, 0, p, 2, p, None, None) == 2
+        assert lib.kv_prefill_attn(ctypes.byref(d2), p, 256, p, 8, p, p, 4, p, 2, p, None, None) == 3
 
 
 def test_grouped_key_cache_sizes_and_limits(lib):

@@ -56,7 +56,8 @@ def _run(cfg, T, seed, check_decode=True):
         if Tb == 0:
             continue
         k, v = dw.host_kv[b]
-        cache = quantize_sequence(bf16_bits(k), bf16_bits(v), cfg.had_block, cfg.sink, cfg.recent)
+        cache = quantize_sequence(bf16_bits(k), bf16_bits(v), cfg.had_block, cfg.sink, cfg.recent,
+                                  main_bits=cfg.code_bits)
         ref, ref_lse = prefill_attend(qb[r0:r0 + Tb], cache)
         got = out[r0:r0 + Tb]
         assert np.isfinite(got).all(), f"non-finite output in sequence {b}"
@@ -143,4 +144,57 @@ def test_prefill_long_chunk_sampled_rows():
         ref, _ = softmax_attention(rotated_query(qb[t], 128), K[:p + 1], V[:p + 1])
         worst = max(worst, float(np.abs(out[t] - ref).max()))
     _report("4096 x 1024 chunk", rows=len(pick), max_abs=f"{worst:.2e}")
+    assert worst <= ATOL and np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("h", [1, 128])
+def test_prefill_sub4bit_edge_lengths_and_chunks(bits, h):
+    """The 3- and 2-bit main caches (KV4-RL, "Future Directions"): every row
+    against the oracle's prefill attention over its own 3- / 2-bit
+    quantization, the last row against kv_decode_attn."""
+    Ts = [1, 2, 3, 4, 5, 16, 17, 18, 33, 7, 64, 100, 300]
+    cfg = small_config(EDGE, h=h, s=4, w=32, seed=2600 + 10 * h + bits, bits=bits)
+    err, err_lse = _run(cfg, Ts, seed=100 + h + bits)
+    _report(f"{bits}-bit edge lengths h={h}", max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
+    assert err <= ATOL and err_lse <= ATOL
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("s,w,g,Hkv,P", [(0, 0, 4, 2, 16), (16, 128, 8, 2, 64), (4, 64, 16, 1, 16),
+                                         (4, 4000, 3, 2, 1024)])
+def test_prefill_sub4bit_budgets_groups_pages(bits, s, w, g, Hkv, P):
+    lengths = [0, 3, 17, 40, 129, 300, 700]
+    cfg = small_config(lengths, Hq=g * Hkv, Hkv=Hkv, P=P, h=64, s=s, w=w, seed=2700 + s + w + g + bits, bits=bits)
+    err, err_lse = _run(cfg, [0, 3, 9, 40, 70, 150, 64], seed=s + w + g)
+    _report(f"{bits}-bit s={s} w={w} g={g} P={P}", max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
+    assert err <= ATOL and err_lse <= ATOL
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_prefill_sub4bit_long_chunk_sampled_rows(bits):
+    """A 4096-token sequence, 1024-row chunk, Qwen3-8B heads, 3- / 2-bit main
+    cache; rows sampled for the oracle."""
+    from decode_attention_int4_block_amd import kv_prefill_attn
+    L, T = 4096, 1024
+    cfg = small_config([L], Hq=32, Hkv=8, h=128, s=4, w=128, seed=2800 + bits, bits=bits)
+    dw = make_device_workload(cfg, keep=[0], prefill=False)
+    dw.prefill(include_step_token=True)
+    q = _query_rows(np.array([T]), 32, 78 + bits)
+    q_start = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    out, _ = kv_prefill_attn(dw.cache, q.cuda(), q_start, dw.slots, dw.block_table, dw.ctx_len, max_rows=T)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    qb = bf16_bits(q)
+    k, v = dw.host_kv[0]
+    cache = quantize_sequence(bf16_bits(k), bf16_bits(v), 128, 4, 128, main_bits=bits)
+    K, V = dequantized_kv(cache)
+    rng = np.random.default_rng(6)
+    pick = sorted({0, T - 1, T - 128, T - 129} | set(int(x) for x in rng.integers(0, T, 12)))
+    worst = 0.0
+    for t in pick:
+        p = L - T + t
+        ref, _ = softmax_attention(rotated_query(qb[t], 128), K[:p + 1], V[:p + 1])
+        worst = max(worst, float(np.abs(out[t] - ref).max()))
+    _report(f"{bits}-bit 4096 x 1024 chunk", rows=len(pick), max_abs=f"{worst:.2e}")
     assert worst <= ATOL and np.isfinite(out).all()
