@@ -127,7 +127,12 @@ __host__ __device__ inline int64_t div_nonneg(int64_t n, int64_t d) {
     return n / d;
 }
 
+// Workers of a launch: min_units per worker, capped at max_workers.  A launch
+// with fewer units than 512 workers of min_units each (a few short rows) takes
+// half that per worker: its time is one worker's chain of steps, not the
+// combine of the extra pieces (measured: a 1024-token row, 20 -> 17 us).
 __host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_workers, int64_t min_units) {
+    if (total < 512 * min_units && min_units > 1) min_units = (min_units + 1) / 2;
     int64_t w = div_nonneg(total + min_units - 1, min_units);
     if (w < 1) w = 1;
     return w < max_workers ? w : max_workers;

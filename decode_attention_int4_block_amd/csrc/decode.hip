@@ -1705,16 +1705,24 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
                          [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); }, sh);
         return;
     }
-    // helper: the pieces of workers [w0, w0 + T)
+    // helper: the pieces of workers [w0, w0 + T).  The worker count and the
+    // workers' segment records load in one round trip (the records array holds
+    // the whole grid's; those of workers >= W are dropped afterwards), the
+    // records' segment bounds in a second.
     const int64_t jc = (int64_t)blockIdx.x - nseg;
-    const int64_t W = ldc(a.ws_header, 0);
     const int64_t w0 = jc * T;
+    const bool mine = lane < 2 * T && w0 + lane / 2 < a.max_workers;
+    int v = mine ? a.ws_wseg[2 * w0 + lane] : -1;
+    const int64_t W = ldc(a.ws_header, 0);
     if (w0 >= W) return;
-    int v = -1;
-    if (lane < 2 * T && w0 + lane / 2 < W) v = a.ws_wseg[2 * w0 + lane];
-    if (v >= nseg) v = -1;
-    // keep the long segments among them (one round trip for all lanes)
-    if (v >= 0 && a.ws_last[v] - a.ws_first[v] + 1 <= T) v = -1;
+    if (w0 + lane / 2 >= W || v >= nseg) v = -1;
+    // keep the long segments among them
+    int vf = 0, vl = 0;
+    if (v >= 0) {
+        vf = a.ws_first[v];
+        vl = a.ws_last[v];
+        if (vl - vf + 1 <= T) v = -1;
+    }
     int prev = -1;
     for (;;) {
         // the long segments of these workers' pieces, in increasing order (the
@@ -1722,7 +1730,9 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
         const int s = wave_min(v > prev ? v : 0x7fffffff);
         if (s == 0x7fffffff) break;
         prev = s;
-        const int64_t wf = ldc(a.ws_first, s), wl = ldc(a.ws_last, s);
+        // its bounds, from a lane that holds it
+        const int src = __ffsll((unsigned long long)__ballot(v == s)) - 1;
+        const int64_t wf = __builtin_amdgcn_readlane(vf, src), wl = __builtin_amdgcn_readlane(vl, src);
         const int n = (int)(wl - wf + 1);
         const int b = s / a.H, hk = s % a.H;
         const int64_t wa = w0 > wf ? w0 : wf;
