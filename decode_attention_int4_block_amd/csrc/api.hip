@@ -117,7 +117,7 @@ float inv_sqrt(int h) { return (float)(1.0 / sqrt((double)h)); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-kvq_status max_workers(int g, bool fused, int bits, int *out, bool grouped = false) {
+kvq_status max_workers(int g, bool fused, int bits, int *out, bool grouped = false, int *out_wg = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device index %d", dev);
@@ -126,11 +126,15 @@ kvq_status max_workers(int g, bool fused, int bits, int *out, bool grouped = fal
                             : (g <= 4 ? 0 : (g <= 8 ? 1 : 2)) + 6 * bi + (fused ? 3 : 0);
     int v = g_max_workers[dev][cls].load(std::memory_order_relaxed);
     if (v <= 0) {
-        hipError_t e = kvq::decode_max_workers(g, fused, bits, &v, grouped);
+        int wg = 1;
+        hipError_t e = kvq::decode_max_workers(g, fused, bits, &v, grouped, &wg);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        // workers and workers per workgroup in one word (workers < 2^24)
+        v = (v << 4) | wg;
         g_max_workers[dev][cls].store(v, std::memory_order_relaxed);
     }
-    *out = v;
+    *out = v >> 4;
+    if (out_wg) *out_wg = v & 15;
     return KVQ_OK;
 }
 
@@ -274,8 +278,8 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     if (c->sink + c->recent > 0 && !c->int8_pool) return fail(KVQ_ERR_NULL, "int8_pool is NULL");
     if (bt_stride < 1) return fail(KVQ_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
-    int workers = 0;
-    st = max_workers(g, fused, bits_of(c), &workers, grouped);
+    int workers = 0, wg = 1;
+    st = max_workers(g, fused, bits_of(c), &workers, grouped, &wg);
     if (st != KVQ_OK) return st;
     const WsLayout l = ws_layout(c, B, g, workers);
     if (workspace_bytes < l.total)
@@ -317,7 +321,7 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     int cus = 0;
     st = cu_count(&cus);
     if (st != KVQ_OK) return st;
-    const bool paired = (int64_t)workers >= 2LL * kvq::kSplitWaves * cus;
+    const bool paired = wg == kvq::kSplitWaves && (int64_t)workers >= 2LL * kvq::kSplitWaves * cus;
     for (int i = 0; i < 4; ++i) a.part_wt[i] = paired ? kPartWeights[i] : 1;
     a.seg_wt = kSegWeight;
     a.ws_header = reinterpret_cast<int32_t *>(ws);

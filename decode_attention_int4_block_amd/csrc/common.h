@@ -148,39 +148,45 @@ constexpr int kSplitWaves = 4;
 
 // Weighted split of the units over W workers: worker w takes a share in
 // proportion to wt[2 r + o], where r = (w >= W / 2) and o = the parity of its
-// workgroup w / kSplitWaves, so that waves of different measured speed
-// (dispatch order, XCD) finish together.  With fewer units than W full
-// workers need, an even split over the workers needed.
+// workgroup w / wg (wg = 1 or kSplitWaves workers per workgroup), so that
+// waves of different measured speed (dispatch order, XCD) finish together.
+// With fewer units than W full workers need, an even split over the workers
+// needed.
 struct Partition {
     int64_t total, W, half;
     int64_t wt[4];
     int64_t csum;           // cumulative weight of all W workers
+    int32_t wg_log2;        // log2 of the workers per workgroup
 };
 
-// Workers of [0, n) in even-numbered workgroups.
-__host__ __device__ inline int64_t even_wg_workers(int64_t n) {
-    constexpr int64_t S = kSplitWaves;
-    const int64_t rem = n % (2 * S);
-    return n / (2 * S) * S + (rem < S ? rem : S);
+// Workers of [0, n) in even-numbered workgroups of 2^l workers.
+__host__ __device__ inline int64_t even_wg_workers(int64_t n, int l) {
+    const int64_t S = (int64_t)1 << l;
+    const int64_t rem = n & (2 * S - 1);
+    return (n >> (l + 1)) * S + (rem < S ? rem : S);
 }
 
-__host__ __device__ inline int64_t count_even(int64_t a, int64_t b) { return even_wg_workers(b) - even_wg_workers(a); }
+__host__ __device__ inline int64_t count_even(const Partition &p, int64_t a, int64_t b) {
+    return even_wg_workers(b, p.wg_log2) - even_wg_workers(a, p.wg_log2);
+}
 
 // Cumulative weight of the workers [0, w).
 __host__ __device__ inline int64_t part_cum(const Partition &p, int64_t w) {
     const int64_t w0 = w < p.half ? w : p.half;
-    const int64_t e0 = count_even(0, w0);
+    const int64_t e0 = count_even(p, 0, w0);
     int64_t c = e0 * p.wt[0] + (w0 - e0) * p.wt[1];
     if (w > p.half) {
-        const int64_t e1 = count_even(p.half, w);
+        const int64_t e1 = count_even(p, p.half, w);
         c += e1 * p.wt[2] + (w - p.half - e1) * p.wt[3];
     }
     return c;
 }
 
+// wg: workers per workgroup of the launch (1 or kSplitWaves).
 __host__ __device__ inline Partition make_partition(int64_t total, int64_t max_workers, const int32_t *wt,
-                                                    int64_t min_units) {
+                                                    int64_t min_units, int wg = kSplitWaves) {
     Partition p;
+    p.wg_log2 = wg >= 4 ? 2 : (wg >= 2 ? 1 : 0);
     p.total = total;
     p.W = effective_workers(total, max_workers, min_units);
     p.half = p.W / 2;
@@ -285,6 +291,6 @@ hipError_t launch_quant_append(const AppendArgs &a, hipStream_t stream, bool gro
 hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream, bool grouped = false);
 hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t stream);
-hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool grouped = false);
+hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool grouped = false, int *out_wg = nullptr);
 
 }  // namespace kvq

@@ -1168,17 +1168,25 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
 template <int GP, bool APPEND, int BITS>
 constexpr int kSplitMinWaves = (GP == 16 && (APPEND || BITS != 4)) ? 1 : 2;
 
+// Workers per workgroup of one instantiation: kSplitWaves when a wave's LDS fits
+// its 1/8 share of the CU (two workgroups per CU), else 1 (the 8-head fused and
+// 16-head kernels need 21-27 KB per wave: a workgroup of four would leave room
+// for one per CU, i.e. one wave per SIMD).
+template <int GP, bool APPEND>
+constexpr int kSplitWG = SmemLayout<GP, APPEND>::kNeed <= SmemLayout<GP, APPEND>::kPad ? kSplitWaves : 1;
+
 template <int GP, bool APPEND, int BITS, bool MEM = false, bool KG = false>
-__global__ __launch_bounds__(64 * kSplitWaves)
+__global__ __launch_bounds__((64 * kSplitWG<GP, APPEND>))
 __attribute__((amdgpu_waves_per_eu(kSplitMinWaves<GP, APPEND, BITS>, 2)))
 void decode_split_kernel(DecodeArgs a) {
     using SL = SmemLayout<GP, APPEND>;
-    // kSplitWaves independent workers per workgroup (no barriers), each with
-    // its own slice of the workgroup's LDS
-    __shared__ __attribute__((aligned(16))) uint8_t smem_wg[kSplitWaves * SL::kRequest];
+    constexpr int NW = kSplitWG<GP, APPEND>;
+    // NW independent workers per workgroup (no barriers), each with its own
+    // slice of the workgroup's LDS
+    __shared__ __attribute__((aligned(16))) uint8_t smem_wg[NW * SL::kRequest];
     const int lane = threadIdx.x & 63;
-    const int wave = uni((int)(threadIdx.x >> 6));
-    const int64_t wid = (int64_t)blockIdx.x * kSplitWaves + wave;
+    const int wave = NW > 1 ? uni((int)(threadIdx.x >> 6)) : 0;
+    const int64_t wid = (int64_t)blockIdx.x * NW + wave;
     uint8_t *const smem = smem_wg + wave * SL::kRequest;
 
     // Exclusive prefix of the row costs (units of all KV heads of a row).  The
@@ -1226,7 +1234,7 @@ void decode_split_kernel(DecodeArgs a) {
         for (int o = 32; o >= 1; o >>= 1) rest += __shfl_xor(rest, o, 64);
         total += uni64(rest);
     }
-    const Partition part = make_partition(total, a.max_workers, a.part_wt, a.min_units);
+    const Partition part = make_partition(total, a.max_workers, a.part_wt, a.min_units, NW);
     const int64_t W = part.W;
     const int64_t u_begin = wid < W ? part_begin(part, wid) : 0;
     const int64_t u_end = wid < W ? part_begin(part, wid + 1) : 0;
@@ -1765,9 +1773,20 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
     }
 }
 
+template <int GP, bool APPEND, int BITS, bool MEM = false, bool KG = false>
+static void launch_split(const DecodeArgs &a, int grid, hipStream_t stream) {
+    constexpr int NW = kSplitWG<GP, APPEND>;
+    hipLaunchKernelGGL((decode_split_kernel<GP, APPEND, BITS, MEM, KG>), dim3(grid / NW), dim3(64 * NW), 0, stream, a);
+}
+
+struct SplitFn {
+    const void *fn;
+    int wg;         // workers per workgroup
+};
+
 template <int GP, bool APPEND, int BITS, bool KG = false>
-static const void *split_fn() {
-    return reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS, false, KG>);
+static SplitFn split_fn() {
+    return {reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS, false, KG>), kSplitWG<GP, APPEND>};
 }
 
 static int group_class(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
@@ -1778,41 +1797,41 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream, bool
         // grouped keys: attention only, query groups up to 8 (checked by the caller)
         const bool g4 = group_class(a.g) == 4;
         if (a.bits == 2) {
-            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
-            else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+            if (g4) launch_split<4, false, 2, false, true>(a, grid, stream);
+            else launch_split<8, false, 2, false, true>(a, grid, stream);
         } else if (a.bits == 3) {
-            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
-            else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+            if (g4) launch_split<4, false, 3, false, true>(a, grid, stream);
+            else launch_split<8, false, 3, false, true>(a, grid, stream);
         } else {
-            if (g4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
-            else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, false, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+            if (g4) launch_split<4, false, 4, false, true>(a, grid, stream);
+            else launch_split<8, false, 4, false, true>(a, grid, stream);
         }
     } else if (a.bits == 2) {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 2>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 4: launch_split<4, false, 2>(a, grid, stream); break;
+            case 5: launch_split<4, true, 2>(a, grid, stream); break;
+            case 8: launch_split<8, false, 2>(a, grid, stream); break;
+            case 9: launch_split<8, true, 2>(a, grid, stream); break;
+            case 16: launch_split<16, false, 2>(a, grid, stream); break;
+            default: launch_split<16, true, 2>(a, grid, stream); break;
         }
     } else if (a.bits == 3) {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 3>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 4: launch_split<4, false, 3>(a, grid, stream); break;
+            case 5: launch_split<4, true, 3>(a, grid, stream); break;
+            case 8: launch_split<8, false, 3>(a, grid, stream); break;
+            case 9: launch_split<8, true, 3>(a, grid, stream); break;
+            case 16: launch_split<16, false, 3>(a, grid, stream); break;
+            default: launch_split<16, true, 3>(a, grid, stream); break;
         }
     } else {
         switch (group_class(a.g) + (fused ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((decode_split_kernel<4, false, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((decode_split_kernel<4, true, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_split_kernel<8, false, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 9: hipLaunchKernelGGL((decode_split_kernel<8, true, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_split_kernel<16, false, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_split_kernel<16, true, 4>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a); break;
+            case 4: launch_split<4, false, 4>(a, grid, stream); break;
+            case 5: launch_split<4, true, 4>(a, grid, stream); break;
+            case 8: launch_split<8, false, 4>(a, grid, stream); break;
+            case 9: launch_split<8, true, 4>(a, grid, stream); break;
+            case 16: launch_split<16, false, 4>(a, grid, stream); break;
+            default: launch_split<16, true, 4>(a, grid, stream); break;
         }
     }
     hipError_t e = hipGetLastError();
@@ -1826,19 +1845,19 @@ hipError_t launch_decode_read_ceiling(const DecodeArgs &a, int grid, hipStream_t
     const int cls = group_class(a.g);
     if (cls == 16) return hipErrorNotSupported;
     if (a.bits == 2) {
-        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 2, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
-        else hipLaunchKernelGGL((decode_split_kernel<8, false, 2, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+        if (cls == 4) launch_split<4, false, 2, true>(a, grid, stream);
+        else launch_split<8, false, 2, true>(a, grid, stream);
     } else if (a.bits == 3) {
-        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 3, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
-        else hipLaunchKernelGGL((decode_split_kernel<8, false, 3, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+        if (cls == 4) launch_split<4, false, 3, true>(a, grid, stream);
+        else launch_split<8, false, 3, true>(a, grid, stream);
     } else {
-        if (cls == 4) hipLaunchKernelGGL((decode_split_kernel<4, false, 4, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
-        else hipLaunchKernelGGL((decode_split_kernel<8, false, 4, true>), dim3(grid / kSplitWaves), dim3(64 * kSplitWaves), 0, stream, a);
+        if (cls == 4) launch_split<4, false, 4, true>(a, grid, stream);
+        else launch_split<8, false, 4, true>(a, grid, stream);
     }
     return hipGetLastError();
 }
 
-hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool grouped) {
+hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool grouped, int *out_wg) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -1847,7 +1866,7 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool groupe
     if (e != hipSuccess) return e;
     int per_cu = 0;
     const int cls = group_class(g);
-    const void *fn;
+    SplitFn fn;
     if (grouped)
         fn = bits == 2 ? (cls == 4 ? split_fn<4, false, 2, true>() : split_fn<8, false, 2, true>())
            : bits == 3 ? (cls == 4 ? split_fn<4, false, 3, true>() : split_fn<8, false, 3, true>())
@@ -1864,7 +1883,7 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool groupe
         fn = cls == 4 ? split_fn<4, true, 4>() : (cls == 8 ? split_fn<8, true, 4>() : split_fn<16, true, 4>());
     else
         fn = cls == 4 ? split_fn<4, false, 4>() : (cls == 8 ? split_fn<8, false, 4>() : split_fn<16, false, 4>());
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kSplitWaves, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn.fn, 64 * fn.wg, 0);
     if (e != hipSuccess) return e;
     // The split kernel relies on every worker being resident at once (a worker
     // that starts late finishes late).  Measured on MI355X, a workgroup's LDS
@@ -1872,7 +1891,7 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool groupe
     // per workgroup admits 11, not 12, per CU), so bound the count by 160 KB of
     // LDS per CU in 2 KB blocks as well.
     hipFuncAttributes attr;
-    e = hipFuncGetAttributes(&attr, fn);
+    e = hipFuncGetAttributes(&attr, fn.fn);
     if (e != hipSuccess) return e;
     const size_t lds = (attr.sharedSizeBytes + 2047) & ~(size_t)2047;
     if (lds > 0) {
@@ -1880,7 +1899,8 @@ hipError_t decode_max_workers(int g, bool fused, int bits, int *out, bool groupe
         if (by_lds < per_cu) per_cu = by_lds;
     }
     if (per_cu < 1) per_cu = 1;
-    *out = cus * per_cu * kSplitWaves;      // workers (waves)
+    *out = cus * per_cu * fn.wg;            // workers (waves)
+    if (out_wg) *out_wg = fn.wg;
     return hipSuccess;
 }
 

@@ -37,11 +37,19 @@ int main() {
             if (m >= 1 && div_nonneg(m - 1, d) != (m - 1) / d) { printf("div_nonneg(%lld, %lld)\n", m - 1, d); return 1; }
         }
     }
+    // workers of [0, n) in even-numbered workgroups, against a count
+    for (int l : {0, 1, 2})
+    for (long long n = 0; n < 200; ++n) {
+        long long c = 0;
+        for (long long w = 0; w < n; ++w) c += ((w >> l) & 1) == 0;
+        if (even_wg_workers(n, l) != c) { printf("even_wg_workers(%lld, %d) = %lld, want %lld\n", n, l, (long long)even_wg_workers(n, l), c); return 1; }
+    }
+    for (int wg : {1, 4})
     for (const auto &wt : weights)
     for (long long total : {1LL, 7LL, 8LL, 100LL, 16383LL, 16384LL, 16385LL, 96700LL, 1234567LL, 99999989LL,
                             1099511627776LL})
     for (long long maxw : {1LL, 2LL, 3LL, 5LL, 2047LL, 2048LL, 2816LL}) {
-        const Partition p = make_partition(total, maxw, wt, 8);
+        const Partition p = make_partition(total, maxw, wt, 8, wg);
         if (p.W < 1 || p.W > maxw) { printf("bad W\n"); return 1; }
         long long prev = 0;
         for (long long w = 0; w < p.W; ++w) {
