@@ -324,28 +324,37 @@ void prefill_kernel(PrefillArgs a) {
             // an INT4 step inside the region and at or before the tile's first
             // row is valid for every column: no per-position tests
             const bool full = !int8 && base >= rp.lo4 && base + 32 <= min(rp.hi4, pos0 + 1);
+            if (full) {
+                // the common step: one wave-uniform branch, no per-position selects
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bool okA, okB;
-                if (full) {
-                    okA = okB = true;
-                } else if (int8) {
-                    const int e = base + 4 * G + j;
-                    okA = e < rp.n8e && ring_position(e, L, a.s, a.w) <= cpos;
-                    okB = false;
-                } else {
-                    const int pA = base + 4 * G + j, pB = pA + 16;
-                    okA = pA >= rp.lo4 && pA < rp.hi4 && pA <= cpos;
-                    okB = pB >= rp.lo4 && pB < rp.hi4 && pB <= cpos;
+                for (int j = 0; j < 4; ++j) {
+                    t[j] = fmaf(sA[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh);
+                    t[4 + j] = fmaf(sB[j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh);
+                    vp[j] = vpA[j];
+                    vp[4 + j] = vpB[j];
                 }
-                // params of positions outside the context may be arbitrary bytes
-                // (NaN as fp16): dropped by a select, never multiplied by zero
-                const float tA = fmaf(sA[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh);
-                const float tB = fmaf(sB[j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh);
-                t[j] = okA ? tA : kNegInf;
-                t[4 + j] = okB ? tB : kNegInf;
-                vp[j] = okA ? vpA[j] : 0u;
-                vp[4 + j] = okB ? vpB[j] : 0u;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    bool okA, okB;
+                    if (int8) {
+                        const int e = base + 4 * G + j;
+                        okA = e < rp.n8e && ring_position(e, L, a.s, a.w) <= cpos;
+                        okB = false;
+                    } else {
+                        const int pA = base + 4 * G + j, pB = pA + 16;
+                        okA = pA >= rp.lo4 && pA < rp.hi4 && pA <= cpos;
+                        okB = pB >= rp.lo4 && pB < rp.hi4 && pB <= cpos;
+                    }
+                    // params of positions outside the context may be arbitrary bytes
+                    // (NaN as fp16): dropped by a select, never multiplied by zero
+                    const float tA = fmaf(sA[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh);
+                    const float tB = fmaf(sB[j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh);
+                    t[j] = okA ? tA : kNegInf;
+                    t[4 + j] = okB ? tB : kNegInf;
+                    vp[j] = okA ? vpA[j] : 0u;
+                    vp[4 + j] = okB ? vpB[j] : 0u;
+                }
             }
         }
 
