@@ -144,7 +144,7 @@ struct SegCtx {
     float Ko;           // grouped keys: sum(o_d q~_d) * 2^(e - 24) over this lane's head (else 0)
     float mK;           // running max of this lane's head (log2 units)
     float lsum, zsum;   // sums of p and of p * zero_v over this lane's scores
-    floatx4 O[8];       // acc[row 4G+i][16 t + n], odd tiles scaled by 16
+    floatx4 O[8];       // acc[row 4G+i][16 t + n], tile t scaled by tile_scale
 };
 
 // Wave-uniform position in the unit stream of one worker.
@@ -331,7 +331,7 @@ __device__ inline QRing<GP> read_query(const uint8_t *slot, int lane) {
     return q;
 }
 
-template <int GP, bool KG = false>
+template <int GP, bool KG = false, int BITS = 4>
 __device__ inline void build_query(const DecodeArgs &a, const QRing<GP> &qr, const LaneCtx<GP> &L, SegCtx<GP> &c) {
     constexpr int V = GC<GP>::kVPL;
     constexpr int CPL = V / 8;            // chunks of 8 dims per lane (= kNP)
@@ -416,15 +416,17 @@ __device__ inline void build_query(const DecodeArgs &a, const QRing<GP> &qr, con
     c.Rh = ldexpf(sum, e - 24);
     c.Ko = KG ? ldexpf(osum, e - 24) : 0.0f;
     // chunks of 8 dims in the nibble order of a code dword:
-    // dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
+    // dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16); a 2-bit cache's key codes sit at
+    // their field positions (x4^d in operand dword d), so its query pairs are
+    // scaled by 1, 1/4, 1/16 and 1/64 instead
+    constexpr bool kPos2 = BITS == 2 && !KG;
+    const float sd[4] = {sc, kPos2 ? sc * 0.25f : s16, kPos2 ? s16 : sc, kPos2 ? sc * 0.015625f : s16};
     uint32_t H[CPL][4], Lo[CPL][4];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const float *y = x + 8 * k;
-        split2<1>(y[0] * sc, y[4] * sc, H[k][0], Lo[k][0]);
-        split2<1>(y[1] * s16, y[5] * s16, H[k][1], Lo[k][1]);
-        split2<1>(y[2] * sc, y[6] * sc, H[k][2], Lo[k][2]);
-        split2<1>(y[3] * s16, y[7] * s16, H[k][3], Lo[k][3]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) split2<1>(y[d] * sd[d], y[4 + d] * sd[d], H[k][d], Lo[k][d]);
     }
     if constexpr (GC<GP>::kPacked) {
         uint32_t w[4][4];
@@ -781,48 +783,51 @@ __device__ inline half8 group_key_operand(uint32_t x, int b) {
 template <int GP, int BITS, bool KG = false>
 __device__ inline KAcc<GP> kpart_mfma(const DecodeArgs &a, const SegCtx<GP> &c, const StepRegs<GP> &r, bool main2) {
     constexpr int kQ = GC<GP>::kQ;
-    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    KAcc<GP> k;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) k.dA[q] = k.dB[q] = zero4;
+    // Operands of chunks 0-3 of subblocks A and B (an INT8 step: of its low- and
+    // high-nibble planes), built by whichever kind of step this is; the MFMAs
+    // below are shared, so the accumulators keep one register assignment.
+    half8 ak[4], bk[4];
     if (KG && main2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int b = a.key_bits[i];
-            const half8 ak = group_key_operand(r.kA[i], b), bk = group_key_operand(r.kB[i], b);
-#pragma unroll
-            for (int q = 0; q < kQ; ++q) {
-                k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
-                k.dB[q] = mfma16(bk, c.q4[q][i], k.dB[q]);
-            }
+            ak[i] = group_key_operand(r.kA[i], b);
+            bk[i] = group_key_operand(r.kB[i], b);
         }
-        return k;
-    }
-    if ((BITS == 2 || BITS == 3) && main2) {
+    } else if ((BITS == 2 || BITS == 3) && main2) {
         // chunk i: dword i / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t xa = r.kA[i >> 1] >> (8 * (i & 1)), xb = r.kB[i >> 1] >> (8 * (i & 1));
-            const half8 ak = BITS == 3 ? int3_key_chunk(xa, r.kA[2], i) : int2_chunk(xa);
-            const half8 bk = BITS == 3 ? int3_key_chunk(xb, r.kB[2], i) : int2_chunk(xb);
-#pragma unroll
-            for (int q = 0; q < kQ; ++q) {
-                k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
-                k.dB[q] = mfma16(bk, c.q4[q][i], k.dB[q]);
-            }
+            ak[i] = BITS == 3 ? int3_key_chunk(xa, r.kA[2], i) : int2_chunk_pos(xa);
+            bk[i] = BITS == 3 ? int3_key_chunk(xb, r.kB[2], i) : int2_chunk_pos(xb);
         }
-        return k;
+    } else if (BITS == 2 && !KG) {
+        // INT8 steps of a 2-bit cache: the nibbles at the 2-bit query scaling
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ak[i] = nibble_chunk_pos(r.kA[i]);
+            bk[i] = nibble_chunk_pos(r.kB[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t x = r.kA[i], x8 = x >> 8;
+            ak[i] = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
+            const uint32_t y = r.kB[i], y8 = y >> 8;
+            bk[i] = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
+        }
     }
+    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    KAcc<GP> k;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) k.dA[q] = k.dB[q] = zero4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t x = r.kA[i], x8 = x >> 8;
-        const half8 ak = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
-        const uint32_t y = r.kB[i], y8 = y >> 8;
-        const half8 bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            k.dA[q] = mfma16(ak, c.q4[q][i], k.dA[q]);
-            k.dB[q] = mfma16(bk, c.q4[q][i], k.dB[q]);
+            k.dA[q] = mfma16(ak[i], c.q4[q][i], k.dA[q]);
+            k.dB[q] = mfma16(bk[i], c.q4[q][i], k.dB[q]);
         }
     }
     return k;
@@ -883,34 +888,55 @@ __device__ inline void vpart(SegCtx<GP> &c, const LaneCtx<GP> &L, const KOut<GP>
             for (int j = 0; j < 4; ++j) pop[q][4 + j] = pop[q][4 + j] * wb + pop[q][j] * wa;
         }
     }
+    // B operand of accumulator tile t, built by whichever kind of step this is;
+    // the MFMAs below are shared, so the accumulators keep one register
+    // assignment across the branch.
+    half8 vt[8];
     if ((BITS == 2 || BITS == 3) && !k.int8) {
-        // 2-bit values: dword cc, field f = dims 16 (4 cc + f) + n, tile 4 cc + f
-        // (3-bit: with the high bits of the lane's value-plane dword word 2)
+        // 2-bit values: dword cc, field f = dims 16 (4 cc + f) + n, tile 4 cc + f,
+        // the codes left at their field positions (x4^f); 3-bit: normalised
+        // fields with the high bits of the lane's value-plane dword word 2
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                const half8 vt = BITS == 3
+                const uint32_t m = 0x00030003u << (2 * f);
+                vt[4 * cc + f] = BITS == 3
                     ? pack8(int3_value_field(x, k.vA[2], cc, f, false), int3_value_field(x8, k.vA[2], cc, f, true),
                             int3_value_field(y, k.vB[2], cc, f, false), int3_value_field(y8, k.vB[2], cc, f, true))
-                    : pack8(int2_field(x, f), int2_field(x8, f), int2_field(y, f), int2_field(y8, f));
-#pragma unroll
-                for (int q = 0; q < kQ; ++q) c.O[4 * cc + f] = mfma16(pop[q], vt, c.O[4 * cc + f]);
+                    : pack8(x & m, x8 & m, y & m, y8 & m);
             }
         }
-        return;
+    } else if (BITS == 2) {
+        // INT8 steps of a 2-bit cache: each nibble moved to its tile's scaling
+        // 4^(t % 4) (tiles 2 cc and 2 cc + 1)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
+            if (cc & 1) {
+                vt[2 * cc] = pack8((x << 4) & 0x00F000F0u, (x8 << 4) & 0x00F000F0u, (y << 4) & 0x00F000F0u,
+                                   (y8 << 4) & 0x00F000F0u);
+                vt[2 * cc + 1] = pack8((x << 2) & 0x03C003C0u, (x8 << 2) & 0x03C003C0u, (y << 2) & 0x03C003C0u,
+                                       (y8 << 2) & 0x03C003C0u);
+            } else {
+                vt[2 * cc] = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
+                vt[2 * cc + 1] = pack8((x >> 2) & 0x003C003Cu, (x8 >> 2) & 0x003C003Cu, (y >> 2) & 0x003C003Cu,
+                                       (y8 >> 2) & 0x003C003Cu);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
+            vt[2 * cc] = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
+            vt[2 * cc + 1] = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
+        }
     }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-        const uint32_t x = k.vA[cc], x8 = x >> 8, y = k.vB[cc], y8 = y >> 8;
-        const half8 ve = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
-        const half8 vo = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
+    for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-            c.O[2 * cc] = mfma16(pop[q], ve, c.O[2 * cc]);
-            c.O[2 * cc + 1] = mfma16(pop[q], vo, c.O[2 * cc + 1]);
-        }
+        for (int q = 0; q < kQ; ++q) c.O[t] = mfma16(pop[q], vt[t], c.O[t]);
     }
 }
 
@@ -975,8 +1001,17 @@ __device__ inline SegOut<GP> reduce_segment(SegCtx<GP> &c, const LaneCtx<GP> &L,
     return s;
 }
 
+// Factor from accumulator tile t to the value codes' units times 2^24 (the
+// codes enter the MFMAs as f16 subnormals c 2^-24): odd tiles hold 16 c, and a
+// 2-bit cache's tiles 4^(t % 4) c.
+template <int BITS>
+__device__ inline float tile_scale(int t) {
+    if constexpr (BITS == 2) return ldexpf(1.0f, 24 - 2 * (t & 3));
+    return (t & 1) ? 1048576.0f : 16777216.0f;      // 2^20 / 2^24
+}
+
 // Output of a segment that one worker attended completely: straight from registers.
-template <int GP>
+template <int GP, int BITS>
 __device__ inline void finalize_regs(const DecodeArgs &a, const SegCtx<GP> &c, const LaneCtx<GP> &L,
                                      const SegOut<GP> &s, int b, int hk) {
     float *ob = a.out + ((int64_t)b * a.Hq + (int64_t)hk * a.g) * kHeadDim;
@@ -989,8 +1024,7 @@ __device__ inline void finalize_regs(const DecodeArgs &a, const SegCtx<GP> &c, c
         if (hd >= 0) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float sc = (t & 1) ? 1048576.0f : 16777216.0f;   // 2^20 / 2^24
-                ob[hd * kHeadDim + 16 * t + L.n] = fmaf(s.R[t][k], sc, zr) * ir;
+                ob[hd * kHeadDim + 16 * t + L.n] = fmaf(s.R[t][k], tile_scale<BITS>(t), zr) * ir;
             }
         }
     }
@@ -999,7 +1033,7 @@ __device__ inline void finalize_regs(const DecodeArgs &a, const SegCtx<GP> &c, c
 }
 
 // Partial statistics of a segment: per query head m, l and the unnormalised acc[128].
-template <int GP>
+template <int GP, int BITS>
 __device__ inline void write_piece(const DecodeArgs &a, const SegCtx<GP> &c, const LaneCtx<GP> &L,
                                    const SegOut<GP> &s, float *pp) {
     if (L.lane < a.g && L.lane < GP) {
@@ -1013,8 +1047,7 @@ __device__ inline void write_piece(const DecodeArgs &a, const SegCtx<GP> &c, con
         if (hd >= 0) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float sc = (t & 1) ? 1048576.0f : 16777216.0f;
-                pp[hd * kPieceStride + 4 + 16 * t + L.n] = fmaf(s.R[t][k], sc, zr);
+                pp[hd * kPieceStride + 4 + 16 * t + L.n] = fmaf(s.R[t][k], tile_scale<BITS>(t), zr);
             }
         }
     }
@@ -1390,9 +1423,9 @@ void decode_split_kernel(DecodeArgs a) {
         if (!first) wseg0 = (int32_t)seg;            // only the wave's first segment can start earlier
         if (!last) wseg1 = (int32_t)seg;             // only its last one can go on after it
         if (first && last)
-            finalize_regs<GP>(a, c, L, so, E.b, E.hk);
+            finalize_regs<GP, BITS>(a, c, L, so, E.b, E.hk);
         else
-            write_piece<GP>(a, c, L, so, a.ws_piece + (wid + seg) * (int64_t)a.g * kPieceStride);
+            write_piece<GP, BITS>(a, c, L, so, a.ws_piece + (wid + seg) * (int64_t)a.g * kPieceStride);
     };
     bool open = false;          // the next step continues the current segment
     bool pend = false;          // a step of the current segment awaits its value part
@@ -1432,7 +1465,7 @@ void decode_split_kernel(DecodeArgs a) {
             }
             // a segment's first step finds mK = -inf and scales O, lsum and
             // zsum (finite leftovers of the previous segment) by 0
-            build_query<GP, KG>(a, qr, L, c);
+            build_query<GP, KG, BITS>(a, qr, L, c);
             c.mK = kNegInf;
             open = true;
         }

@@ -149,6 +149,17 @@ __device__ inline uint32_t int2_field(uint32_t x, int f) {
 __device__ inline half8 int2_chunk(uint32_t x) {
     return pack8(int2_field(x, 0), int2_field(x, 1), int2_field(x, 2), int2_field(x, 3));
 }
+// The decode kernel's 2-bit operands leave each code at its field position:
+// operand dword f holds field f of bytes 0 and 2 (dims f, 4 + f of the chunk)
+// as (4^f c) 2^-24, one AND each; the query pairs carry the inverse scales.
+__device__ inline half8 int2_chunk_pos(uint32_t x) {
+    return pack8(x & 0x00030003u, x & 0x000C000Cu, x & 0x00300030u, x & 0x00C000C0u);
+}
+// INT8 key nibbles (INT4 order: dims (0, 4), (1, 5), (2, 6), (3, 7) of the
+// chunk) at those scales: 1, 4, 16, 64 (15 * 64 < 1024 stays subnormal).
+__device__ inline half8 nibble_chunk_pos(uint32_t x) {
+    return pack8(x & 0x000F000Fu, (x >> 2) & 0x003C003Cu, (x >> 4) & 0x00F000F0u, (x >> 6) & 0x03C003C0u);
+}
 // 3-bit codes: a 2-bit field with its high bit ORed in at value 4 (bit 2 or 6
 // of each half, next to the field's two bits).  h holds the high bits of the
 // field's codes at bits 2 / 6 (+ 16) for the even / odd fields, or 8 above.

@@ -199,3 +199,23 @@ def test_fused_full_size_step(bits):
     err, err_lse, _ = compare_attention(fus, rows)
     _report(f"qwen3_8b_async_256 {bits}-bit", rows=rows, max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
     assert err <= ATOL and err_lse <= ATOL
+
+
+def test_fused_full_size_long_row():
+    """The 128K-position row (query group 8) in the benchmark's launch
+    configuration: the fused kernel of that group size holds one worker per
+    workgroup (its stage ring and append slots fill a worker's LDS share), and
+    the row is split over many workers and folded by the combine's helpers."""
+    cfg = get_config("long_128k")
+    sep, fus = _pair(cfg, keep=[0], gen_device="cuda")
+    assert torch.equal(sep.cache.int4_pool, fus.cache.int4_pool)
+    assert torch.equal(sep.cache.int8_pool, fus.cache.int8_pool)
+    d_out = float((sep.out - fus.out).abs().max())
+    if _workers(sep) == _workers(fus):
+        assert torch.equal(sep.out, fus.out) and torch.equal(sep.lse, fus.lse)
+    else:
+        assert d_out <= 1e-5, d_out
+    err, err_lse, _ = compare_attention(fus, [0])
+    _report("long_128k", workers=(_workers(sep), _workers(fus)), d_two_launch=f"{d_out:.1e}",
+            max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
+    assert err <= ATOL and err_lse <= ATOL
