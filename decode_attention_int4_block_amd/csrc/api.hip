@@ -321,6 +321,7 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     int cus = 0;
     st = cu_count(&cus);
     if (st != KVQ_OK) return st;
+    a.simds = 4 * cus;
     const bool paired = wg == kvq::kSplitWaves && (int64_t)workers >= 2LL * kvq::kSplitWaves * cus;
     for (int i = 0; i < 4; ++i) a.part_wt[i] = paired ? kPartWeights[i] : 1;
     a.seg_wt = kSegWeight;

@@ -131,10 +131,16 @@ __host__ __device__ inline int64_t div_nonneg(int64_t n, int64_t d) {
 // with fewer units than 512 workers of min_units each (a few short rows) takes
 // half that per worker: its time is one worker's chain of steps, not the
 // combine of the extra pieces (measured: a 1024-token row, 20 -> 17 us).
-__host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_workers, int64_t min_units) {
+// Between one worker per SIMD (simds, when given) and max_workers, the count
+// is rounded down to one per SIMD: a few workers past it would put a second
+// wave on a few SIMDs, and those pairs end the launch (measured on one 128K
+// row: split 20.6 -> 18.4 us, and half the pieces for the combine).
+__host__ __device__ inline int64_t effective_workers(int64_t total, int64_t max_workers, int64_t min_units,
+                                                     int64_t simds = 0) {
     if (total < 512 * min_units && min_units > 1) min_units = (min_units + 1) / 2;
     int64_t w = div_nonneg(total + min_units - 1, min_units);
     if (w < 1) w = 1;
+    if (simds > 0 && w > simds && w < max_workers) w = simds;
     return w < max_workers ? w : max_workers;
 }
 
@@ -182,13 +188,14 @@ __host__ __device__ inline int64_t part_cum(const Partition &p, int64_t w) {
     return c;
 }
 
-// wg: workers per workgroup of the launch (1 or kSplitWaves).
+// wg: workers per workgroup of the launch (1 or kSplitWaves); simds: SIMDs of
+// the device, or 0 for no rounding of the worker count.
 __host__ __device__ inline Partition make_partition(int64_t total, int64_t max_workers, const int32_t *wt,
-                                                    int64_t min_units, int wg = kSplitWaves) {
+                                                    int64_t min_units, int wg = kSplitWaves, int64_t simds = 0) {
     Partition p;
     p.wg_log2 = wg >= 4 ? 2 : (wg >= 2 ? 1 : 0);
     p.total = total;
-    p.W = effective_workers(total, max_workers, min_units);
+    p.W = effective_workers(total, max_workers, min_units, simds);
     p.half = p.W / 2;
     const bool weighted = p.W == max_workers && p.W >= 2;
     for (int i = 0; i < 4; ++i) p.wt[i] = weighted ? wt[i] : 1;
@@ -205,9 +212,9 @@ __host__ __device__ inline int64_t part_begin(const Partition &p, int64_t w) {
 // ranges are never returned.  (The inverse of part_begin, for checking it.)
 __host__ __device__ inline int64_t part_of(const Partition &p, int64_t u) {
     // invert the cumulative weight, then correct the rounding
-    const int64_t c = u * p.csum / p.total;
+    const int64_t c = div_nonneg(u * p.csum, p.total);
     const int64_t ch = part_cum(p, p.half);
-    int64_t w = c < ch ? 2 * c / (p.wt[0] + p.wt[1]) : p.half + 2 * (c - ch) / (p.wt[2] + p.wt[3]);
+    int64_t w = c < ch ? div_nonneg(2 * c, p.wt[0] + p.wt[1]) : p.half + div_nonneg(2 * (c - ch), p.wt[2] + p.wt[3]);
     if (w > p.W - 1) w = p.W - 1;
     if (w < 0) w = 0;
     while (w > 0 && part_begin(p, w) > u) --w;
@@ -251,6 +258,7 @@ struct DecodeArgs {
     int32_t bits;                       // main cache code width: 4, 3 or 2
     float inv_sqrt_h;
     int32_t max_workers, min_units;
+    int32_t simds;                      // SIMDs of the device (4 per CU)
     int32_t part_wt[4];                 // worker weights (Partition)
     int32_t seg_wt;                     // weight-only units counted before each segment
     int32_t key_bits[4];    // grouped keys: width of each RoPE-block group (KG launches)

@@ -1231,7 +1231,7 @@ void decode_split_kernel(DecodeArgs a) {
     // used, each load waited on the prologue's critical path).
     __asm__ volatile("" ::"s"(a.ws_header), "s"(a.ws_wseg), "s"(a.block_table), "s"(a.bt_stride), "s"(a.H),
                      "s"(a.P), "s"(a.logP), "s"(a.s), "s"(a.w), "s"(a.nr8), "s"(a.max_workers), "s"(a.min_units),
-                     "s"(a.part_wt[0]), "s"(a.part_wt[1]), "s"(a.part_wt[2]), "s"(a.part_wt[3]), "s"(a.seg_wt),
+                     "s"(a.simds), "s"(a.part_wt[0]), "s"(a.part_wt[1]), "s"(a.part_wt[2]), "s"(a.part_wt[3]), "s"(a.seg_wt),
                      "s"(a.int4_pool), "s"(a.int8_pool), "s"(a.q), "s"(a.Hq), "s"(a.g), "s"(a.ws_piece),
                      "s"(a.out), "s"(a.lse));
     int64_t cost[4], excl[4];
@@ -1267,7 +1267,7 @@ void decode_split_kernel(DecodeArgs a) {
         for (int o = 32; o >= 1; o >>= 1) rest += __shfl_xor(rest, o, 64);
         total += uni64(rest);
     }
-    const Partition part = make_partition(total, a.max_workers, a.part_wt, a.min_units, NW);
+    const Partition part = make_partition(total, a.max_workers, a.part_wt, a.min_units, NW, a.simds);
     const int64_t W = part.W;
     const int64_t u_begin = wid < W ? part_begin(part, wid) : 0;
     const int64_t u_end = wid < W ? part_begin(part, wid + 1) : 0;

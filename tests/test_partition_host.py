@@ -1,6 +1,8 @@
 """Host check of the work split shared by the decode kernels (csrc/common.h).
 
 The split kernel gives worker w the units [part_begin(w), part_begin(w + 1)).
+Between one worker per SIMD and the maximum, the worker count is rounded down
+to one per SIMD.
 The ranges must tile [0, total), and part_of(u), their inverse, must agree
 with them exactly and never return a worker without units.  part_begin
 divides with div_nonneg, whose 32-bit, corrected double-precision and 64-bit
@@ -46,11 +48,16 @@ int main() {
     }
     for (int wg : {1, 4})
     for (const auto &wt : weights)
-    for (long long total : {1LL, 7LL, 8LL, 100LL, 16383LL, 16384LL, 16385LL, 96700LL, 1234567LL, 99999989LL,
-                            1099511627776LL})
-    for (long long maxw : {1LL, 2LL, 3LL, 5LL, 2047LL, 2048LL, 2816LL}) {
-        const Partition p = make_partition(total, maxw, wt, 8, wg);
+    for (long long total : {1LL, 7LL, 8LL, 100LL, 8230LL, 12000LL, 16383LL, 16384LL, 16385LL, 96700LL, 1234567LL,
+                            99999989LL, 1099511627776LL})
+    for (long long maxw : {1LL, 2LL, 3LL, 5LL, 2047LL, 2048LL, 2816LL})
+    for (long long simds : {0LL, 1024LL}) {
+        const Partition p = make_partition(total, maxw, wt, 8, wg, simds);
         if (p.W < 1 || p.W > maxw) { printf("bad W\n"); return 1; }
+        // between one worker per SIMD and the maximum, one per SIMD
+        const Partition p0 = make_partition(total, maxw, wt, 8, wg, 0);
+        const long long want = (simds > 0 && p0.W > simds && p0.W < maxw) ? simds : p0.W;
+        if (p.W != want) { printf("W %lld, want %lld (total %lld, max %lld)\n", (long long)p.W, want, total, maxw); return 1; }
         long long prev = 0;
         for (long long w = 0; w < p.W; ++w) {
             const long long b0 = part_begin(p, w), b1 = part_begin(p, w + 1);
