@@ -641,6 +641,69 @@ __device__ inline void issue_step(const DecodeArgs &a, const Cursor &c, const Lo
 
 
 
+// Paired 2-bit steps.  Two consecutive INT4-region steps of one segment
+// (positions pos0 .. pos0 + 63, subblocks A, B, C, D) share a stage: five
+// loads of 64 lanes copy the key codes of A | B and of C | D, the value codes
+// of A | B and of C | D, and the params of all four (lanes 0-15 those of A and
+// B, as for a single step, lanes 16-31 those of C and D).  Stage layout: the
+// single step's at offset 0 (A, B) and again at 2048 (C, D), the params at
+// 4096 and 4352.  A pair moves the bytes of one 4-bit step, and its producer
+// work, stage wait and cursor advance are those of one step.
+constexpr int kPairHalf = 2048;         // stage offset of the second step's codes
+constexpr int kPairParams = 256;        // and of its params (relative to the first's)
+constexpr int kStagePair = kStageBytes + kPairParams;
+
+// Built where the second step's registers fit beside the first's: query
+// groups up to 4, and up to 8 without the fused append (the 8-head fused
+// kernel would spill).
+template <int GP, bool APPEND, int BITS, bool KG>
+constexpr bool kPair = BITS == 2 && !KG && (GP == 4 || (GP == 8 && !APPEND));
+
+template <int GP, bool APPEND, int BITS, bool KG>
+constexpr int kStageB = kPair<GP, APPEND, BITS, KG> ? kStagePair : kStageBytes;
+
+// Whether the step at cursor c is paired with the next: both INT4-region steps
+// of the segment inside the worker's range [.., u_end), and neither the unit of
+// the appended token (the fused append patches that step's stage alone).
+// Producer and consumer walk the same cursors, so they pair alike.
+template <int GP, int BITS, bool KG, bool APPEND>
+__device__ inline bool pairable(const Cursor &c, int64_t u_end) {
+    if constexpr (!kPair<GP, APPEND, BITS, KG>) {
+        return false;
+    } else {
+        bool ok = c.r + 1 < c.rp.n4 && c.u + 1 < u_end;
+        if constexpr (APPEND) ok = ok && c.r != c.rp.rn && c.r + 1 != c.rp.rn;
+        return ok;
+    }
+}
+
+// Producer of a paired 2-bit step at cursor c (k0, k1: pages of its two units).
+__device__ inline void issue_pair2(const DecodeArgs &a, const Cursor &c, const Lookup &k0, const Lookup &k1,
+                                   uint8_t *st, uint32_t offP4, int lane) {
+    const uint32_t sh = (uint32_t)a.logP - 4;
+    const int pos0 = (c.rp.k0 + c.r) * 32;
+    auto sub = [&](int page, int pos) {
+        const uint32_t idx =
+            (((uint32_t)page * (uint32_t)a.H + (uint32_t)c.hk) << sh) + ((uint32_t)(pos & (a.P - 1)) >> 4);
+        return a.int4_pool + (uint64_t)idx * kSub2Bytes;
+    };
+    // B and C lie inside the INT4 region (the second step exists); D past it
+    // is never used: re-read C (valid memory)
+    const uint8_t *bA = sub(k0.pageA, pos0), *bB = sub(k0.pageB, pos0 + 16);
+    const uint8_t *bC = sub(k1.pageA, pos0 + 32);
+    const uint8_t *bD = pos0 + 48 < c.rp.hi4 ? sub(k1.pageB, pos0 + 48) : bC;
+    const uint32_t o16 = 16u * (uint32_t)(lane & 31);
+    const bool upper = lane >= 32;
+    dma16_stream(upper ? bB : bA, kSub2K + o16, st + 0);
+    dma16_stream(upper ? bD : bC, kSub2K + o16, st + kPairHalf);
+    dma16_stream(upper ? bB : bA, kSub2V + o16, st + 1024);
+    dma16_stream(upper ? bD : bC, kSub2V + o16, st + kPairHalf + 1024);
+    if (lane < 32) {
+        const uint8_t *pb = (lane & 16) ? ((lane & 4) ? bD : bC) : ((lane & 4) ? bB : bA);
+        dma16_stream(pb, offP4 - kSub4KP + kSub2KP, st + kStKP);
+    }
+}
+
 // main2: a 2- or 3-bit main-cache step (8 bytes of low-plane codes per lane and
 // quarter; at 3 bits the lane's high-plane dword goes to word 2).
 __device__ inline uint32_t lds16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
@@ -650,8 +713,11 @@ __device__ inline uint32_t lds16(const uint8_t *p) { return *reinterpret_cast<co
 // dword (width 4), the 16-bit field word (width 2), or the field word with the
 // high-bit byte in bits 16-23 (width 3); values as the value width's step, at
 // the stage offsets the grouped copy uses.
+// pdelta: offset of the step's params from where a single step keeps them
+// (the second step of a pair: kPairParams - kPairHalf).
 template <int GP, int BITS, bool KG = false>
-__device__ inline StepRegs<GP> read_stage(const DecodeArgs &a, const uint8_t *st, const LaneCtx<GP> &L, bool main2) {
+__device__ inline StepRegs<GP> read_stage(const DecodeArgs &a, const uint8_t *st, const LaneCtx<GP> &L, bool main2,
+                                          int pdelta = 0) {
     StepRegs<GP> r;
     const int lane = L.lane;
     if (KG && main2) {
@@ -701,8 +767,8 @@ __device__ inline StepRegs<GP> read_stage(const DecodeArgs &a, const uint8_t *st
         r.vA = *reinterpret_cast<const u32x4 *>(st + 2048 + lane * 16);
         r.vB = *reinterpret_cast<const u32x4 *>(st + 3072 + lane * 16);
     }
-    const uint8_t *kp = st + L.offKP;
-    const uint8_t *vp = st + L.offKP + (kStVP - kStKP);
+    const uint8_t *kp = st + pdelta + L.offKP;
+    const uint8_t *vp = st + pdelta + L.offKP + (kStVP - kStKP);
     if constexpr (GP == 4) {
         // tokens t0, t0 + 2
         r.kp[0] = lds32(kp);
@@ -1148,9 +1214,9 @@ __device__ inline void append_new_token(const DecodeArgs &a, const RowRegs &R, c
 // faster than 12).
 constexpr int kWavesPerCU = 8;
 
-template <int GP, bool APPEND>
+template <int GP, bool APPEND, int SB = kStageBytes>
 struct SmemLayout {
-    static constexpr int kPages = kStages * kStageBytes;
+    static constexpr int kPages = kStages * SB;
     static constexpr int kQ = kPages + kPgBytes;
     static constexpr int kKv = kQ + kStages * QRing<GP>::kBytes;
     static constexpr int kNeed = kKv + (APPEND ? kStages * kKvBytes : 0);
@@ -1205,15 +1271,21 @@ constexpr int kSplitMinWaves = (GP == 16 && (APPEND || BITS != 4)) ? 1 : 2;
 // its 1/8 share of the CU (two workgroups per CU), else 1 (the 8-head fused and
 // 16-head kernels need 21-27 KB per wave: a workgroup of four would leave room
 // for one per CU, i.e. one wave per SIMD).
-template <int GP, bool APPEND>
-constexpr int kSplitWG = SmemLayout<GP, APPEND>::kNeed <= SmemLayout<GP, APPEND>::kPad ? kSplitWaves : 1;
+template <int GP, bool APPEND, int BITS, bool KG = false>
+using SplitSmem = SmemLayout<GP, APPEND, kStageB<GP, APPEND, BITS, KG>>;
+
+template <int GP, bool APPEND, int BITS = 4, bool KG = false>
+constexpr int kSplitWG =
+    SplitSmem<GP, APPEND, BITS, KG>::kNeed <= SplitSmem<GP, APPEND, BITS, KG>::kPad ? kSplitWaves : 1;
 
 template <int GP, bool APPEND, int BITS, bool MEM = false, bool KG = false>
-__global__ __launch_bounds__((64 * kSplitWG<GP, APPEND>))
+__global__ __launch_bounds__((64 * kSplitWG<GP, APPEND, BITS, KG>))
 __attribute__((amdgpu_waves_per_eu(kSplitMinWaves<GP, APPEND, BITS>, 2)))
 void decode_split_kernel(DecodeArgs a) {
-    using SL = SmemLayout<GP, APPEND>;
-    constexpr int NW = kSplitWG<GP, APPEND>;
+    using SL = SplitSmem<GP, APPEND, BITS, KG>;
+    constexpr int NW = kSplitWG<GP, APPEND, BITS, KG>;
+    constexpr int SB = kStageB<GP, APPEND, BITS, KG>;       // bytes of a stage slot
+    constexpr bool PAIR = kPair<GP, APPEND, BITS, KG>;
     // NW independent workers per workgroup (no barriers), each with its own
     // slice of the workgroup's LDS
     __shared__ __attribute__((aligned(16))) uint8_t smem_wg[NW * SL::kRequest];
@@ -1362,8 +1434,8 @@ void decode_split_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     KVQ_FENCE();
     // pages of the producer's next step (LDS reads; waited with the stage reads)
-    auto read_pages = [&](const Cursor &c) {
-        int j = (int)(c.u - hb);
+    auto read_pages = [&](const Cursor &c, int d) {
+        int j = (int)(c.u + d - hb);
         int h = hcur;
         if (j >= kPgHalf) {
             j -= kPgHalf;
@@ -1392,12 +1464,19 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < kStages; ++s) {
         if (P.u < u_end) {
-            const Lookup look = uniform(read_pages(P));
+            const bool pp = pairable<GP, BITS, KG, APPEND>(P, u_end);
+            const Lookup look = uniform(read_pages(P, 0));
             if (P.r == 0 || P.u == start.u) issue_query<GP>(a, P.b, P.hk, L, qring + s * QRing<GP>::kBytes);
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + s * kKvBytes, lane);
             }
-            issue_step<BITS, KG>(a, P, look, smem + s * kStageBytes, offK, offV, offP4, offP8, lane);
+            if (PAIR && pp) {
+                issue_pair2(a, P, look, uniform(read_pages(P, 1)), smem + s * SB, offP4, lane);
+                ++P.u;          // the pair's second step (same segment)
+                ++P.r;
+            } else {
+                issue_step<BITS, KG>(a, P, look, smem + s * SB, offK, offV, offP4, offP8, lane);
+            }
             cursor_next(a, R, P);
             ++issued;
             advance_half(P);
@@ -1438,21 +1517,36 @@ void decode_split_kernel(DecodeArgs a) {
     // (A query copy issued with a later step only makes the stage waits
     // stricter.)
     Lookup look = {0, 0, 0};    // pages of the producer's step P
-    if (P.u < u_end) look = read_pages(P);
+    Lookup look1 = {0, 0, 0};   // and of its second step when it is a pair
+    bool ppair = false;         // the producer's step P is a pair
+    if (P.u < u_end) {
+        ppair = pairable<GP, BITS, KG, APPEND>(P, u_end);
+        look = read_pages(P, 0);
+        if (PAIR && ppair) look1 = read_pages(P, 1);
+    }
     wait_vm_steps(issued - 1);
     if constexpr (APPEND) {
         if (C.r == C.rp.rn) append_new_token<BITS>(a, R, C, kvring, smem, lane);
     }
+    bool cpair = pairable<GP, BITS, KG, APPEND>(C, u_end);      // the step at C is a pair
     StepRegs<GP> r = read_stage<GP, BITS, KG>(a, smem, L, C.r < C.rp.n4);
+    StepRegs<GP> r1 = r;        // its second step
+    if (PAIR && cpair) r1 = read_stage<GP, BITS, KG>(a, smem + kPairHalf, L, true, kPairParams - kPairHalf);
     QRing<GP> qr = read_query<GP>(qring, lane);     // the first step opens a segment
     wait_lgkm0();
     look = uniform(look);
+    look1 = uniform(look1);
     uint32_t sink = 0;          // MEM: what the stage reads returned, kept live
     for (int i = 0; C.u < u_end; ++i) {
         const int scur = i % kStages, snxt = (i + 1) % kStages;
         const bool int4 = C.r < C.rp.n4;
         if constexpr (MEM) {
             sink ^= r.kA[0] ^ r.kB[1] ^ r.vA[2] ^ r.vB[3] ^ r.kp[0] ^ r.vp[0] ^ qr.w[0][0];
+            if (PAIR && cpair) {
+                sink ^= r1.kA[0] ^ r1.kB[1] ^ r1.vA[0] ^ r1.vB[1] ^ r1.kp[0] ^ r1.vp[0];
+                ++C.u;
+                ++C.r;
+            }
             if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
             cursor_next(a, R, C);
         } else {
@@ -1478,6 +1572,15 @@ void decode_split_kernel(DecodeArgs a) {
         kp = kpart_tail<GP, KG>(c, L, r, ka, !int4, sbase, slo, shi);
         pend = true;
         E = C;
+        if (PAIR && cpair) {
+            // the pair's second step: the same sequence, 32 positions on
+            const KAcc<GP> ka1 = kpart_mfma<GP, BITS, KG>(a, c, r1, true);
+            vpart<GP, BITS>(c, L, kp);
+            kp = kpart_tail<GP, KG>(c, L, r1, ka1, false, sbase + 32, slo, shi);
+            ++C.u;
+            ++C.r;
+            E = C;
+        }
         if (C.r == C.rp.cost - 1 || C.u + 1 == u_end) open = false;
         cursor_next(a, R, C);
         }
@@ -1486,9 +1589,12 @@ void decode_split_kernel(DecodeArgs a) {
             wait_vm_steps(issued - i - 2);
             if constexpr (APPEND) {
                 if (C.r == C.rp.rn)
-                    append_new_token<BITS>(a, R, C, kvring + snxt * kKvBytes, smem + snxt * kStageBytes, lane);
+                    append_new_token<BITS>(a, R, C, kvring + snxt * kKvBytes, smem + snxt * SB, lane);
             }
-            r = read_stage<GP, BITS, KG>(a, smem + snxt * kStageBytes, L, C.r < C.rp.n4);
+            cpair = pairable<GP, BITS, KG, APPEND>(C, u_end);
+            r = read_stage<GP, BITS, KG>(a, smem + snxt * SB, L, C.r < C.rp.n4);
+            if (PAIR && cpair)
+                r1 = read_stage<GP, BITS, KG>(a, smem + snxt * SB + kPairHalf, L, true, kPairParams - kPairHalf);
             if (!open) qr = read_query<GP>(qring + snxt * QRing<GP>::kBytes, lane);
         }
         // producer: step P into the slot this iteration's step was read from
@@ -1498,14 +1604,25 @@ void decode_split_kernel(DecodeArgs a) {
             if constexpr (APPEND) {
                 if (P.r == P.rp.rn) issue_new_token(a, R, P, kvring + scur * kKvBytes, lane);
             }
-            issue_step<BITS, KG>(a, P, look, smem + scur * kStageBytes, offK, offV, offP4, offP8, lane);
+            if (PAIR && ppair) {
+                issue_pair2(a, P, look, look1, smem + scur * SB, offP4, lane);
+                ++P.u;
+                ++P.r;
+            } else {
+                issue_step<BITS, KG>(a, P, look, smem + scur * SB, offK, offV, offP4, offP8, lane);
+            }
             cursor_next(a, R, P);
             ++issued;
             advance_half(P);
-            if (P.u < u_end) look = read_pages(P);
+            if (P.u < u_end) {
+                ppair = pairable<GP, BITS, KG, APPEND>(P, u_end);
+                look = read_pages(P, 0);
+                if (PAIR && ppair) look1 = read_pages(P, 1);
+            }
         }
         wait_lgkm0();
         look = uniform(look);
+        if (PAIR) look1 = uniform(look1);
     }
     if constexpr (MEM) {
         // practically never true, but not provably so: the reads stay
@@ -1808,7 +1925,7 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
 
 template <int GP, bool APPEND, int BITS, bool MEM = false, bool KG = false>
 static void launch_split(const DecodeArgs &a, int grid, hipStream_t stream) {
-    constexpr int NW = kSplitWG<GP, APPEND>;
+    constexpr int NW = kSplitWG<GP, APPEND, BITS, KG>;
     hipLaunchKernelGGL((decode_split_kernel<GP, APPEND, BITS, MEM, KG>), dim3(grid / NW), dim3(64 * NW), 0, stream, a);
 }
 
@@ -1819,7 +1936,7 @@ struct SplitFn {
 
 template <int GP, bool APPEND, int BITS, bool KG = false>
 static SplitFn split_fn() {
-    return {reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS, false, KG>), kSplitWG<GP, APPEND>};
+    return {reinterpret_cast<const void *>(&decode_split_kernel<GP, APPEND, BITS, false, KG>), kSplitWG<GP, APPEND, BITS, KG>};
 }
 
 static int group_class(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
