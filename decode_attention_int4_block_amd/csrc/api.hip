@@ -469,7 +469,8 @@ kvq_status kv_prefill_attn(const kvq_cache *c, const uint16_t *q, int32_t num_q_
     a.inv_sqrt_h = inv_sqrt(c->had_block);
     a.out = out;
     a.lse = lse;
-    const int64_t tiles = ((int64_t)max_rows + a.R - 1) / a.R;
+    const int64_t rows_per_wave = (int64_t)a.R * kvq::prefill_tiles(a.bits);
+    const int64_t tiles = ((int64_t)max_rows + rows_per_wave - 1) / rows_per_wave;
     if (tiles > 0x7FFFFFFF) return fail(KVQ_ERR_SHAPE, "max_rows too large");
     hipError_t e = kvq::launch_prefill(a, (int)tiles, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));

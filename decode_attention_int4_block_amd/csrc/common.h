@@ -276,10 +276,15 @@ struct DecodeArgs {
     float *lse;
 };
 
+// Query tiles of 16 columns per prefill wave: two share each step's unpacked
+// codes for the 4-bit cache; the 3- and 2-bit operand builders leave no
+// registers for a second tile (it spilled 156-176 B per lane).
+__host__ __device__ constexpr int prefill_tiles(int bits) { return bits == 4 ? 2 : 1; }
+
 // Causal multi-row attention over the quantized cache (prefill).
 struct PrefillArgs {
     const uint16_t *q;          // [N][Hq][128] bf16 query rows
-    int32_t Hq, g, R;           // query heads, group size, rows per tile (R g <= 16)
+    int32_t Hq, g, R;           // query heads, group size, rows per 16-column tile (R g <= 16)
     const int32_t *q_start;     // [B + 1] first query row of each sequence
     const int32_t *slot;
     const int32_t *block_table;

@@ -9,19 +9,21 @@
 // cache holds it at length L -- the INT8 side cache for the sinks and the last
 // w positions, the INT4 pages elsewhere.  The last row is decode attention.
 //
-// Work: one wave per (sequence, KV head, tile of R rows), R = floor(16 / g), so
-// that the tile's (row, query head) pairs fill the 16 columns of
-// v_mfma_f32_16x16x32_f16.  The wave streams the tile's causal prefix through
-// the same 3-stage LDS ring of 5-load steps as the decode kernel (INT4 steps of
-// 32 positions, INT8 steps of 16 ring entries) and per step computes
+// Work: one wave per (sequence, KV head, prefill_tiles(bits) tiles of R rows), R =
+// floor(16 / g), so that a tile's (row, query head) pairs fill the 16 columns
+// of v_mfma_f32_16x16x32_f16.  The wave streams its rows' causal prefix
+// through the same 3-stage LDS ring of 5-load steps as the decode kernel (INT4
+// steps of 32 positions, INT8 steps of 16 ring entries) and per step computes,
+// for each tile,
 //   S[tok][col] = codes[tok][:] . Q[:][col]          A = codes, B = query
 //   O[col][dim] += P[col][tok] * vcodes[tok][dim]    A = p * s_v, B = codes
-// with the query and p * s_v each split into f16 hi + lo (separate MFMAs, all
-// 16 columns being in use).  The first product leaves lane (G, n) with column
-// n's scores of tokens 4G..4G+3 of both 16-token halves of the step -- exactly
-// the k slots the value layout gives that lane in the second product -- so p
-// never crosses lanes.  Softmax statistics are per column, kept identical in
-// the four lanes of a column.
+// with the query and p * s_v each split into f16 hi + lo of the same scale
+// (separate MFMAs into one fp32 accumulator, all 16 columns being in use).
+// The code operands are unpacked once per step for all tiles.  The first
+// product leaves lane (G, n) with column n's scores of tokens 4G..4G+3 of both
+// 16-token halves of the step -- exactly the k slots the value layout gives
+// that lane in the second product -- so p never crosses lanes.  Softmax
+// statistics are per column, kept identical in the four lanes of a column.
 #include <hip/hip_fp16.h>
 
 #include "common.h"
@@ -32,8 +34,19 @@ namespace kvq {
 
 namespace {
 
-constexpr float kTau = 8.0f;            // lazy max: p <= 2^kTau
-constexpr float kHiScale = 256.0f;      // hi part of p * s_v holds pv / 256
+// Running max raised whenever a step's max exceeds it, so p <= 1 and p * s_v
+// stays inside the f16 range (s_v itself is an fp16 value): the hi and lo
+// parts of p * s_v can then both be at the unit scale and accumulate in one
+// fp32 accumulator per tile, lo keeping absolute steps of 2^-24.
+constexpr float kTau = 0.0f;
+
+// hi = f16(a, b), lo = f16(a - hi, b - hi): hi + lo carries ~22 bits of a, b.
+__device__ inline void split_unit(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = f16x2(a, b);
+    uint32_t h = hi;
+    __asm__("" : "+v"(h));
+    lo = f16x2(a - h_lo(h), b - h_hi(h));
+}
 
 // Position held by ring entry e at length L (e < min(L, s + w)): a sink, or the
 // position of the recent window [max(s, L - w), L) that maps to e.
@@ -126,74 +139,89 @@ __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &r
 template <int BITS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
+    constexpr int NT = prefill_tiles(BITS);
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x;
     const int b = blockIdx.z, hk = blockIdx.y;
     const int row0 = ldc(a.q_start, b);
     const int T = ldc(a.q_start, b + 1) - row0;
-    // tiles in reverse order: the longest causal prefixes are dispatched first
-    const int tile = (int)(gridDim.x - 1 - blockIdx.x);
-    const int t0 = tile * a.R;
+    // waves in reverse order: the longest causal prefixes are dispatched first
+    const int wv = (int)(gridDim.x - 1 - blockIdx.x);
+    const int t0 = wv * a.R * NT;               // the wave's first row
     if (t0 >= T) return;
     const int L = ldc(a.ctx_len, b);
     const int slot = ldc(a.slot, b);
-    const int nrow = min(a.R, T - t0);
-    const int pos0 = L - T + t0;                // position of the tile's first row
+    const int nrow = min(a.R * NT, T - t0);
+    const int pos0 = L - T + t0;                // position of the wave's first row
     const int pmax = pos0 + nrow - 1;           // and of its last
 
-    // This lane's column n = (row n / g, head n % g); columns past the tile's
-    // rows repeat column 0 and are never stored.
+    // Tile k holds rows t0 + k R .. ; this lane's column n of tile k is (row
+    // n / g, head n % g).  Columns past a tile's rows repeat the tile's column
+    // 0 (a tile without rows: the wave's first column) and are never stored.
     const int G = lane >> 4, n = lane & 15;
-    const int ncol = nrow * a.g;
-    const int cn = n < ncol ? n : 0;
-    const int crow = cn / a.g, chead = cn % a.g;
-    const int cpos = pos0 + crow;               // causal bound of the column
+    int ncol[NT], crow[NT], chead[NT], cpos[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int nr = min(max(nrow - k * a.R, 0), a.R);
+        ncol[k] = nr * a.g;
+        const int cn = n < ncol[k] ? n : 0;
+        crow[k] = nr > 0 ? k * a.R + cn / a.g : 0;     // row within the wave
+        chead[k] = cn % a.g;
+        cpos[k] = pos0 + crow[k];               // causal bound of the column
+    }
 
-    // ---- query of the column: dims 32 G .. 32 G + 31, rotated (SAW-INT4,
+    // ---- queries of the columns: dims 32 G .. 32 G + 31, rotated (SAW-INT4,
     // section 2, block-diagonal Hadamard; strides below 32 in the lane, 32 and
-    // 64 across lanes G ^ 1, G ^ 2), scaled by 2^e, split into f16 hi + lo
-    half8 qh[4], ql[4];
-    float K1, Rh;
+    // 64 across lanes G ^ 1, G ^ 2), scaled by one power of two 2^e for the
+    // wave, split into f16 hi + lo of the same scale
+    half8 qh[NT][4], ql[NT][4];
+    float Rh[NT];
+    float K1;
     {
-        const uint16_t *qp = a.q + ((int64_t)(row0 + t0 + crow) * a.Hq + (int64_t)hk * a.g + chead) * kHeadDim + 32 * G;
-        float x[32];
+        float x[NT][32];
+        float sum[NT], amax = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const u32x4 wv = ldg<u32x4>(qp + 8 * v);
+        for (int k = 0; k < NT; ++k) {
+            const uint16_t *qp =
+                a.q + ((int64_t)(row0 + t0 + crow[k]) * a.Hq + (int64_t)hk * a.g + chead[k]) * kHeadDim + 32 * G;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[8 * v + 2 * e] = bf16f(wv[e] & 0xFFFFu);
-                x[8 * v + 2 * e + 1] = bf16f(wv[e] >> 16);
+            for (int v = 0; v < 4; ++v) {
+                const u32x4 wq = ldg<u32x4>(qp + 8 * v);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[k][8 * v + 2 * e] = bf16f(wq[e] & 0xFFFFu);
+                    x[k][8 * v + 2 * e + 1] = bf16f(wq[e] >> 16);
+                }
             }
-        }
 #pragma unroll
-        for (int len = 1; len < 32; len <<= 1) {
-            if (len < a.h) {
+            for (int len = 1; len < 32; len <<= 1) {
+                if (len < a.h) {
 #pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    if ((i & len) == 0) {
-                        const float u = x[i], v = x[i + len];
-                        x[i] = u + v;
-                        x[i + len] = u - v;
+                    for (int i = 0; i < 32; ++i) {
+                        if ((i & len) == 0) {
+                            const float u = x[k][i], v = x[k][i + len];
+                            x[k][i] = u + v;
+                            x[k][i + len] = u - v;
+                        }
                     }
                 }
             }
-        }
-        if (32 < a.h) {
+            if (32 < a.h) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) x[i] = butterfly<16>(x[i], lane);
-        }
-        if (64 < a.h) {
+                for (int i = 0; i < 32; ++i) x[k][i] = butterfly<16>(x[k][i], lane);
+            }
+            if (64 < a.h) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) x[i] = butterfly<32>(x[i], lane);
-        }
-        float sum = 0.0f, amax = 0.0f;
+                for (int i = 0; i < 32; ++i) x[k][i] = butterfly<32>(x[k][i], lane);
+            }
+            float sm = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            sum += x[i];
-            amax = fmaxf(amax, fabsf(x[i]));
+            for (int i = 0; i < 32; ++i) {
+                sm += x[k][i];
+                amax = fmaxf(amax, fabsf(x[k][i]));
+            }
+            sum[k] = sum_rows(sm) * a.inv_sqrt_h;   // the column's four lanes
         }
-        sum = sum_rows(sum) * a.inv_sqrt_h;          // the column's four lanes
         amax = wave_max(amax) * a.inv_sqrt_h;
         int E = 0;
         (void)frexpf(amax, &E);
@@ -201,22 +229,25 @@ void prefill_kernel(PrefillArgs a) {
         const float sc = a.inv_sqrt_h * ldexpf(1.0f, e);
         const float s16 = sc * 0.0625f;
         K1 = ldexpf(kLog2e * 0.08838834764831845f, 24 - e);   // log2(e) / sqrt(128), undoing 2^(e - 24)
-        Rh = ldexpf(sum, e - 24);
-        // chunks of 8 dims in the nibble order of a code dword: dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float *y = x + 8 * k;
-            uint32_t H[4], Lo[4];
-            split2<1>(y[0] * sc, y[4] * sc, H[0], Lo[0]);
-            split2<1>(y[1] * s16, y[5] * s16, H[1], Lo[1]);
-            split2<1>(y[2] * sc, y[6] * sc, H[2], Lo[2]);
-            split2<1>(y[3] * s16, y[7] * s16, H[3], Lo[3]);
-            qh[k] = pack8(H[0], H[1], H[2], H[3]);
-            ql[k] = pack8(Lo[0], Lo[1], Lo[2], Lo[3]);
+        for (int k = 0; k < NT; ++k) {
+            Rh[k] = ldexpf(sum[k], e - 24);
+            // chunks of 8 dims in the nibble order of a code dword: dims 0,4 | 1,5 (/16) | 2,6 | 3,7 (/16)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float *y = x[k] + 8 * c;
+                uint32_t H[4], Lo[4];
+                split2<1>(y[0] * sc, y[4] * sc, H[0], Lo[0]);
+                split2<1>(y[1] * s16, y[5] * s16, H[1], Lo[1]);
+                split2<1>(y[2] * sc, y[6] * sc, H[2], Lo[2]);
+                split2<1>(y[3] * s16, y[7] * s16, H[3], Lo[3]);
+                qh[k][c] = pack8(H[0], H[1], H[2], H[3]);
+                ql[k][c] = pack8(Lo[0], Lo[1], Lo[2], Lo[3]);
+            }
         }
     }
 
-    // ---- the tile's steps: INT4 steps up to its last row, then INT8 subblocks
+    // ---- the wave's steps: INT4 steps up to its last row, then INT8 subblocks
     const RowPlan rp = row_plan(L, a.s, a.w);
     const int lim4 = min(rp.hi4, pmax + 1);
     const int n4 = lim4 > rp.lo4 ? ((lim4 + 31) >> 5) - rp.k0 : 0;
@@ -241,10 +272,20 @@ void prefill_kernel(PrefillArgs a) {
     StepPages next = step_pages(a, rp, n4, slot, kStages);    // pages of the producer's next step
 
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 Oh[8], Ol[8];                       // O[col 4G + i][16 t + n], hi (x 256) and lo parts
+    // O[k][t]: tile k, row 4 G + i = column 4 G + i, dims 16 t + n; the hi and lo
+    // parts of p s_v accumulate together
+    floatx4 O[NT][8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) Oh[t] = Ol[t] = zero4;
-    float mK = kNegInf, lsum = 0.0f, zsum = 0.0f;
+    for (int k = 0; k < NT; ++k)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) O[k][t] = zero4;
+    float mK[NT], lsum[NT], zsum[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        mK[k] = kNegInf;
+        lsum[k] = 0.0f;
+        zsum[k] = 0.0f;
+    }
 
     for (int i = 0; i < nsteps; ++i) {
         wait_vm_steps(issued - i - 1);
@@ -285,53 +326,61 @@ void prefill_kernel(PrefillArgs a) {
         const bool int8 = i >= n4;
 
         // scores of tokens 4G + j (A half) and 16 + 4G + j (B half) for column n
-        floatx4 hA = zero4, lA = zero4, hB = zero4, lB = zero4;
-        if (main2) {
-            // chunk c: dword c / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
+        // of each tile; the key codes are unpacked once for both tiles
+        floatx4 sA[NT], sB[NT];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+        for (int k = 0; k < NT; ++k) sA[k] = sB[k] = zero4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            half8 ak, bk;
+            if (main2) {
+                // chunk c: dword c / 2 of the lane's 8 bytes, bytes (0, 2) or (1, 3)
                 const uint32_t xa = kA[c >> 1] >> (8 * (c & 1)), xb = kB[c >> 1] >> (8 * (c & 1));
-                const half8 ak = BITS == 3 ? int3_key_chunk(xa, kA[2], c) : int2_chunk(xa);
-                const half8 bk = BITS == 3 ? int3_key_chunk(xb, kB[2], c) : int2_chunk(xb);
-                hA = mfma16(ak, qh[c], hA);
-                lA = mfma16(ak, ql[c], lA);
-                hB = mfma16(bk, qh[c], hB);
-                lB = mfma16(bk, ql[c], lB);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
+                ak = BITS == 3 ? int3_key_chunk(xa, kA[2], c) : int2_chunk(xa);
+                bk = BITS == 3 ? int3_key_chunk(xb, kB[2], c) : int2_chunk(xb);
+            } else {
                 const uint32_t x = kA[c], x8 = x >> 8;
-                const half8 ak = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
+                ak = pack8(x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u);
                 const uint32_t y = kB[c], y8 = y >> 8;
-                const half8 bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
-                hA = mfma16(ak, qh[c], hA);
-                lA = mfma16(ak, ql[c], lA);
-                hB = mfma16(bk, qh[c], hB);
-                lB = mfma16(bk, ql[c], lB);
+                bk = pack8(y & 0x000F000Fu, y & 0x00F000F0u, y8 & 0x000F000Fu, y8 & 0x00F000F0u);
+            }
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                sA[k] = mfma16(ak, qh[k][c], sA[k]);
+                sB[k] = mfma16(bk, qh[k][c], sB[k]);
+                sA[k] = mfma16(ak, ql[k][c], sA[k]);
+                sB[k] = mfma16(bk, ql[k][c], sB[k]);
             }
         }
-        float t[8];
-        uint32_t vp[8];
-        {
-            const floatx4 sB = hB + lB;
-            floatx4 sA = hA + lA;
+        const int base = int8 ? 16 * (i - n4) : (rp.k0 + i) * 32;
+        // an INT4 step inside the region and at or before the wave's first row
+        // is valid for every column: no per-position tests
+        const bool full = !int8 && base >= rp.lo4 && base + 32 <= min(rp.hi4, pos0 + 1);
+        // value (scale, zero) of the step's tokens (shared by the columns)
+        uint32_t vpr[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            vpr[j] = vpA[j];
+            vpr[4 + j] = int8 ? 0u : vpB[j];
+        }
+        half8 ph[NT], pl[NT];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            float t[8];
+            uint32_t vp[8];
+            floatx4 a4 = sA[k];
             if (int8) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sA[j] = fmaf(sB[j], 16.0f, sA[j]);   // high-nibble plane
+                for (int j = 0; j < 4; ++j) a4[j] = fmaf(sB[k][j], 16.0f, a4[j]);   // high-nibble plane
             }
-            const int base = int8 ? 16 * (i - n4) : (rp.k0 + i) * 32;
-            // an INT4 step inside the region and at or before the tile's first
-            // row is valid for every column: no per-position tests
-            const bool full = !int8 && base >= rp.lo4 && base + 32 <= min(rp.hi4, pos0 + 1);
             if (full) {
                 // the common step: one wave-uniform branch, no per-position selects
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    t[j] = fmaf(sA[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh);
-                    t[4 + j] = fmaf(sB[j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh);
-                    vp[j] = vpA[j];
-                    vp[4 + j] = vpB[j];
+                    t[j] = fmaf(a4[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh[k]);
+                    t[4 + j] = fmaf(sB[k][j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh[k]);
+                    vp[j] = vpr[j];
+                    vp[4 + j] = vpr[4 + j];
                 }
             } else {
 #pragma unroll
@@ -339,70 +388,69 @@ void prefill_kernel(PrefillArgs a) {
                     bool okA, okB;
                     if (int8) {
                         const int e = base + 4 * G + j;
-                        okA = e < rp.n8e && ring_position(e, L, a.s, a.w) <= cpos;
+                        okA = e < rp.n8e && ring_position(e, L, a.s, a.w) <= cpos[k];
                         okB = false;
                     } else {
                         const int pA = base + 4 * G + j, pB = pA + 16;
-                        okA = pA >= rp.lo4 && pA < rp.hi4 && pA <= cpos;
-                        okB = pB >= rp.lo4 && pB < rp.hi4 && pB <= cpos;
+                        okA = pA >= rp.lo4 && pA < rp.hi4 && pA <= cpos[k];
+                        okB = pB >= rp.lo4 && pB < rp.hi4 && pB <= cpos[k];
                     }
                     // params of positions outside the context may be arbitrary bytes
                     // (NaN as fp16): dropped by a select, never multiplied by zero
-                    const float tA = fmaf(sA[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh);
-                    const float tB = fmaf(sB[j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh);
+                    const float tA = fmaf(a4[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh[k]);
+                    const float tB = fmaf(sB[k][j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh[k]);
                     t[j] = okA ? tA : kNegInf;
                     t[4 + j] = okB ? tB : kNegInf;
-                    vp[j] = okA ? vpA[j] : 0u;
-                    vp[4 + j] = okB ? vpB[j] : 0u;
+                    vp[j] = okA ? vpr[j] : 0u;
+                    vp[4 + j] = okB ? vpr[4 + j] : 0u;
                 }
             }
-        }
 
-        // online softmax of the column (lazy max)
-        float ml = t[0];
+            // online softmax of the column
+            float ml = t[0];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) ml = fmaxf(ml, t[j]);
-        if (__any(ml * K1 > mK + kTau)) {
-            const float mt = max_rows(ml) * K1;
-            const bool grow = mt > mK + kTau;
-            const float mnew = grow ? mt : mK;
-            const float alpha = mK == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mK - mnew);
-            lsum *= alpha;
-            zsum *= alpha;
-            mK = mnew;
-            // accumulator row i of this lane is column 4 G + i
+            for (int j = 1; j < 8; ++j) ml = fmaxf(ml, t[j]);
+            if (__any(ml * K1 > mK[k] + kTau)) {
+                const float mt = max_rows(ml) * K1;
+                const bool grow = mt > mK[k] + kTau;
+                const float mnew = grow ? mt : mK[k];
+                const float alpha = mK[k] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mK[k] - mnew);
+                lsum[k] *= alpha;
+                zsum[k] *= alpha;
+                mK[k] = mnew;
+                // accumulator row r of this lane is column 4 G + r
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * G + r, 64);
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * G + r, 64);
 #pragma unroll
-                for (int tt = 0; tt < 8; ++tt) {
-                    Oh[tt][r] *= ar;
-                    Ol[tt][r] *= ar;
+                    for (int tt = 0; tt < 8; ++tt) O[k][tt][r] *= ar;
                 }
             }
-        }
-        // a column with no valid position yet keeps mK = -inf: its p are exp2(-inf) = 0
-        const float nm = mK == kNegInf ? 0.0f : -mK;
-        float pv[8];
+            // a column with no valid position yet keeps mK = -inf: its p are exp2(-inf) = 0
+            const float nm = mK[k] == kNegInf ? 0.0f : -mK[k];
+            float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(t[j], K1, nm));
-            lsum += p;
-            zsum = fmaf(p, h_hi(vp[j]), zsum);
-            pv[j] = p * h_lo(vp[j]);
-        }
-        if (int8) {
-            // the B half of the step is the high-nibble plane of the same entries
+            for (int j = 0; j < 8; ++j) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(t[j], K1, nm));
+                lsum[k] += p;
+                zsum[k] = fmaf(p, h_hi(vp[j]), zsum[k]);
+                pv[j] = p * h_lo(vp[j]);
+            }
+            if (int8) {
+                // the B half of the step is the high-nibble plane of the same entries
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pv[4 + j] = 16.0f * pv[j];
+                for (int j = 0; j < 4; ++j) pv[4 + j] = 16.0f * pv[j];
+            }
+            // A operand in the value layout's k order: A0 A2 A1 A3 | B0 B2 B1 B3
+            uint32_t H0, H1, H2, H3, L0, L1, L2, L3;
+            split_unit(pv[0], pv[2], H0, L0);
+            split_unit(pv[1], pv[3], H1, L1);
+            split_unit(pv[4], pv[6], H2, L2);
+            split_unit(pv[5], pv[7], H3, L3);
+            ph[k] = pack8(H0, H1, H2, H3);
+            pl[k] = pack8(L0, L1, L2, L3);
         }
-        // A operand in the value layout's k order: A0 A2 A1 A3 | B0 B2 B1 B3
-        uint32_t H0, H1, H2, H3, L0, L1, L2, L3;
-        split2<256>(pv[0], pv[2], H0, L0);
-        split2<256>(pv[1], pv[3], H1, L1);
-        split2<256>(pv[4], pv[6], H2, L2);
-        split2<256>(pv[5], pv[7], H3, L3);
-        const half8 ph = pack8(H0, H1, H2, H3), pl = pack8(L0, L1, L2, L3);
+        // value tiles, unpacked once for both query tiles
         if (main2) {
             // dword cc, field f: dims 16 (4 cc + f) + n, tile 4 cc + f (odd tiles
             // scaled by 16 as the 4-bit ones)
@@ -415,8 +463,11 @@ void prefill_kernel(PrefillArgs a) {
                         ? pack8(int3_value_field(x, vA[2], cc, f, false), int3_value_field(x8, vA[2], cc, f, true),
                                 int3_value_field(y, vB[2], cc, f, false), int3_value_field(y8, vB[2], cc, f, true))
                         : pack8(int2_field(x, f), int2_field(x8, f), int2_field(y, f), int2_field(y8, f));
-                    Oh[4 * cc + f] = mfma16(ph, vt, Oh[4 * cc + f]);
-                    Ol[4 * cc + f] = mfma16(pl, vt, Ol[4 * cc + f]);
+#pragma unroll
+                    for (int k = 0; k < NT; ++k) {
+                        O[k][4 * cc + f] = mfma16(ph[k], vt, O[k][4 * cc + f]);
+                        O[k][4 * cc + f] = mfma16(pl[k], vt, O[k][4 * cc + f]);
+                    }
                 }
             }
         } else {
@@ -425,35 +476,41 @@ void prefill_kernel(PrefillArgs a) {
                 const uint32_t x = vA[c], x8 = x >> 8, y = vB[c], y8 = y >> 8;
                 const half8 ve = pack8(x & 0x000F000Fu, x8 & 0x000F000Fu, y & 0x000F000Fu, y8 & 0x000F000Fu);
                 const half8 vo = pack8(x & 0x00F000F0u, x8 & 0x00F000F0u, y & 0x00F000F0u, y8 & 0x00F000F0u);
-                Oh[2 * c] = mfma16(ph, ve, Oh[2 * c]);
-                Ol[2 * c] = mfma16(pl, ve, Ol[2 * c]);
-                Oh[2 * c + 1] = mfma16(ph, vo, Oh[2 * c + 1]);
-                Ol[2 * c + 1] = mfma16(pl, vo, Ol[2 * c + 1]);
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    O[k][2 * c] = mfma16(ph[k], ve, O[k][2 * c]);
+                    O[k][2 * c] = mfma16(pl[k], ve, O[k][2 * c]);
+                    O[k][2 * c + 1] = mfma16(ph[k], vo, O[k][2 * c + 1]);
+                    O[k][2 * c + 1] = mfma16(pl[k], vo, O[k][2 * c + 1]);
+                }
             }
         }
     }
 
     // ---- output: out = (sum p s_v c_v + sum p z_v) / sum p per column
-    lsum = sum_rows(lsum);
-    zsum = sum_rows(zsum);
-    const float rl = 1.0f / lsum;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int col = 4 * G + r;
-        const float ir = __shfl(rl, col, 64);
-        const float zr = __shfl(zsum, col, 64);
-        if (col < ncol) {
-            const int rr = col / a.g, hd = col % a.g;
-            float *o = a.out + ((int64_t)(row0 + t0 + rr) * a.Hq + (int64_t)hk * a.g + hd) * kHeadDim;
+    for (int k = 0; k < NT; ++k) {
+        const float ls = sum_rows(lsum[k]);
+        const float zs = sum_rows(zsum[k]);
+        const float rl = 1.0f / ls;
 #pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                const float sc = (tt & 1) ? 1048576.0f : 16777216.0f;   // 2^20 / 2^24 code scaling
-                o[16 * tt + n] = fmaf(fmaf(Oh[tt][r], kHiScale, Ol[tt][r]), sc, zr) * ir;
+        for (int r = 0; r < 4; ++r) {
+            const int col = 4 * G + r;
+            const float ir = __shfl(rl, col, 64);
+            const float zr = __shfl(zs, col, 64);
+            if (col < ncol[k]) {
+                const int rr = k * a.R + col / a.g, hd = col % a.g;
+                float *o = a.out + ((int64_t)(row0 + t0 + rr) * a.Hq + (int64_t)hk * a.g + hd) * kHeadDim;
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) {
+                    const float sc = (tt & 1) ? 1048576.0f : 16777216.0f;   // 2^20 / 2^24 code scaling
+                    o[16 * tt + n] = fmaf(O[k][tt][r], sc, zr) * ir;
+                }
             }
         }
+        if (a.lse && G == 0 && n < ncol[k])
+            a.lse[(int64_t)(row0 + t0 + crow[k]) * a.Hq + (int64_t)hk * a.g + chead[k]] = (mK[k] + __log2f(ls)) / kLog2e;
     }
-    if (a.lse && G == 0 && n < ncol)
-        a.lse[(int64_t)(row0 + t0 + crow) * a.Hq + (int64_t)hk * a.g + chead] = (mK + __log2f(lsum)) / kLog2e;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, int tiles, hipStream_t stream) {
