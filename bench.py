@@ -509,6 +509,16 @@ def prefill_cpu_baseline(wl, q, T, budget_s=6.0):
                        f"took another {t_quant:.1f} s)")
 
 
+def prefill_sub4bit(torch, steps, warmup):
+    """The same re-prefill over the 3- and 2-bit main caches."""
+    out = []
+    for bits in (3, 2):
+        px = measure_prefill(torch, steps=steps, warmup=warmup, code_bits=bits)
+        out.append({k: px[k] for k in ("code_bits", "us_mean", "us_p10_p90", "algorithmic_flops", "kv_bytes_unique")}
+                   | {"achieved_TFLOPs": px["roofline"]["achieved"], "frac_of_fp16_mfma_peak": px["roofline"]["frac"]})
+    return out
+
+
 def measure_prefill(torch, steps, warmup, cpu=False, code_bits=4):
     """kv_prefill_attn on the re-prefill workload: the last `chunk` positions of each
     sequence attended again as causal query rows over the quantized cache (main
@@ -611,8 +621,10 @@ def main():
     from workloads import build_workload, get_config
 
     if args.prefill_only:
-        print(json.dumps({"prefill": measure_prefill(torch, steps=args.steps, warmup=args.warmup, cpu=False)}),
-              flush=True)
+        pf = measure_prefill(torch, steps=args.steps, warmup=args.warmup, cpu=False)
+        if not args.no_sub4bit:
+            pf["sub4bit"] = prefill_sub4bit(torch, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"prefill": pf}), flush=True)
         return
 
     cfg = get_config(args.workload)
@@ -784,14 +796,7 @@ def main():
     if not args.no_prefill:
         rec["prefill"] = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2,
                                          cpu=not args.no_cpu_baseline)
-        # the same re-prefill over the 3- and 2-bit main caches
-        rec["prefill"]["sub4bit"] = []
-        for bits in (3, 2):
-            px = measure_prefill(torch, steps=max(5, min(args.steps, 20)), warmup=2, code_bits=bits)
-            rec["prefill"]["sub4bit"].append({k: px[k] for k in ("code_bits", "us_mean", "us_p10_p90",
-                                                                  "algorithmic_flops", "kv_bytes_unique")}
-                                             | {"achieved_TFLOPs": px["roofline"]["achieved"],
-                                                "frac_of_fp16_mfma_peak": px["roofline"]["frac"]})
+        rec["prefill"]["sub4bit"] = prefill_sub4bit(torch, steps=max(5, min(args.steps, 20)), warmup=2)
     if args.variants:
         del layers
         dw.cache = None

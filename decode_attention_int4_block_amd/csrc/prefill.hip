@@ -135,9 +135,14 @@ __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &r
 
 }  // namespace
 
+// Waves per SIMD: the two-tile 4-bit kernel needs ~250 registers (two waves);
+// the one-tile 3- and 2-bit kernels fit 168 (three waves).
+template <int BITS>
+constexpr int kPrefillWaves = prefill_tiles(BITS) == 2 ? 2 : 3;
+
 // BITS: width of the main cache's codes (4, 3 or 2; KV4-RL, "Future Directions").
 template <int BITS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWaves<BITS>, kPrefillWaves<BITS>)))
 void prefill_kernel(PrefillArgs a) {
     constexpr int NT = prefill_tiles(BITS);
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
