@@ -23,8 +23,7 @@ What it computes, and where each step comes from:
 
 Parity status of each function is listed in the module that defines it; every
 function here is pinned by tests under ``tests/`` against closed forms,
-library routines or brute force (none is "parity unpinned" except the error
-against unquantized attention, which is only reported).
+library routines or brute force; none is "parity unpinned".
 """
 
 from . import numerics, hadamard, quant, regions, attention, cache  # noqa: F401

@@ -287,3 +287,27 @@ def test_attend_equals_brute_force_composition(h):
     K, V = dequantized_kv(oc)
     ref = _brute(qt.tolist(), K.tolist(), V.tolist())
     assert np.abs(out - ref).max() < 1e-12
+
+
+def test_unquantized_attention_matches_torch_bf16_sdpa():
+    """Plain attention over the raw bf16 tensors: torch converts the bf16 tensors
+    itself (not the oracle's bit conversion) and runs fp64 SDPA with the grouped
+    heads repeated; a rotated or quantized path would move the result by far more."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, L, d = 8, 2, 257, 128
+    q = torch.from_numpy(rng.standard_normal((Hq, d)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy((rng.standard_normal((L, Hkv, d)) * 2).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((L, Hkv, d)).astype(np.float32)).to(torch.bfloat16)
+    out, lse = unquantized_attention(bf16_bits(q), bf16_bits(k), bf16_bits(v))
+    g = Hq // Hkv
+    tq = q.to(torch.float64)[:, None, :]
+    tk = k.to(torch.float64).permute(1, 0, 2).repeat_interleave(g, 0).contiguous()
+    tv = v.to(torch.float64).permute(1, 0, 2).repeat_interleave(g, 0).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[:, 0, :].numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    z = torch.einsum("hld,hd->hl", tk, tq[:, 0, :]) / math.sqrt(d)
+    assert np.allclose(lse, torch.logsumexp(z, dim=1).numpy(), rtol=0, atol=1e-12)
+    # the rotated query against unrotated keys is a different function
+    out_rot, _ = unquantized_attention(bf16_bits(torch.from_numpy(rotated_query(bf16_bits(q), 128))
+                                                 .to(torch.bfloat16)), bf16_bits(k), bf16_bits(v))
+    assert np.abs(out_rot - ref).max() > 1e-2
