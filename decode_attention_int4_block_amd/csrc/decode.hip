@@ -1643,15 +1643,14 @@ void decode_split_kernel(DecodeArgs a) {
 // workers share; also writes the rows with no context.
 //
 // Workgroups [0, B*H) take one segment each: rows without context, and
-// segments of at most kChunkPieces pieces, merged directly.  A longer segment
-// (a long row split over many workers) is folded in parallel by the helper
-// workgroups B*H + j, j = 0, 1, ...: helper j takes the pieces of workers
-// [j T, (j + 1) T), T = kChunkPieces, folds each long segment's share into a
-// chunk partial, and counts the folded pieces on the segment (an agent-scope
-// acquire-release add: the helpers run on different XCDs); the helper that
-// completes the count folds the chunk partials.  Pieces and chunks are folded in
-// worker order, so the result is the same whoever finishes last.  Each of these
-// folds is shared by the kCombWaves waves of the workgroup (block_fold_heads).
+// segments of at most kChunkPieces pieces, merged directly in worker order by
+// the kCombWaves waves of the workgroup (block_fold_heads).  A longer segment
+// (a long row split over many workers) is folded by the helper workgroups
+// B*H + h, kLongHelpers per chunk of kChunkPieces workers: the helpers whose
+// chunks hold pieces of the segment split its (query head, dim slice) tasks
+// among themselves, and each task reads all of the segment's pieces for its
+// slice in one pass (fold_long_task): a segment of up to 512 pieces costs a
+// task one round trip of piece loads.
 //
 // Lane l handles query heads l / 16 (g <= 4), or 8 k + l / 16 and 8 k + 4 +
 // l / 16, and dims 8 (l % 16) .. + 8 of a piece laid out as
@@ -1729,23 +1728,6 @@ __device__ inline void merge_write(const DecodeArgs &a, const MergeAcc &r, int b
     *reinterpret_cast<u32x4 *>(o) = w0;
     *reinterpret_cast<u32x4 *>(o + 4) = w1;
     if (a.lse && part == 0) a.lse[(int64_t)b * a.Hq + (int64_t)hk * a.g + j] = (r.M + __log2f(r.Ls)) / kLog2e;
-}
-
-// Raw fold (m, l, acc) of head j into a piece-shaped chunk partial.
-__device__ inline void merge_store(const MergeAcc &r, float *pp, int j, int part) {
-    float *ph = pp + j * kPieceStride;
-    if (part == 0) {
-        ph[0] = r.M;
-        ph[1] = r.Ls;
-    }
-    u32x4 w0, w1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        w0[e] = __float_as_uint(r.acc[e]);
-        w1[e] = __float_as_uint(r.acc[4 + e]);
-    }
-    *reinterpret_cast<u32x4 *>(ph + 4 + 8 * part) = w0;
-    *reinterpret_cast<u32x4 *>(ph + 8 + 8 * part) = w1;
 }
 
 __device__ inline int wave_min(int x) {
@@ -1832,9 +1814,111 @@ __device__ inline void block_fold_heads(int g, int wave, int lane, int part, int
     }
 }
 
+// Long segments.  A helper task is one query head j and one slice of the
+// output's dims; the workgroup's lanes are nq dim quads (4 dims each) times
+// 64 kCombWaves / nq piece slots, and each lane folds every slot-count-th
+// piece of the segment, kLongBatch pieces per round trip (their loads issue
+// together).  The lanes of a quad then merge in a fixed tree inside each wave
+// and the waves' partials in wave order through LDS, so the result does not
+// depend on timing.  Every piece of the segment is read once per slice, all
+// of a slice's round trips by one workgroup.
+constexpr int kLongBatch = 8;
+constexpr int kLongHelpers = 4;         // helper workgroups per chunk of kChunkPieces workers
+constexpr int kLongSlices = 8;          // dim slices per query head at most (16 dims each)
+
+struct Fold4 {
+    float M, Ls, acc[4];
+};
+
+struct LongShared {
+    Fold4 part[kCombWaves][32];         // per wave, per dim quad
+};
+
+__device__ inline void fold4_merge(Fold4 &r, const Fold4 &o) {
+    const float Mn = fmaxf(r.M, o.M);
+    if (Mn == kNegInf) return;
+    const float fr = r.M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(r.M - Mn);
+    const float fo = o.M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(o.M - Mn);
+    r.Ls = fmaf(r.Ls, fr, o.Ls * fo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.acc[e] = fmaf(r.acc[e], fr, o.acc[e] * fo);
+    r.M = Mn;
+}
+
+// Folds head j, dims [d0, d0 + 4 nq) of the n pieces at basep, basep +
+// piece_elems, ... and writes the normalized output (and lse).  Every wave of
+// the workgroup calls it with the same arguments (it holds barriers).
+__device__ inline void fold_long_task(const DecodeArgs &a, const float *basep, int64_t piece_elems, int n, int j,
+                                      int d0, int nq, int b, int hk, LongShared &sh) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int q = lane & (nq - 1);
+    const int nslots = 64 * kCombWaves / nq;
+    const int slot = (int)(threadIdx.x / nq);
+    const float *ph = basep + j * kPieceStride;
+    Fold4 r;
+    r.M = kNegInf;
+    r.Ls = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.acc[e] = 0.0f;
+    for (int k0 = slot; k0 < n; k0 += nslots * kLongBatch) {
+        float m[kLongBatch], l[kLongBatch];
+        u32x4 v[kLongBatch];
+        // branch-free: slots past the last piece re-read it and drop it
+#pragma unroll
+        for (int t = 0; t < kLongBatch; ++t) {
+            const int k = k0 + t * nslots;
+            const float *pp = ph + (int64_t)min(k, n - 1) * piece_elems;
+            const float2 ml = *reinterpret_cast<const float2 *>(pp);
+            m[t] = k < n ? ml.x : kNegInf;
+            l[t] = ml.y;
+            v[t] = ldg<u32x4>(pp + 4 + d0 + 4 * q);
+        }
+        float Mn = r.M;
+#pragma unroll
+        for (int t = 0; t < kLongBatch; ++t) Mn = fmaxf(Mn, m[t]);
+        if (Mn == kNegInf) continue;
+        const float fr = r.M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(r.M - Mn);
+        r.Ls *= fr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.acc[e] *= fr;
+#pragma unroll
+        for (int t = 0; t < kLongBatch; ++t) {
+            const float f = m[t] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m[t] - Mn);
+            r.Ls = fmaf(l[t], f, r.Ls);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r.acc[e] = fmaf(__uint_as_float(v[t][e]), f, r.acc[e]);
+        }
+        r.M = Mn;
+    }
+    // the slots of one quad inside the wave: lanes q, q + nq, ...
+    for (int o = nq; o < 64; o <<= 1) {
+        Fold4 x;
+        x.M = __shfl_xor(r.M, o, 64);
+        x.Ls = __shfl_xor(r.Ls, o, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x.acc[e] = __shfl_xor(r.acc[e], o, 64);
+        fold4_merge(r, x);
+    }
+    if (lane < nq) sh.part[wave][lane] = r;
+    __syncthreads();
+    if (wave == 0 && lane < nq) {
+        for (int w = 1; w < kCombWaves; ++w) fold4_merge(r, sh.part[w][lane]);
+        const int64_t hq = (int64_t)b * a.Hq + (int64_t)hk * a.g + j;
+        const float inv = 1.0f / r.Ls;
+        u32x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = __float_as_uint(r.acc[e] * inv);
+        *reinterpret_cast<u32x4 *>(a.out + hq * kHeadDim + d0 + 4 * q) = o4;
+        if (a.lse && d0 == 0 && lane == 0) a.lse[hq] = (r.M + __log2f(r.Ls)) / kLog2e;
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeArgs a) {
     constexpr int T = kChunkPieces;
     __shared__ CombShared sh;
+    __shared__ LongShared lsh;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = a.g;
@@ -1863,11 +1947,13 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
                          [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); }, sh);
         return;
     }
-    // helper: the pieces of workers [w0, w0 + T).  The worker count and the
+    // helper h of the chunk of workers [w0, w0 + T): the worker count and the
     // workers' segment records load in one round trip (the records array holds
     // the whole grid's; those of workers >= W are dropped afterwards), the
     // records' segment bounds in a second.
-    const int64_t jc = (int64_t)blockIdx.x - nseg;
+    const int64_t hix = (int64_t)blockIdx.x - nseg;
+    const int64_t jc = hix / kLongHelpers;
+    const int hm = (int)(hix - jc * kLongHelpers);
     const int64_t w0 = jc * T;
     const bool mine = lane < 2 * T && w0 + lane / 2 < a.max_workers;
     int v = mine ? a.ws_wseg[2 * w0 + lane] : -1;
@@ -1893,33 +1979,17 @@ __global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(DecodeA
         const int64_t wf = __builtin_amdgcn_readlane(vf, src), wl = __builtin_amdgcn_readlane(vl, src);
         const int n = (int)(wl - wf + 1);
         const int b = s / a.H, hk = s % a.H;
-        const int64_t wa = w0 > wf ? w0 : wf;
-        const int64_t wb = (w0 + T - 1 < wl ? w0 + T - 1 : wl);
-        const float *basep = a.ws_piece + (wa + s) * piece_elems;
-        float *chunk = a.ws_l2 + (jc + s) * piece_elems;
-        block_fold_heads(g, wave, lane, part, (int)(wb - wa + 1), [&](int k) { return basep + k * piece_elems; },
-                         [&](const MergeAcc &r, int j) { merge_store(r, chunk, j, part); }, sh);
-        // wave 0 stored the chunk partial; its release-acquire add publishes it
-        // and finds whether this helper completes the segment
-        if (wave == 0) {
-            int before = 0;
-            if (lane == 0)
-                before = __hip_atomic_fetch_add(a.ws_count + s, (int)(wb - wa + 1), __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-            before = uni(before);
-            if (lane == 0) sh.before = before;
-        }
-        __syncthreads();
-        const int before = sh.before;
-        __syncthreads();
-        if (before + (int)(wb - wa + 1) != n) continue;
-        // the last helper of the segment folds its chunk partials (written by
-        // helpers on other XCDs): every wave acquires before reading them
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // every helper of the chunks [wf / T, wl / T] finds this segment; they
+        // share its tasks (query head, dim slice) round robin, with slices as
+        // narrow as the helper count allows
         const int64_t jf = wf / T, jl = wl / T;
-        const float *c0 = a.ws_l2 + (jf + s) * piece_elems;
-        block_fold_heads(g, wave, lane, part, (int)(jl - jf + 1), [&](int k) { return c0 + k * piece_elems; },
-                         [&](const MergeAcc &r, int j) { merge_write(a, r, b, hk, j, part); }, sh);
+        const int nh = (int)((jl - jf + 1) * kLongHelpers);
+        const int rank = (int)((jc - jf) * kLongHelpers + hm);
+        int nc = kLongSlices;
+        while (nc > 1 && g * nc > nh) nc >>= 1;
+        const float *basep = a.ws_piece + (wf + s) * piece_elems;
+        for (int t = rank; t < g * nc; t += nh)
+            fold_long_task(a, basep, piece_elems, n, t / nc, (t % nc) * (kHeadDim / nc), 32 / nc, b, hk, lsh);
     }
 }
 
@@ -1986,7 +2056,7 @@ hipError_t launch_decode(const DecodeArgs &a, int grid, hipStream_t stream, bool
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int helpers = (grid + kChunkPieces - 1) / kChunkPieces;
+    const int helpers = (grid + kChunkPieces - 1) / kChunkPieces * kLongHelpers;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H + helpers), dim3(64 * kCombWaves), 0, stream, a);
     return hipGetLastError();
 }

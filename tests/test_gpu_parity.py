@@ -160,6 +160,38 @@ def test_repeated_decode_is_deterministic():
     assert torch.equal(a, dw.out)
 
 
+def _segment_pieces(dw, segs):
+    """Pieces of each (row, KV head) segment in the last launch, from the
+    workspace's first- and last-worker records (256-byte aligned arrays after
+    the 256-byte header)."""
+    ws = dw.workspace
+    first = ws[256:256 + 4 * segs].view(torch.int32).cpu().numpy()
+    off = (256 + 4 * segs + 255) // 256 * 256
+    last = ws[off:off + 4 * segs].view(torch.int32).cpu().numpy()
+    return last - first + 1
+
+
+# long rows split over hundreds of workers: the combine's helpers fold them
+# per (query head, dim slice); the last case has 1024 pieces in one segment
+LONG_CASES = [(8, 2, [70000, 5, 3000]), (16, 2, [70000, 700]), (16, 1, [90000]), (6, 2, [70000, 40]),
+              (8, 1, [262144])]
+
+
+@pytest.mark.parametrize("Hq,Hkv,lengths", LONG_CASES)
+def test_long_segments(Hq, Hkv, lengths):
+    cfg = small_config(lengths, Hq=Hq, Hkv=Hkv, h=128, s=4, w=128, seed=700 + Hq + len(lengths))
+    rows = list(range(cfg.batch))
+    dw = make_device_workload(cfg, keep=rows, gen_device="cuda")
+    dw.decode_step()
+    torch.cuda.synchronize()
+    n = _segment_pieces(dw, cfg.batch * Hkv)
+    err, err_lse, _ = compare_attention(dw, rows)
+    _report(f"long segments g={Hq // Hkv} lengths={lengths}", pieces=n.tolist(), max_abs=f"{err:.2e}",
+            lse=f"{err_lse:.2e}")
+    assert n.max() > 32
+    assert err <= ATOL and err_lse <= ATOL
+
+
 FULL = ["qwen3_4b_b64", "qwen3_8b_async_256", "long_128k", "refill_512"]
 
 
