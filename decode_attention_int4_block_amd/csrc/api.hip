@@ -153,23 +153,18 @@ kvq_status cu_count(int *out) {
 }
 
 struct WsLayout {
-    size_t first_off, last_off, wseg_off, count_off, l2_off, piece_off, total;
+    size_t first_off, last_off, wseg_off, piece_off, total;
 };
-
-size_t l2_slots(size_t segs, int workers) { return (size_t)workers / kvq::kChunkPieces + 1 + segs; }
 
 WsLayout ws_layout(const kvq_cache *c, int B, int g, int workers) {
     WsLayout l;
     const size_t segs = (size_t)B * c->num_kv_heads;
-    const size_t piece_bytes = (size_t)g * kvq::kPieceStride * sizeof(float);
     l.first_off = kvq::kWsHeaderBytes;
     l.last_off = align256(l.first_off + segs * sizeof(int32_t));
     l.wseg_off = align256(l.last_off + segs * sizeof(int32_t));
-    l.count_off = align256(l.wseg_off + 2 * (size_t)workers * sizeof(int32_t));
-    l.l2_off = align256(l.count_off + segs * sizeof(int32_t));
-    l.piece_off = align256(l.l2_off + l2_slots(segs, workers) * piece_bytes);
+    l.piece_off = align256(l.wseg_off + 2 * (size_t)workers * sizeof(int32_t));
     const size_t pieces = (size_t)workers + (size_t)B * c->num_kv_heads;
-    l.total = align256(l.piece_off + pieces * g * kvq::kPieceStride * sizeof(float));
+    l.total = align256(l.piece_off + pieces * (size_t)g * kvq::kPieceStride * sizeof(float));
     return l;
 }
 
@@ -328,8 +323,6 @@ kvq_status decode_launch(const kvq_cache *c, bool fused, const uint16_t *k_new, 
     a.ws_header = reinterpret_cast<int32_t *>(ws);
     a.ws_first = reinterpret_cast<int32_t *>(ws + l.first_off);
     a.ws_wseg = reinterpret_cast<int32_t *>(ws + l.wseg_off);
-    a.ws_count = reinterpret_cast<int32_t *>(ws + l.count_off);
-    a.ws_l2 = reinterpret_cast<float *>(ws + l.l2_off);
     a.ws_last = reinterpret_cast<int32_t *>(ws + l.last_off);
     a.ws_piece = reinterpret_cast<float *>(ws + l.piece_off);
     a.out = out;

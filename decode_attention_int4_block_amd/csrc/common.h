@@ -60,7 +60,7 @@ __host__ __device__ constexpr int value_area_bytes(int bits) {
 // Workspace of the decode attention: header, per-row cost prefix, partial pieces.
 constexpr int kPieceStride = 132;           // floats per (piece, query head): m, l, 0, 0, acc[128]
 constexpr size_t kWsHeaderBytes = 256;
-constexpr int kChunkPieces = 32;            // a segment with more pieces is combined in chunks of this many
+constexpr int kChunkPieces = 32;            // a segment with more pieces is folded by the combine's helpers
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -269,8 +269,6 @@ struct DecodeArgs {
     int32_t *ws_first;      // [B*H] worker that attended the segment's first unit
     int32_t *ws_last;       // [B*H] worker that attended the segment's last unit
     int32_t *ws_wseg;       // [2*workers] segment of each worker's first / last piece, or -1
-    int32_t *ws_count;      // [B*H] pieces of a long segment folded so far (zeroed by the split kernel)
-    float *ws_l2;           // [workers/kChunkPieces + 1 + B*H][g][kPieceStride] chunk partials of long segments
     float *ws_piece;        // [max_workers + B*H][g][kPieceStride] per-worker pieces
     float *out;
     float *lse;

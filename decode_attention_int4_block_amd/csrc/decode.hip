@@ -1493,10 +1493,7 @@ void decode_split_kernel(DecodeArgs a) {
         const bool first = E.u - E.r >= u_begin, last = E.r == E.rp.cost - 1;
         const int64_t seg = (int64_t)E.b * a.H + E.hk;
         if (lane == 0) {
-            if (first) {
-                a.ws_first[seg] = (int32_t)wid;
-                a.ws_count[seg] = 0;
-            }
+            if (first) a.ws_first[seg] = (int32_t)wid;
             if (last) a.ws_last[seg] = (int32_t)wid;
         }
         if (!first) wseg0 = (int32_t)seg;            // only the wave's first segment can start earlier

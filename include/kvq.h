@@ -298,7 +298,7 @@ kvq_status kv_decode_read_ceiling(const kvq_cache *cache,
  *
  *   Limit: B rows of num_q_heads heads fit when kv_decode_attn_workspace_bytes
  *   (cache, B, num_q_heads) <= KVQ_NOALLOC_SCRATCH_BYTES (e.g. 256 rows of 32
- *   query heads over 8 KV heads need about 14 MB, 512 such rows about 23 MB);
+ *   query heads over 8 KV heads need about 9 MB, 512 such rows about 13 MB);
  *   larger requests return KVQ_ERR_WORKSPACE and enqueue nothing.
  *   Every call on one device shares that device's array: calls that can run
  *   at the same time on one device (different streams, or host threads with
