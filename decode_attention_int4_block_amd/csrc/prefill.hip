@@ -34,11 +34,16 @@ namespace kvq {
 
 namespace {
 
-// Running max raised whenever a step's max exceeds it, so p <= 1 and p * s_v
-// stays inside the f16 range (s_v itself is an fp16 value): the hi and lo
-// parts of p * s_v can then both be at the unit scale and accumulate in one
-// fp32 accumulator per tile, lo keeping absolute steps of 2^-24.
-constexpr float kTau = 0.0f;
+// Lazy running max: the max m of a column is raised only when a step's max
+// exceeds it by more than kTau (log2 units), and the exponentials are taken
+// against m + kTau, so p = 2^(s - m - kTau) <= 1 and p * s_v stays inside the
+// f16 range (s_v itself is an fp16 value): the hi and lo parts of p * s_v can
+// then both be at the unit scale and accumulate in one fp32 accumulator per
+// tile, lo keeping absolute steps of 2^-24.  A raise rescales the tile's
+// accumulator (32 products and the column's factor from its lanes), which
+// with kTau = 0 most steps of a 32-column wave paid; a new maximum must now
+// beat the running one by a factor of 4.
+constexpr float kTau = 2.0f;
 
 // hi = f16(a, b), lo = f16(a - hi, b - hi): hi + lo carries ~22 bits of a, b.
 __device__ inline void split_unit(float a, float b, uint32_t &hi, uint32_t &lo) {
@@ -432,7 +437,7 @@ void prefill_kernel(PrefillArgs a) {
                 }
             }
             // a column with no valid position yet keeps mK = -inf: its p are exp2(-inf) = 0
-            const float nm = mK[k] == kNegInf ? 0.0f : -mK[k];
+            const float nm = mK[k] == kNegInf ? 0.0f : -(mK[k] + kTau);
             float pv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -514,7 +519,7 @@ void prefill_kernel(PrefillArgs a) {
             }
         }
         if (a.lse && G == 0 && n < ncol[k])
-            a.lse[(int64_t)(row0 + t0 + crow[k]) * a.Hq + (int64_t)hk * a.g + chead[k]] = (mK[k] + __log2f(ls)) / kLog2e;
+            a.lse[(int64_t)(row0 + t0 + crow[k]) * a.Hq + (int64_t)hk * a.g + chead[k]] = (mK[k] + kTau + __log2f(ls)) / kLog2e;
     }
 }
 
