@@ -45,12 +45,40 @@ namespace {
 // beat the running one by a factor of 4.
 constexpr float kTau = 2.0f;
 
+// Mixed-precision helpers.  These are inline asm, and the compiler's hazard
+// checks do not look inside inline asm: an operand written by an MFMA, a
+// transcendental (exp) or a cross-lane move just before could be read stale.
+// They are used only on operands that ordinary VALU instructions or LDS reads
+// produce (params words, the query sum, f16 conversions and products), never
+// on the MFMA scores or on exp results.
+
+// a - (float)(low / high f16 half of h) in one mixed-precision fma (h * -1 + a
+// with h read as f16), which the compiler otherwise emits as a conversion and
+// a subtraction.  The difference is exact in fp32 when h holds a rounded to f16.
+__device__ inline float sub_f16_lo(float a, uint32_t h) {
+    float r;
+    __asm__("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
+    return r;
+}
+__device__ inline float sub_f16_hi(float a, uint32_t h) {
+    float r;
+    __asm__("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
+    return r;
+}
+
+// hi(w) * x in one mixed-precision fma with a +0 addend (the compiler otherwise
+// converts the half first); it rounds as the product does and differs only in
+// giving +0 for a -0 product.
+__device__ inline float mul_f16_hi(uint32_t w, float x) {
+    float r;
+    __asm__("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+    return r;
+}
+
 // hi = f16(a, b), lo = f16(a - hi, b - hi): hi + lo carries ~22 bits of a, b.
 __device__ inline void split_unit(float a, float b, uint32_t &hi, uint32_t &lo) {
     hi = f16x2(a, b);
-    uint32_t h = hi;
-    __asm__("" : "+v"(h));
-    lo = f16x2(a - h_lo(h), b - h_hi(h));
+    lo = f16x2(sub_f16_lo(a, hi), sub_f16_hi(b, hi));
 }
 
 // Position held by ring entry e at length L (e < min(L, s + w)): a sink, or the
@@ -387,8 +415,8 @@ void prefill_kernel(PrefillArgs a) {
                 // the common step: one wave-uniform branch, no per-position selects
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    t[j] = fmaf(a4[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh[k]);
-                    t[4 + j] = fmaf(sB[k][j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh[k]);
+                    t[j] = fmaf(a4[j], h_lo(kpA[j]), mul_f16_hi(kpA[j], Rh[k]));
+                    t[4 + j] = fmaf(sB[k][j], h_lo(kpB[j]), mul_f16_hi(kpB[j], Rh[k]));
                     vp[j] = vpr[j];
                     vp[4 + j] = vpr[4 + j];
                 }
@@ -407,8 +435,8 @@ void prefill_kernel(PrefillArgs a) {
                     }
                     // params of positions outside the context may be arbitrary bytes
                     // (NaN as fp16): dropped by a select, never multiplied by zero
-                    const float tA = fmaf(a4[j], h_lo(kpA[j]), h_hi(kpA[j]) * Rh[k]);
-                    const float tB = fmaf(sB[k][j], h_lo(kpB[j]), h_hi(kpB[j]) * Rh[k]);
+                    const float tA = fmaf(a4[j], h_lo(kpA[j]), mul_f16_hi(kpA[j], Rh[k]));
+                    const float tB = fmaf(sB[k][j], h_lo(kpB[j]), mul_f16_hi(kpB[j], Rh[k]));
                     t[j] = okA ? tA : kNegInf;
                     t[4 + j] = okB ? tB : kNegInf;
                     vp[j] = okA ? vpr[j] : 0u;
