@@ -168,6 +168,71 @@ __device__ inline void issue_prefill_step(const PrefillArgs &a, const RowPlan &r
 
 }  // namespace
 
+// Dispatch order of the waves (launches of at most 64 sequences): the
+// workgroups are dispatched in linear index order and a wave's time grows with
+// its causal prefix, so the waves are handed out longest prefix first over
+// all sequences (heads of one block of rows together), which leaves the
+// shortest waves for the end of the launch.  A wave of RW rows of sequence b
+// ends at position pmax(b, v) = L_b - T_b + min((v + 1) RW, T_b) - 1.  Lane l
+// holds sequence l; the wave finds the k-th largest pmax by a binary search on
+// the count of waves at or above a bound, and among equal ones takes them in
+// sequence order.  Simulated on the 8 x 1024-row Qwen3-8B chunks (waves of
+// 8 rows, 2048 resident, time proportional to the prefix), the makespan goes
+// from 7.5% to 3.9% above a perfect split.
+struct PrefillTask {
+    int b, hk, wv;          // b = -1: no work for this workgroup
+};
+
+__device__ inline int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return uni(x);
+}
+__device__ inline int wave_max_i(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+    return uni(x);
+}
+
+__device__ inline PrefillTask prefill_task(const PrefillArgs &a, int RW, int lane) {
+    const int64_t i = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t k = i / a.H;
+    PrefillTask tk;
+    tk.b = -1;
+    tk.hk = (int)(i - k * a.H);
+    tk.wv = 0;
+    const bool in = lane < a.B;
+    const int T = in ? ldc(a.q_start, lane + 1) - ldc(a.q_start, lane) : 0;
+    const int base = in ? ldc(a.ctx_len, lane) - T : 0;    // position of the chunk's first row
+    const int nw = (T + RW - 1) / RW;
+    // waves of this lane's sequence with pmax >= x
+    auto count_ge = [&](int x) {
+        const int y = x + 1 - base;
+        const int c = T == 0 ? 0 : (y <= 1 ? nw : (y > T ? 0 : nw - (y + RW - 1) / RW + 1));
+        return wave_sum_i(c);
+    };
+    if (k >= wave_sum_i(nw)) return tk;
+    // the largest x with count_ge(x) > k (pmax >= 0 for every wave)
+    int lo = 0, hi = wave_max_i(T > 0 ? base + T - 1 : 0);
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (count_ge(mid) > k) lo = mid;
+        else hi = mid - 1;
+    }
+    // rank among the waves ending exactly at lo (at most one per sequence)
+    const int j = (int)(k - count_ge(lo + 1));
+    const int y = lo + 1 - base;
+    const bool at = T > 0 && y >= 1 && y <= T && (y == T || y % RW == 0);
+    uint64_t m = __ballot(at);
+    for (int r = 0; r < j; ++r) m &= m - 1;
+    const int src = __ffsll((unsigned long long)m) - 1;
+    const int yb = __builtin_amdgcn_readlane(y, src), Tb = __builtin_amdgcn_readlane(T, src);
+    const int nwb = __builtin_amdgcn_readlane(nw, src);
+    tk.b = src;
+    tk.wv = yb == Tb ? nwb - 1 : yb / RW - 1;
+    return tk;
+}
+
 // Waves per SIMD: the two-tile 4-bit kernel needs ~250 registers (two waves);
 // the one-tile 3- and 2-bit kernels fit 168 (three waves).
 template <int BITS>
@@ -180,11 +245,22 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int NT = prefill_tiles(BITS);
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x;
-    const int b = blockIdx.z, hk = blockIdx.y;
+    int b, hk, wv;
+    if (a.B <= 64) {
+        const PrefillTask tk = prefill_task(a, a.R * NT, lane);
+        if (tk.b < 0) return;
+        b = tk.b;
+        hk = tk.hk;
+        wv = tk.wv;
+    } else {
+        // waves in reverse order inside each sequence: its longest causal
+        // prefixes are dispatched first
+        b = blockIdx.z;
+        hk = blockIdx.y;
+        wv = (int)(gridDim.x - 1 - blockIdx.x);
+    }
     const int row0 = ldc(a.q_start, b);
     const int T = ldc(a.q_start, b + 1) - row0;
-    // waves in reverse order: the longest causal prefixes are dispatched first
-    const int wv = (int)(gridDim.x - 1 - blockIdx.x);
     const int t0 = wv * a.R * NT;               // the wave's first row
     if (t0 >= T) return;
     const int L = ldc(a.ctx_len, b);

@@ -168,6 +168,22 @@ def test_prefill_page_sizes_empty_rows_and_whole_sequences():
         assert err <= ATOL and err_lse <= ATOL
 
 
+@pytest.mark.parametrize("B", [64, 70])
+def test_prefill_many_sequences(B):
+    """Launches of up to 64 sequences hand the waves out longest causal prefix
+    first over all sequences; larger ones keep the per-sequence order.  Both
+    sides of the limit, with empty chunks and chunks of every size up to a few
+    waves."""
+    rng = np.random.default_rng(2600 + B)
+    lengths = [int(x) for x in rng.integers(1, 260, size=B)]
+    lengths[3] = 0
+    Ts = [min(L, int(t)) for L, t in zip(lengths, rng.integers(0, 40, size=B))]
+    cfg = small_config(lengths, h=64, s=4, w=32, seed=2600 + B)
+    err, err_lse = _run(cfg, Ts, seed=B, check_decode=False)
+    _report(f"{B} sequences", max_abs=f"{err:.2e}", lse=f"{err_lse:.2e}")
+    assert err <= ATOL and err_lse <= ATOL
+
+
 def test_prefill_long_chunk_sampled_rows():
     """A 4096-token sequence with a 1024-row chunk, Qwen3-8B heads; rows sampled
     for the oracle (the first, the last, the window boundary, random)."""
