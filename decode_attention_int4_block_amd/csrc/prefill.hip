@@ -42,8 +42,10 @@ namespace {
 // tile, lo keeping absolute steps of 2^-24.  A raise rescales the tile's
 // accumulator (32 products and the column's factor from its lanes), which
 // with kTau = 0 most steps of a 32-column wave paid; a new maximum must now
-// beat the running one by a factor of 4.
-constexpr float kTau = 2.0f;
+// beat the running one by a factor of 16.  The price is lo's absolute step:
+// 2^-24 against a largest p of 2^-kTau (measured on the parity cases: 2-bit
+// errors 5.65e-4 -> 5.82e-4 from kTau = 2 to 4, far inside the 2e-3 bound).
+constexpr float kTau = 4.0f;
 
 // Mixed-precision helpers.  These are inline asm, and the compiler's hazard
 // checks do not look inside inline asm: an operand written by an MFMA, a
